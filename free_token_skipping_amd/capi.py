@@ -1,0 +1,326 @@
+"""Thin Python binding of libspts.so (the C ABI in include/spts.h).
+
+Argument marshalling only: every function checks that its torch tensors sit
+on the GPU with the dtype and contiguity the C call expects, passes their
+device pointers and the current HIP stream, and raises SptsError on a
+non-OK status.  All computation happens in the library's HIP kernels; there
+is no CPU fallback -- without the built library every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspts.so")
+
+BF16, F32, I32 = 0, 1, 2
+_DTYPE = {torch.bfloat16: BF16, torch.float32: F32, torch.int32: I32}
+
+# Every function the header declares (checked against include/spts.h by the tests).
+EXPORTS = [
+    "spts_create", "spts_destroy", "spts_set_stream", "spts_set_workspace", "spts_last_error",
+    "spts_status_name", "spts_check",
+    "spts_probe_attention_workspace", "spts_score_topk_workspace", "spts_ltp_probe_workspace",
+    "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace",
+    "spts_probe_attention", "spts_score_topk", "spts_gather", "spts_scatter",
+    "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
+    "spts_linear", "spts_linear_rope", "spts_rope_table", "spts_rmsnorm",
+]
+
+_c = ctypes
+_P, _I, _F, _D, _SZ = _c.c_void_p, _c.c_int, _c.c_float, _c.c_double, _c.c_size_t
+_SIGS = {
+    "spts_create": (_I, [_c.POINTER(_P), _P]),
+    "spts_destroy": (_I, [_P]),
+    "spts_set_stream": (_I, [_P, _P]),
+    "spts_set_workspace": (_I, [_P, _P, _SZ]),
+    "spts_last_error": (_c.c_char_p, [_P]),
+    "spts_status_name": (_c.c_char_p, [_I]),
+    "spts_check": (_I, [_P]),
+    "spts_probe_attention_workspace": (_SZ, [_I, _I, _I]),
+    "spts_score_topk_workspace": (_SZ, [_I]),
+    "spts_ltp_probe_workspace": (_SZ, [_I, _I, _I]),
+    "spts_reduced_ffn_workspace": (_SZ, [_I, _I]),
+    "spts_msdp_stage_workspace": (_SZ, [_I]),
+    "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
+    "spts_gather": (_I, [_P, _I, _P, _P, _I, _I, _P]),
+    "spts_scatter": (_I, [_P, _I, _P, _P, _I, _I, _P, _I]),
+    "spts_reduced_attention": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "spts_ltp_probe": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
+    "spts_reduced_ffn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _I]),
+    "spts_msdp_stage": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I]),
+    "spts_linear": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P, _I]),
+    "spts_linear_rope": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P, _P]),
+    "spts_rope_table": (_I, [_P, _I, _I, _D, _P]),
+    "spts_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P]),
+}
+
+_lib = None
+
+
+class SptsError(RuntimeError):
+    def __init__(self, status, name, message):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+
+
+def lib():
+    """Load libspts.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m free_token_skipping_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------- context
+
+class Context:
+    """One spts_ctx bound to the current torch stream, with a growable
+    workspace tensor (torch allocates it; the library only borrows it)."""
+
+    def __init__(self):
+        self.handle = _P()
+        st = lib().spts_create(ctypes.byref(self.handle), None)
+        if st != 0:
+            raise SptsError(st, "spts_create", "failed")
+        self.ws = None
+
+    def __del__(self):
+        try:
+            if self.handle and _lib is not None:
+                _lib.spts_destroy(self.handle)
+        except Exception:
+            pass
+
+    def bind(self, ws_bytes=0, device=None):
+        if device is None or torch.device(device).type != "cuda":
+            raise ValueError("libspts works on GPU tensors only (got device %s)" % (device,))
+        L = lib()
+        stream = torch.cuda.current_stream(device).cuda_stream
+        L.spts_set_stream(self.handle, _P(stream))
+        if ws_bytes:
+            if self.ws is None or self.ws.numel() < ws_bytes or self.ws.device != device:
+                self.ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=device)
+            _check(self, L.spts_set_workspace(self.handle, _P(self.ws.data_ptr()), self.ws.numel()), "workspace")
+        return self.handle
+
+    def check(self):
+        _check(self, lib().spts_check(self.handle), "spts_check")
+
+
+_ctx = None
+
+
+def context():
+    global _ctx
+    if _ctx is None:
+        _ctx = Context()
+    return _ctx
+
+
+def _check(ctx, status, what):
+    if status != 0:
+        L = lib()
+        name = L.spts_status_name(status).decode()
+        msg = L.spts_last_error(ctx.handle).decode() if ctx is not None else ""
+        raise SptsError(status, name, f"{what}: {msg}")
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _P(t.data_ptr())
+
+
+def _dt(t):
+    if t.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+# -------------------------------------------------------------- entry points
+
+def spts_probe_attention(q_probe, k, scale=None, scores=None):
+    """q_probe [P,Hq,dh], k [n,Hkv,dh] (bf16 or fp32) -> scores [n] fp32."""
+    P, Hq, dh = q_probe.shape
+    n, Hkv, _ = k.shape
+    scale = float(dh ** -0.5) if scale is None else float(scale)
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=k.device)
+    ctx = context()
+    h = ctx.bind(lib().spts_probe_attention_workspace(n, P, Hq), k.device)
+    _check(ctx, lib().spts_probe_attention(h, _dt(k), _ptr(q_probe, k.dtype, "q_probe"), _ptr(k, name="k"),
+                                           n, P, Hq, Hkv, dh, scale, _ptr(scores, torch.float32, "scores")),
+           "spts_probe_attention")
+    return scores
+
+
+def spts_score_topk(s_a, k, n_forced, s_b=None, w_a=0.5, w_b=0.5, idx=None, fused_out=None):
+    """Ascending int32 indices of the k kept rows (see include/spts.h)."""
+    n = s_a.shape[0]
+    if idx is None:
+        idx = torch.empty(min(k, n), dtype=torch.int32, device=s_a.device)
+    ctx = context()
+    h = ctx.bind(lib().spts_score_topk_workspace(n), s_a.device)
+    _check(ctx, lib().spts_score_topk(h, _ptr(s_a, torch.float32, "s_a"), _ptr(s_b, torch.float32, "s_b"),
+                                      float(w_a), float(w_b), n, int(k), int(n_forced),
+                                      _ptr(idx, torch.int32, "idx"), _ptr(fused_out, torch.float32, "fused_out")),
+           "spts_score_topk")
+    return idx
+
+
+def _row_elems(t):
+    return int(t[0].numel()) if t.dim() > 1 else 1
+
+
+def spts_gather(src, idx, dst=None):
+    k = idx.shape[0]
+    if dst is None:
+        dst = torch.empty((k,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    ctx = context()
+    h = ctx.bind(0, src.device)
+    _check(ctx, lib().spts_gather(h, _dt(src), _ptr(src, name="src"), _ptr(idx, torch.int32, "idx"), k,
+                                  _row_elems(src), _ptr(dst, src.dtype, "dst")), "spts_gather")
+    return dst
+
+
+def spts_scatter(src, idx, dst, accumulate=False):
+    k = idx.shape[0]
+    ctx = context()
+    h = ctx.bind(0, dst.device)
+    _check(ctx, lib().spts_scatter(h, _dt(dst), _ptr(src, dst.dtype, "src"), _ptr(idx, torch.int32, "idx"), k,
+                                   _row_elems(dst), _ptr(dst, name="dst"), int(bool(accumulate))), "spts_scatter")
+    return dst
+
+
+def spts_reduced_attention(q_sel, idx, k, v, scale=None, o_sel=None):
+    kq, Hq, dh = q_sel.shape
+    n, Hkv, _ = k.shape
+    scale = float(dh ** -0.5) if scale is None else float(scale)
+    if o_sel is None:
+        o_sel = torch.empty_like(q_sel)
+    ctx = context()
+    h = ctx.bind(0, k.device)
+    _check(ctx, lib().spts_reduced_attention(h, _dt(k), _ptr(q_sel, k.dtype, "q_sel"), _ptr(idx, torch.int32, "idx"),
+                                             _ptr(k, name="k"), _ptr(v, k.dtype, "v"), kq, n, Hq, Hkv, dh, scale,
+                                             _ptr(o_sel, k.dtype, "o_sel")), "spts_reduced_attention")
+    return o_sel
+
+
+def spts_ltp_probe(z, u_t, v_t, score=None):
+    n, d = z.shape
+    r = u_t.shape[0]
+    if score is None:
+        score = torch.empty(n, dtype=torch.float32, device=z.device)
+    ctx = context()
+    h = ctx.bind(lib().spts_ltp_probe_workspace(n, d, r), z.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_ltp_probe(h, _ptr(z, bf, "z"), _ptr(u_t, bf, "u_t"), _ptr(v_t, bf, "v_t"), n, d, r,
+                                     _ptr(score, torch.float32, "score")), "spts_ltp_probe")
+    return score
+
+
+def spts_reduced_ffn(z, w_gate, w_up, w_down, rows=None, y=None, y_rows=None, accumulate=False):
+    d = z.shape[1]
+    f = w_gate.shape[0]
+    k = rows.shape[0] if rows is not None else z.shape[0]
+    if y is None:
+        y = torch.empty((k, d), dtype=torch.bfloat16, device=z.device)
+    ctx = context()
+    h = ctx.bind(lib().spts_reduced_ffn_workspace(k, f), z.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_reduced_ffn(h, _ptr(z, bf, "z"), _ptr(rows, torch.int32, "rows"), _ptr(w_gate, bf, "w_gate"),
+                                       _ptr(w_up, bf, "w_up"), _ptr(w_down, bf, "w_down"), k, d, f,
+                                       _ptr(y, bf, "y"), _ptr(y_rows, torch.int32, "y_rows"),
+                                       int(bool(accumulate))), "spts_reduced_ffn")
+    return y
+
+
+def spts_msdp_stage(scores, budget, n_forced, pos_prev, x_prev=None, keep=None, pos_new=None, x_new=None):
+    n_prev = scores.shape[0]
+    dev = scores.device
+    if keep is None:
+        keep = torch.empty(budget, dtype=torch.int32, device=dev)
+    if pos_new is None:
+        pos_new = torch.empty(budget, dtype=torch.int32, device=dev)
+    d = 0
+    if x_prev is not None:
+        d = x_prev.shape[1]
+        if x_new is None:
+            x_new = torch.empty((budget, d), dtype=x_prev.dtype, device=dev)
+    ctx = context()
+    h = ctx.bind(lib().spts_msdp_stage_workspace(n_prev), dev)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_msdp_stage(h, _ptr(scores, torch.float32, "scores"), n_prev, int(budget), int(n_forced),
+                                      _ptr(pos_prev, torch.int32, "pos_prev"), _ptr(keep, torch.int32, "keep"),
+                                      _ptr(pos_new, torch.int32, "pos_new"), _ptr(x_prev, bf, "x_prev"),
+                                      _ptr(x_new, bf, "x_new"), d), "spts_msdp_stage")
+    return keep, pos_new, x_new
+
+
+def spts_linear(a, w, a_rows=None, out=None, out_rows=None, accumulate=False):
+    kdim = a.shape[1]
+    n = w.shape[0]
+    m = a_rows.shape[0] if a_rows is not None else a.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    ctx = context()
+    h = ctx.bind(0, a.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_linear(h, _ptr(a, bf, "a"), _ptr(a_rows, torch.int32, "a_rows"), m, kdim,
+                                  _ptr(w, bf, "w"), n, _ptr(out, bf, "out"), _ptr(out_rows, torch.int32, "out_rows"),
+                                  int(bool(accumulate))), "spts_linear")
+    return out
+
+
+def spts_linear_rope(a, w, pos, table, a_rows=None, out=None):
+    kdim = a.shape[1]
+    n = w.shape[0]
+    m = a_rows.shape[0] if a_rows is not None else a.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    ctx = context()
+    h = ctx.bind(0, a.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_linear_rope(h, _ptr(a, bf, "a"), _ptr(a_rows, torch.int32, "a_rows"), m, kdim,
+                                       _ptr(w, bf, "w"), n, _ptr(out, bf, "out"), _ptr(pos, torch.int32, "pos"),
+                                       _ptr(table, torch.float32, "table")), "spts_linear_rope")
+    return out
+
+
+def spts_rope_table(max_pos, dh, theta, device, table=None):
+    if table is None:
+        table = torch.empty((max_pos, dh // 2, 2), dtype=torch.float32, device=device)
+    ctx = context()
+    h = ctx.bind(0, device)
+    _check(ctx, lib().spts_rope_table(h, int(max_pos), int(dh), float(theta), _ptr(table, torch.float32, "table")),
+           "spts_rope_table")
+    return table
+
+
+def spts_rmsnorm(x, eps=1e-5, out=None):
+    n, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    ctx = context()
+    h = ctx.bind(0, x.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_rmsnorm(h, _ptr(x, bf, "x"), n, d, float(eps), _ptr(out, bf, "out")), "spts_rmsnorm")
+    return out

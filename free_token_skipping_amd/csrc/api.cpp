@@ -1,0 +1,413 @@
+// C-ABI host layer: argument validation, workspace carving and kernel launch
+// for every call declared in include/spts.h.  Validation runs on the host
+// before anything is enqueued; no exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/spts.h"
+#include "kernels.hpp"
+
+struct spts_ctx {
+  hipStream_t stream;
+  void* ws;
+  size_t ws_bytes;
+  char err[512];
+};
+
+namespace {
+
+using namespace spts;
+
+spts_status fail(spts_ctx* c, spts_status st, const char* fmt, ...) {
+  if (c) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(c->err, sizeof(c->err), fmt, ap);
+    va_end(ap);
+  }
+  return st;
+}
+
+spts_status hip_status(spts_ctx* c, hipError_t e, const char* what) {
+  if (e == hipSuccess) return SPTS_OK;
+  return fail(c, SPTS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, st, ...)                     \
+  do {                                             \
+    if (!(cond)) return fail(ctx, st, __VA_ARGS__); \
+  } while (0)
+
+#define CHECK_CTX() \
+  do {              \
+    if (!ctx) return SPTS_ERR_INVALID; \
+    ctx->err[0] = 0; \
+  } while (0)
+
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr, SPTS_ERR_INVALID, "%s is NULL", #p)
+#define REQUIRE_ALIGN(p) REQUIRE(aligned16(p), SPTS_ERR_ALIGN, "%s is not 16-byte aligned", #p)
+
+// element offsets inside kernels are computed in 64-bit, but row counts and
+// per-row strides are int: keep every extent below 2^31 elements per row.
+constexpr long kMaxElems = 1L << 40;
+
+}  // namespace
+
+extern "C" {
+
+const char* spts_status_name(spts_status s) {
+  switch (s) {
+    case SPTS_OK: return "SPTS_OK";
+    case SPTS_ERR_INVALID: return "SPTS_ERR_INVALID";
+    case SPTS_ERR_SHAPE: return "SPTS_ERR_SHAPE";
+    case SPTS_ERR_DTYPE: return "SPTS_ERR_DTYPE";
+    case SPTS_ERR_ALIGN: return "SPTS_ERR_ALIGN";
+    case SPTS_ERR_NOMEM: return "SPTS_ERR_NOMEM";
+    case SPTS_ERR_HIP: return "SPTS_ERR_HIP";
+    case SPTS_ERR_UNSUPPORTED: return "SPTS_ERR_UNSUPPORTED";
+  }
+  return "SPTS_UNKNOWN";
+}
+
+spts_status spts_create(spts_ctx** out, void* hip_stream) {
+  if (!out) return SPTS_ERR_INVALID;
+  spts_ctx* c = new (std::nothrow) spts_ctx;
+  if (!c) return SPTS_ERR_NOMEM;
+  c->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  c->ws = nullptr;
+  c->ws_bytes = 0;
+  c->err[0] = 0;
+  *out = c;
+  return SPTS_OK;
+}
+
+spts_status spts_destroy(spts_ctx* ctx) {
+  if (!ctx) return SPTS_ERR_INVALID;
+  delete ctx;
+  return SPTS_OK;
+}
+
+spts_status spts_set_stream(spts_ctx* ctx, void* hip_stream) {
+  CHECK_CTX();
+  ctx->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  return SPTS_OK;
+}
+
+spts_status spts_set_workspace(spts_ctx* ctx, void* dev_ptr, size_t bytes) {
+  CHECK_CTX();
+  REQUIRE(dev_ptr != nullptr || bytes == 0, SPTS_ERR_INVALID, "workspace pointer is NULL");
+  REQUIRE(aligned16(dev_ptr), SPTS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  ctx->ws = dev_ptr;
+  ctx->ws_bytes = bytes;
+  return SPTS_OK;
+}
+
+const char* spts_last_error(const spts_ctx* ctx) { return ctx ? ctx->err : "NULL context"; }
+
+spts_status spts_check(spts_ctx* ctx) {
+  CHECK_CTX();
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "stream");
+  return hip_status(ctx, hipGetLastError(), "pending");
+}
+
+// ------------------------------------------------------------ workspace sizes
+
+size_t spts_probe_attention_workspace(int n, int P, int Hq) {
+  if (n <= 0 || P <= 0 || Hq <= 0) return 0;
+  return probe_workspace(n, P, Hq);
+}
+size_t spts_score_topk_workspace(int n) { return n > 0 ? topk_workspace(n) : 0; }
+size_t spts_ltp_probe_workspace(int n, int d, int r) {
+  if (n <= 0 || d <= 0 || r <= 0) return 0;
+  const size_t t2 = ((size_t)n * 2 * r * 2 + 255) & ~(size_t)255;      // z U as bf16 hi/lo
+  const size_t part = ((size_t)n * (d / 256) * 4 + 255) & ~(size_t)255; // row sums of squares
+  return t2 + part;
+}
+size_t spts_reduced_ffn_workspace(int k, int f) {
+  if (k <= 0 || f <= 0) return 0;
+  return ((size_t)k * f * 2 + 255) & ~(size_t)255;
+}
+size_t spts_msdp_stage_workspace(int n_prev) { return n_prev > 0 ? topk_workspace(n_prev) : 0; }
+
+// ------------------------------------------------------------------------ PAP
+
+spts_status spts_probe_attention(spts_ctx* ctx, spts_dtype dtype, const void* q_probe, const void* k,
+                                 int n, int P, int Hq, int Hkv, int dh, float scale, float* scores) {
+  CHECK_CTX();
+  REQUIRE_PTR(q_probe); REQUIRE_PTR(k); REQUIRE_PTR(scores);
+  REQUIRE_ALIGN(q_probe); REQUIRE_ALIGN(k); REQUIRE_ALIGN(scores);
+  REQUIRE(n > 0 && P > 0 && P <= n, SPTS_ERR_SHAPE, "need 0 < P <= n (P=%d n=%d)", P, n);
+  REQUIRE(Hq > 0 && Hkv > 0 && Hq % Hkv == 0, SPTS_ERR_SHAPE, "Hq %% Hkv != 0 (Hq=%d Hkv=%d)", Hq, Hkv);
+  REQUIRE((long)n * Hkv * dh < kMaxElems, SPTS_ERR_SHAPE, "too large");
+  const size_t need = probe_workspace(n, P, Hq);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  if (dtype == SPTS_BF16) {
+    REQUIRE(dh == 128, SPTS_ERR_UNSUPPORTED, "bf16 probe needs dh == 128 (dh=%d)", dh);
+    REQUIRE(P == 32 || P == 64 || P == 128, SPTS_ERR_UNSUPPORTED, "bf16 probe needs P in {32,64,128} (P=%d)", P);
+    REQUIRE((Hq / Hkv) % 4 == 0, SPTS_ERR_UNSUPPORTED, "bf16 probe needs Hq/Hkv %% 4 == 0");
+    return hip_status(ctx, launch_probe_bf16(reinterpret_cast<const uint16_t*>(q_probe),
+                                             reinterpret_cast<const uint16_t*>(k), n, P, Hq, Hkv, scale,
+                                             scores, ctx->ws, ctx->stream), "probe_attention");
+  }
+  if (dtype == SPTS_F32) {
+    REQUIRE(dh > 0 && dh <= 128, SPTS_ERR_UNSUPPORTED, "fp32 probe needs 0 < dh <= 128");
+    return hip_status(ctx, launch_probe_f32(reinterpret_cast<const float*>(q_probe),
+                                            reinterpret_cast<const float*>(k), n, P, Hq, Hkv, dh, scale,
+                                            scores, ctx->ws, ctx->stream), "probe_attention");
+  }
+  return fail(ctx, SPTS_ERR_DTYPE, "probe_attention: dtype %d not supported", (int)dtype);
+}
+
+// --------------------------------------------------------------------- select
+
+spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, float w_a, float w_b,
+                            int n, int k, int n_forced, int32_t* idx, float* fused_out) {
+  CHECK_CTX();
+  REQUIRE_PTR(s_a); REQUIRE_PTR(idx);
+  REQUIRE_ALIGN(s_a); REQUIRE_ALIGN(idx);
+  if (s_b) REQUIRE_ALIGN(s_b);
+  if (fused_out) REQUIRE_ALIGN(fused_out);
+  REQUIRE(n >= 1, SPTS_ERR_SHAPE, "n must be >= 1");
+  REQUIRE(n_forced >= 0 && n_forced <= k && n_forced <= n, SPTS_ERR_SHAPE,
+          "need 0 <= n_forced <= k and n_forced <= n (n=%d k=%d n_forced=%d)", n, k, n_forced);
+  const size_t need = topk_workspace(n);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  return hip_status(ctx, launch_topk(s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, ctx->ws, ctx->stream),
+                    "score_topk");
+}
+
+// ------------------------------------------------------------- gather/scatter
+
+static int dtype_bytes(spts_dtype t) {
+  switch (t) {
+    case SPTS_BF16: return 2;
+    case SPTS_F32: return 4;
+    case SPTS_I32: return 4;
+  }
+  return 0;
+}
+
+spts_status spts_gather(spts_ctx* ctx, spts_dtype dtype, const void* src, const int32_t* idx, int k,
+                        int row_elems, void* dst) {
+  CHECK_CTX();
+  const int eb = dtype_bytes(dtype);
+  REQUIRE(eb > 0, SPTS_ERR_DTYPE, "gather: bad dtype %d", (int)dtype);
+  REQUIRE(k >= 0 && row_elems > 0, SPTS_ERR_SHAPE, "gather: need k >= 0, row_elems > 0");
+  if (k == 0) return SPTS_OK;
+  REQUIRE_PTR(src); REQUIRE_PTR(idx); REQUIRE_PTR(dst);
+  REQUIRE_ALIGN(src); REQUIRE_ALIGN(idx); REQUIRE_ALIGN(dst);
+  return hip_status(ctx, launch_gather(src, idx, k, (long)row_elems * eb, dst, ctx->stream), "gather");
+}
+
+spts_status spts_scatter(spts_ctx* ctx, spts_dtype dtype, const void* src, const int32_t* idx, int k,
+                         int row_elems, void* dst, int accumulate) {
+  CHECK_CTX();
+  const int eb = dtype_bytes(dtype);
+  REQUIRE(eb > 0, SPTS_ERR_DTYPE, "scatter: bad dtype %d", (int)dtype);
+  REQUIRE(k >= 0 && row_elems > 0, SPTS_ERR_SHAPE, "scatter: need k >= 0, row_elems > 0");
+  REQUIRE(accumulate == 0 || accumulate == 1, SPTS_ERR_INVALID, "accumulate must be 0 or 1");
+  if (k == 0) return SPTS_OK;
+  REQUIRE_PTR(src); REQUIRE_PTR(idx); REQUIRE_PTR(dst);
+  REQUIRE_ALIGN(src); REQUIRE_ALIGN(idx); REQUIRE_ALIGN(dst);
+  hipError_t e;
+  if (!accumulate) e = launch_scatter(src, idx, k, (long)row_elems * eb, dst, ctx->stream);
+  else if (dtype == SPTS_BF16)
+    e = launch_scatter_add_bf16(reinterpret_cast<const uint16_t*>(src), idx, k, row_elems,
+                                reinterpret_cast<uint16_t*>(dst), ctx->stream);
+  else if (dtype == SPTS_F32)
+    e = launch_scatter_add_f32(reinterpret_cast<const float*>(src), idx, k, row_elems,
+                               reinterpret_cast<float*>(dst), ctx->stream);
+  else
+    e = launch_scatter_add_i32(reinterpret_cast<const int32_t*>(src), idx, k, row_elems,
+                               reinterpret_cast<int32_t*>(dst), ctx->stream);
+  return hip_status(ctx, e, "scatter");
+}
+
+// ----------------------------------------------------------- reduced attention
+
+spts_status spts_reduced_attention(spts_ctx* ctx, spts_dtype dtype, const void* q_sel, const int32_t* idx,
+                                   const void* k, const void* v, int kq, int n, int Hq, int Hkv, int dh,
+                                   float scale, void* o_sel) {
+  CHECK_CTX();
+  REQUIRE(kq >= 0 && n > 0 && kq <= n, SPTS_ERR_SHAPE, "need 0 <= kq <= n (kq=%d n=%d)", kq, n);
+  REQUIRE(Hq > 0 && Hkv > 0 && Hq % Hkv == 0, SPTS_ERR_SHAPE, "Hq %% Hkv != 0");
+  if (kq == 0) return SPTS_OK;
+  REQUIRE_PTR(q_sel); REQUIRE_PTR(idx); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(o_sel);
+  REQUIRE_ALIGN(q_sel); REQUIRE_ALIGN(idx); REQUIRE_ALIGN(k); REQUIRE_ALIGN(v); REQUIRE_ALIGN(o_sel);
+  if (dtype == SPTS_BF16) {
+    REQUIRE(dh == 128, SPTS_ERR_UNSUPPORTED, "bf16 attention needs dh == 128");
+    REQUIRE((Hq / Hkv) % 4 == 0, SPTS_ERR_UNSUPPORTED, "bf16 attention needs Hq/Hkv %% 4 == 0");
+    return hip_status(ctx, launch_attn_bf16(reinterpret_cast<const uint16_t*>(q_sel), idx,
+                                            reinterpret_cast<const uint16_t*>(k),
+                                            reinterpret_cast<const uint16_t*>(v), kq, n, Hq, Hkv, scale,
+                                            reinterpret_cast<uint16_t*>(o_sel), ctx->stream),
+                      "reduced_attention");
+  }
+  if (dtype == SPTS_F32) {
+    REQUIRE(dh > 0 && dh <= 128, SPTS_ERR_UNSUPPORTED, "fp32 attention needs 0 < dh <= 128");
+    return hip_status(ctx, launch_attn_f32(reinterpret_cast<const float*>(q_sel), idx,
+                                           reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v),
+                                           kq, n, Hq, Hkv, dh, scale, reinterpret_cast<float*>(o_sel),
+                                           ctx->stream),
+                      "reduced_attention");
+  }
+  return fail(ctx, SPTS_ERR_DTYPE, "reduced_attention: dtype %d not supported", (int)dtype);
+}
+
+// ------------------------------------------------------------------------ GEMM
+
+static spts_status gemm_shape_ok(spts_ctx* ctx, int m, int kdim, int n) {
+  REQUIRE(m >= 0 && kdim > 0 && n > 0, SPTS_ERR_SHAPE, "bad GEMM sizes m=%d k=%d n=%d", m, kdim, n);
+  REQUIRE(kdim % 64 == 0, SPTS_ERR_UNSUPPORTED, "inner dimension %d is not a multiple of 64", kdim);
+  REQUIRE(n % 256 == 0, SPTS_ERR_UNSUPPORTED, "output width %d is not a multiple of 256", n);
+  return SPTS_OK;
+}
+
+spts_status spts_linear(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim, const void* w,
+                        int n, void* out, const int32_t* out_rows, int accumulate) {
+  CHECK_CTX();
+  spts_status st = gemm_shape_ok(ctx, m, kdim, n);
+  if (st != SPTS_OK) return st;
+  REQUIRE(accumulate == 0 || accumulate == 1, SPTS_ERR_INVALID, "accumulate must be 0 or 1");
+  if (m == 0) return SPTS_OK;
+  REQUIRE_PTR(a); REQUIRE_PTR(w); REQUIRE_PTR(out);
+  REQUIRE_ALIGN(a); REQUIRE_ALIGN(w); REQUIRE_ALIGN(out);
+  if (a_rows) REQUIRE_ALIGN(a_rows);
+  if (out_rows) REQUIRE_ALIGN(out_rows);
+  GemmArgs g{};
+  g.a = reinterpret_cast<const uint16_t*>(a); g.a_rows = a_rows; g.m = m; g.k = kdim; g.lda = kdim;
+  g.b0 = reinterpret_cast<const uint16_t*>(w); g.ldb = kdim; g.n = n;
+  g.out = out; g.ldc = n; g.out_rows = out_rows; g.accumulate = accumulate;
+  return hip_status(ctx, launch_gemm(g, EPI_STORE, ctx->stream), "linear");
+}
+
+spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
+                             const void* w, int n, void* out, const int32_t* pos, const float* table) {
+  CHECK_CTX();
+  spts_status st = gemm_shape_ok(ctx, m, kdim, n);
+  if (st != SPTS_OK) return st;
+  if (m == 0) return SPTS_OK;
+  REQUIRE_PTR(a); REQUIRE_PTR(w); REQUIRE_PTR(out); REQUIRE_PTR(pos); REQUIRE_PTR(table);
+  REQUIRE_ALIGN(a); REQUIRE_ALIGN(w); REQUIRE_ALIGN(out); REQUIRE_ALIGN(table);
+  GemmArgs g{};
+  g.a = reinterpret_cast<const uint16_t*>(a); g.a_rows = a_rows; g.m = m; g.k = kdim; g.lda = kdim;
+  g.b0 = reinterpret_cast<const uint16_t*>(w); g.ldb = kdim; g.n = n;
+  g.out = out; g.ldc = n; g.pos = pos; g.rope_table = table;
+  return hip_status(ctx, launch_gemm(g, EPI_ROPE, ctx->stream), "linear_rope");
+}
+
+spts_status spts_rope_table(spts_ctx* ctx, int max_pos, int dh, double theta, float* table) {
+  CHECK_CTX();
+  REQUIRE_PTR(table);
+  REQUIRE(max_pos > 0 && dh > 0 && dh % 2 == 0 && theta > 0, SPTS_ERR_SHAPE, "bad rope table shape");
+  return hip_status(ctx, launch_rope_table(max_pos, dh, theta, table, ctx->stream), "rope_table");
+}
+
+spts_status spts_rmsnorm(spts_ctx* ctx, const void* x, int n, int d, float eps, void* out) {
+  CHECK_CTX();
+  REQUIRE(n >= 0 && d > 0 && d % 8 == 0, SPTS_ERR_SHAPE, "rmsnorm needs d %% 8 == 0");
+  if (n == 0) return SPTS_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(out);
+  REQUIRE_ALIGN(x); REQUIRE_ALIGN(out);
+  return hip_status(ctx, launch_rmsnorm(reinterpret_cast<const uint16_t*>(x), n, d, eps,
+                                        reinterpret_cast<uint16_t*>(out), ctx->stream), "rmsnorm");
+}
+
+// ------------------------------------------------------------------------ LTP
+
+spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const void* v_t, int n, int d,
+                           int r, float* score) {
+  CHECK_CTX();
+  REQUIRE(n >= 0 && d > 0 && r > 0, SPTS_ERR_SHAPE, "bad LTP sizes");
+  REQUIRE(d % 256 == 0 && r % 256 == 0, SPTS_ERR_UNSUPPORTED, "LTP needs d %% 256 == 0 and r %% 256 == 0");
+  if (n == 0) return SPTS_OK;
+  REQUIRE_PTR(z); REQUIRE_PTR(u_t); REQUIRE_PTR(v_t); REQUIRE_PTR(score);
+  REQUIRE_ALIGN(z); REQUIRE_ALIGN(u_t); REQUIRE_ALIGN(v_t); REQUIRE_ALIGN(score);
+  const size_t need = spts_ltp_probe_workspace(n, d, r);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  uint16_t* t2 = reinterpret_cast<uint16_t*>(ctx->ws);
+  const size_t t2_bytes = ((size_t)n * 2 * r * 2 + 255) & ~(size_t)255;
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + t2_bytes);
+  // T = z U, stored as bf16 hi + lo halves [n, 2r]
+  GemmArgs g1{};
+  g1.a = reinterpret_cast<const uint16_t*>(z); g1.m = n; g1.k = d; g1.lda = d;
+  g1.b0 = reinterpret_cast<const uint16_t*>(u_t); g1.ldb = d; g1.n = r;
+  g1.out = t2; g1.ldc = 2 * r;
+  hipError_t e = launch_gemm(g1, EPI_SPLIT, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe (z U)");
+  // (T_hi + T_lo) V: inner dimension 2r with V's columns read modulo r
+  GemmArgs g2{};
+  g2.a = t2; g2.m = n; g2.k = 2 * r; g2.lda = 2 * r;
+  g2.b0 = reinterpret_cast<const uint16_t*>(v_t); g2.ldb = r; g2.kwrap = r; g2.n = d;
+  g2.out = part; g2.ldc = d / 256;
+  e = launch_gemm(g2, EPI_SUMSQ, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe (T V)");
+  return hip_status(ctx, launch_rowsum_sqrt(part, n, d / 256, score, ctx->stream), "ltp_probe (norm)");
+}
+
+// ------------------------------------------------------------------------ FFN
+
+spts_status spts_reduced_ffn(spts_ctx* ctx, const void* z, const int32_t* rows, const void* w_gate,
+                             const void* w_up, const void* w_down, int k, int d, int f, void* y_sel,
+                             const int32_t* y_rows, int accumulate) {
+  CHECK_CTX();
+  REQUIRE(k >= 0 && d > 0 && f > 0, SPTS_ERR_SHAPE, "bad FFN sizes");
+  REQUIRE(d % 256 == 0 && f % 128 == 0, SPTS_ERR_UNSUPPORTED, "FFN needs d %% 256 == 0 and f %% 128 == 0");
+  REQUIRE(accumulate == 0 || accumulate == 1, SPTS_ERR_INVALID, "accumulate must be 0 or 1");
+  if (k == 0) return SPTS_OK;
+  REQUIRE_PTR(z); REQUIRE_PTR(w_gate); REQUIRE_PTR(w_up); REQUIRE_PTR(w_down); REQUIRE_PTR(y_sel);
+  REQUIRE_ALIGN(z); REQUIRE_ALIGN(w_gate); REQUIRE_ALIGN(w_up); REQUIRE_ALIGN(w_down); REQUIRE_ALIGN(y_sel);
+  if (rows) REQUIRE_ALIGN(rows);
+  if (y_rows) REQUIRE_ALIGN(y_rows);
+  const size_t need = spts_reduced_ffn_workspace(k, f);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  uint16_t* H = reinterpret_cast<uint16_t*>(ctx->ws);
+  GemmArgs g1{};
+  g1.a = reinterpret_cast<const uint16_t*>(z); g1.a_rows = rows; g1.m = k; g1.k = d; g1.lda = d;
+  g1.b0 = reinterpret_cast<const uint16_t*>(w_gate); g1.b1 = reinterpret_cast<const uint16_t*>(w_up);
+  g1.ldb = d; g1.n = 2 * f; g1.out = H; g1.ldc = f;
+  hipError_t e = launch_gemm(g1, EPI_SWIGLU, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "reduced_ffn (gate/up)");
+  GemmArgs g2{};
+  g2.a = H; g2.m = k; g2.k = f; g2.lda = f;
+  g2.b0 = reinterpret_cast<const uint16_t*>(w_down); g2.ldb = f; g2.n = d;
+  g2.out = y_sel; g2.ldc = d; g2.out_rows = y_rows; g2.accumulate = accumulate;
+  return hip_status(ctx, launch_gemm(g2, EPI_STORE, ctx->stream), "reduced_ffn (down)");
+}
+
+// ------------------------------------------------------------------------ MSDP
+
+spts_status spts_msdp_stage(spts_ctx* ctx, const float* scores, int n_prev, int budget, int n_forced,
+                            const int32_t* pos_prev, int32_t* keep, int32_t* pos_new, const void* x_prev,
+                            void* x_new, int d) {
+  CHECK_CTX();
+  REQUIRE_PTR(scores); REQUIRE_PTR(pos_prev); REQUIRE_PTR(keep); REQUIRE_PTR(pos_new);
+  REQUIRE_ALIGN(scores); REQUIRE_ALIGN(pos_prev); REQUIRE_ALIGN(keep); REQUIRE_ALIGN(pos_new);
+  REQUIRE(n_prev >= 1 && budget >= n_forced && n_forced >= 0 && budget <= n_prev, SPTS_ERR_SHAPE,
+          "need n_forced <= budget <= n_prev (n_prev=%d budget=%d n_forced=%d)", n_prev, budget, n_forced);
+  if (x_prev) {
+    REQUIRE_PTR(x_new); REQUIRE_ALIGN(x_prev); REQUIRE_ALIGN(x_new);
+    REQUIRE(d > 0 && d % 8 == 0, SPTS_ERR_SHAPE, "msdp_stage needs d %% 8 == 0");
+  }
+  const size_t need = topk_workspace(n_prev);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  hipError_t e = launch_topk(scores, nullptr, 0.f, 0.f, n_prev, budget, n_forced, keep, nullptr, ctx->ws,
+                             ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "msdp_stage (select)");
+  e = launch_gather(pos_prev, keep, budget, 4, pos_new, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "msdp_stage (positions)");
+  if (x_prev) {
+    e = launch_gather(x_prev, keep, budget, (long)d * 2, x_new, ctx->stream);
+    if (e != hipSuccess) return hip_status(ctx, e, "msdp_stage (rows)");
+  }
+  return SPTS_OK;
+}
+
+}  // extern "C"

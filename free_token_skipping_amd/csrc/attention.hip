@@ -1,0 +1,563 @@
+// PAP probe scores and reduced (selected-query) causal attention, gfx950.
+//
+// Both use v_mfma_f32_32x32x16_bf16 with key/value tiles of 64 tokens staged
+// in LDS and shared by the 4 waves of a workgroup; the 4 waves are 4 query
+// heads of one GQA group, so each K/V tile is read from HBM once per group.
+//
+// Layout trick (reduced attention): logits are formed transposed,
+// S^T = K Q^T, so a lane owns one query and the softmax statistics are
+// lane-local.  The K rows fed to the MFMA are permuted (bits 2 and 3 of the
+// row index swapped) so that the 16 logits a lane holds per 32-key tile are
+// two runs of 8 CONSECUTIVE keys; those become, after exp and bf16
+// rounding, the MFMA B operand of O^T = V^T P^T with no lane exchange, and
+// the matching V^T fragment is a single 16-byte LDS read from a transposed
+// V tile.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace spts {
+namespace {
+
+constexpr int KT = 64;          // keys per LDS tile
+constexpr int DH = 128;
+
+// K tile [64 keys][128] in LDS: 16-byte chunk XOR-swizzled with bits {0,1,3}
+// of the key row (the rows 8 neighbouring lanes read under the permutation).
+__device__ __forceinline__ int kswz(int key, int chunk) {
+  const int f = (key & 3) | ((key & 8) >> 1);
+  return key * DH + ((chunk ^ f) << 3);
+}
+// V^T tile [128 dh][64 keys] in LDS: chunk XOR (dh & 7).
+__device__ __forceinline__ int vswz(int d, int chunk) { return d * KT + ((chunk ^ (d & 7)) << 3); }
+// MFMA A-row -> key row within a 32-key tile: swap index bits 2 and 3.
+__device__ __forceinline__ int perm32(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// Stage one K tile (and optionally the transposed V tile) of KV head g.
+// Rows >= n are clamped to n-1 (they are always masked).
+struct TileRegs { u32x4 k[4]; u32x4 v[4]; };
+
+__device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* k, const uint16_t* v, int j0,
+                                          int n, int Hkv, int g, int tid, bool with_v) {
+  const long row_stride = (long)Hkv * DH;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {        // K: thread -> row tid/16 + 16 i, chunk tid%16
+    int j = j0 + (tid >> 4) + 16 * i;
+    j = j < n ? j : n - 1;
+    t.k[i] = ld16(k + j * row_stride + g * DH + (tid & 15) * 8);
+  }
+  if (with_v) {                        // V: thread -> keys 4*(tid%16)+q, dh chunk tid/16
+    const int kq4 = tid & 15, dc = tid >> 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int j = j0 + kq4 * 4 + q;
+      j = j < n ? j : n - 1;
+      t.v[q] = ld16(v + j * row_stride + g * DH + dc * 8);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* ks, uint16_t* vts, int tid,
+                                           bool with_v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st16(ks + kswz((tid >> 4) + 16 * i, tid & 15), t.k[i]);
+  if (with_v) {
+    const int kq4 = tid & 15, dc = tid >> 4;
+    // transpose 4 keys x 8 dh -> 8 rows of 4 keys (8 bytes each)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const bool hiw = e & 1;
+      uint32_t x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = hiw ? (t.v[q][w] >> 16) : (t.v[q][w] & 0xFFFFu);
+      u32x2 out;
+      out[0] = x[0] | (x[1] << 16);
+      out[1] = x[2] | (x[3] << 16);
+      *reinterpret_cast<u32x2*>(vts + vswz(dc * 8 + e, kq4 >> 1) + (kq4 & 1) * 4) = out;
+    }
+  }
+}
+
+// ============================================================ reduced attention
+// grid: (ceil(kq/64), Hq/4); block 256 = 4 waves = 4 heads of one KV group.
+// Each wave: 64 queries (two 32-query column tiles) of one head.
+__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const uint16_t* __restrict__ q,
+                                                           const int32_t* __restrict__ idx,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v, int kq,
+                                                           int n, int Hq, int Hkv, float sl2,
+                                                           uint16_t* __restrict__ o) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][DH * KT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int nqb = (kq + 63) >> 6;
+  const int qb = nqb - 1 - (int)blockIdx.x;          // latest (longest) query blocks first
+  const int h = blockIdx.y * 4 + wave;
+  const int g = (blockIdx.y * 4) / (Hq / Hkv);
+  const int q0 = qb * 64;
+
+  int qi[2], qpos[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int i = q0 + c * 32 + l32;
+    qi[c] = i < kq ? i : kq - 1;
+    qpos[c] = idx[qi[c]];
+  }
+  const int kmax = idx[min(q0 + 63, kq - 1)];
+  const int ntiles = kmax / KT + 1;
+
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)qi[c] * Hq + h) * DH + kk * 16 + half * 8);
+
+  f32x16 oacc[2][4];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[c][d][r] = 0.f;
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+  TileRegs tr;
+  load_tile(tr, k, v, 0, n, Hkv, g, tid, true);
+  store_tile(tr, Ks[0], Vs[0], tid, true);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int j0 = t * KT;
+    if (t + 1 < ntiles) load_tile(tr, k, v, j0 + KT, n, Hkv, g, tid, true);
+    const uint16_t* ks = Ks[buf];
+    const uint16_t* vs = Vs[buf];
+
+    // S^T tiles: rows = keys (permuted), cols = queries
+    f32x16 s[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[c][kt][r] = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) s[c][kt] = mfma32x32x16(kf, qf[c][kk], s[c][kt]);
+      }
+
+    // online softmax per query (lane); key of reg r = j0 + kt*32 + (r>>3)*16 + half*8 + (r&7)
+    bf16x8 pf[2][4];
+    const bool need_mask = (j0 + KT - 1) > idx[min(q0, kq - 1)];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[c][kt][r] * sl2;
+          if (need_mask) {
+            const int key = j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7);
+            if (key > qpos[c]) x = -INFINITY;
+          }
+          s[c][kt][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[c], mx);
+      const float alpha = exp2f(m[c] - mnew);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          bf16x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = exp2f(s[c][kt][sub * 8 + e] - mnew);
+            rs += p;
+            pv[e] = (__bf16)p;
+          }
+          pf[c][kt * 2 + sub] = pv;
+        }
+      rs += __shfl_xor(rs, 32);
+      l[c] = l[c] * alpha + rs;
+      m[c] = mnew;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[c][d][r] *= alpha;
+    }
+
+    // O^T += V^T P^T : rows = dh, cols = queries, k = 64 keys in 4 steps
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + vswz(d * 32 + l32, ks4 * 2 + half));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) oacc[c][d] = mfma32x32x16(vf, pf[c][ks4], oacc[c][d]);
+      }
+
+    if (t + 1 < ntiles) store_tile(tr, Ks[buf ^ 1], Vs[buf ^ 1], tid, true);
+    __syncthreads();
+  }
+
+  // normalise and store: lane = query, reg r of dh tile d -> dh d*32 + (r>>2)*8 + half*4 + (r&3)
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (q0 + c * 32 + l32 >= kq) continue;
+    const float inv = 1.0f / l[c];
+    uint16_t* orow = o + ((long)qi[c] * Hq + h) * DH;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        u32x2 w;
+        w[0] = pack2bf(oacc[c][d][qd * 4 + 0] * inv, oacc[c][d][qd * 4 + 1] * inv);
+        w[1] = pack2bf(oacc[c][d][qd * 4 + 2] * inv, oacc[c][d][qd * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d * 32 + qd * 8 + half * 4) = w;
+      }
+  }
+}
+
+// =============================================================== PAP probe
+// Pass 1: per key chunk of 256, per head, partial (max, sum) of the probe
+// softmax in log2 units.  grid (ceil(n/256), Hq/4), 4 waves = 4 heads.
+constexpr int CHUNK = 256;
+
+template <int PT>   // probe column tiles of 32 (P = 32*PT)
+__global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k, int n,
+                                                             int Hq, int Hkv, float sl2,
+                                                             float* __restrict__ part_m,
+                                                             float* __restrict__ part_l) {
+  constexpr int P = 32 * PT;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int h = blockIdx.y * 4 + wave;
+  const int g = (blockIdx.y * 4) / (Hq / Hkv);
+  const int chunk = blockIdx.x;
+
+  bf16x8 qf[PT][8];
+#pragma unroll
+  for (int c = 0; c < PT; ++c)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)(c * 32 + l32) * Hq + h) * DH + kk * 16 + half * 8);
+  float m[PT], l[PT];
+#pragma unroll
+  for (int c = 0; c < PT; ++c) { m[c] = -INFINITY; l[c] = 0.f; }
+
+  TileRegs tr;
+  for (int t = 0; t < CHUNK / KT; ++t) {
+    const int j0 = chunk * CHUNK + t * KT;
+    if (j0 >= n) break;
+    load_tile(tr, k, nullptr, j0, n, Hkv, g, tid, false);
+    __syncthreads();
+    store_tile(tr, Ks, nullptr, tid, false);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < PT; ++c) {
+      const int prow = n - P + c * 32 + l32;
+      f32x16 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+          s[kt] = mfma32x32x16(kf, qf[c][kk], s[kt]);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7);
+          float x = s[kt][r] * sl2;
+          if (key > prow) x = -INFINITY;
+          s[kt][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      const float mnew = fmaxf(m[c], mx);
+      if (mnew == -INFINITY) continue;     // nothing visible yet for this probe
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rs += exp2f(s[kt][r] - mnew);
+      l[c] = l[c] * exp2f(m[c] - mnew) + rs;
+      m[c] = mnew;
+    }
+  }
+  // merge the two half-waves (they hold different keys of the same probes)
+#pragma unroll
+  for (int c = 0; c < PT; ++c) {
+    const float m2 = __shfl_xor(m[c], 32), l2 = __shfl_xor(l[c], 32);
+    const float mt = fmaxf(m[c], m2);
+    float lt = 0.f;
+    if (mt != -INFINITY) lt = l[c] * exp2f(m[c] - mt) + l2 * exp2f(m2 - mt);
+    if (half == 0) {
+      const long o = ((long)chunk * Hq + h) * P + c * 32 + l32;
+      part_m[o] = mt;
+      part_l[o] = lt;
+    }
+  }
+}
+
+// Pass 1b: combine chunk partials -> per (head, probe) max and 1/sum.
+__global__ void probe_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ part_l,
+                                     int nchunks, int HP, float* __restrict__ fin_m,
+                                     float* __restrict__ fin_il) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= HP) return;
+  float mt = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) mt = fmaxf(mt, part_m[(long)c * HP + i]);
+  float lt = 0.f;
+  for (int c = 0; c < nchunks; ++c) {
+    const float mc = part_m[(long)c * HP + i];
+    if (mc != -INFINITY) lt += part_l[(long)c * HP + i] * exp2f(mc - mt);
+  }
+  fin_m[i] = mt;
+  fin_il[i] = 1.0f / lt;
+}
+
+// Pass 2: column sums of the normalised probe softmax for one key chunk and
+// one head quad; logits formed as S = Q K^T so a lane owns one key.
+template <int PT>
+__global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k, int n,
+                                                              int Hq, int Hkv, float sl2,
+                                                              const float* __restrict__ fin_m,
+                                                              const float* __restrict__ fin_il,
+                                                              float* __restrict__ quad_sum) {
+  constexpr int P = 32 * PT;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
+  __shared__ __attribute__((aligned(16))) float st_m[4][P];
+  __shared__ __attribute__((aligned(16))) float st_il[4][P];
+  __shared__ float red[4][KT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int h = blockIdx.y * 4 + wave;
+  const int g = (blockIdx.y * 4) / (Hq / Hkv);
+  const int chunk = blockIdx.x;
+
+  for (int i = tid; i < 4 * P; i += 256) {
+    const int hh = blockIdx.y * 4 + i / P, p = i % P;
+    st_m[i / P][p] = fin_m[hh * P + p];
+    st_il[i / P][p] = fin_il[hh * P + p];
+  }
+  bf16x8 qf[PT][8];
+#pragma unroll
+  for (int c = 0; c < PT; ++c)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)(c * 32 + l32) * Hq + h) * DH + kk * 16 + half * 8);
+
+  TileRegs tr;
+  for (int t = 0; t < CHUNK / KT; ++t) {
+    const int j0 = chunk * CHUNK + t * KT;
+    if (j0 >= n) break;
+    load_tile(tr, k, nullptr, j0, n, Hkv, g, tid, false);
+    __syncthreads();
+    store_tile(tr, Ks, nullptr, tid, false);
+    __syncthreads();
+    float colsum[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = j0 + kt * 32 + perm32(l32);          // this lane's key column
+      bf16x8 kf[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        kf[kk] = *reinterpret_cast<const bf16x8*>(Ks + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+#pragma unroll
+      for (int c = 0; c < PT; ++c) {
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) s = mfma32x32x16(qf[c][kk], kf[kk], s);
+        // reg r -> probe row p = c*32 + (r>>2)*8 + half*4 + (r&3)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int pb = c * 32 + qd * 8 + half * 4;
+          const f32x4 mm = *reinterpret_cast<const f32x4*>(&st_m[wave][pb]);
+          const f32x4 il = *reinterpret_cast<const f32x4*>(&st_il[wave][pb]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int prow = n - P + pb + e;
+            if (key <= prow) colsum[kt] += exp2f(s[qd * 4 + e] * sl2 - mm[e]) * il[e];
+          }
+        }
+      }
+    }
+    // add the other half-wave (other probe rows), then the 4 heads
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) colsum[kt] += __shfl_xor(colsum[kt], 32);
+    if (half == 0) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) red[wave][kt * 32 + perm32(l32)] = colsum[kt];
+    }
+    __syncthreads();
+    if (tid < KT && j0 + tid < n)
+      quad_sum[(long)blockIdx.y * n + j0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  }
+}
+
+// Final: S[j] = sum over head quads, fixed order.
+__global__ void quad_reduce_kernel(const float* __restrict__ quad_sum, int nq, int n, float* __restrict__ s) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  float t = 0.f;
+  for (int i = 0; i < nq; ++i) t += quad_sum[(long)i * n + j];
+  s[j] = t;
+}
+
+// ================================================== fp32 paths (small cases)
+// One thread per (head, probe): causal row max and sum.
+__global__ void probe_stats_f32_kernel(const float* q, const float* k, int n, int P, int Hq, int Hkv,
+                                       int dh, float scale, float* fin_m, float* fin_il) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Hq * P) return;
+  const int h = i / P, p = i % P, g = h / (Hq / Hkv), row = n - P + p;
+  const float* qr = q + ((long)p * Hq + h) * dh;
+  float mx = -INFINITY, sum = 0.f;
+  for (int j = 0; j <= row; ++j) {
+    const float* kr = k + ((long)j * Hkv + g) * dh;
+    float dot = 0.f;
+    for (int e = 0; e < dh; ++e) dot += qr[e] * kr[e];
+    const float x = dot * scale;
+    if (x > mx) { sum = sum * expf(mx - x) + 1.f; mx = x; } else { sum += expf(x - mx); }
+  }
+  fin_m[h * P + p] = mx;
+  fin_il[h * P + p] = 1.f / sum;
+}
+
+__global__ void probe_colsum_f32_kernel(const float* q, const float* k, int n, int P, int Hq, int Hkv,
+                                        int dh, float scale, const float* fin_m, const float* fin_il,
+                                        float* s) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  float tot = 0.f;
+  for (int h = 0; h < Hq; ++h) {
+    const int g = h / (Hq / Hkv);
+    const float* kr = k + ((long)j * Hkv + g) * dh;
+    for (int p = 0; p < P; ++p) {
+      if (j > n - P + p) continue;
+      const float* qr = q + ((long)p * Hq + h) * dh;
+      float dot = 0.f;
+      for (int e = 0; e < dh; ++e) dot += qr[e] * kr[e];
+      tot += expf(dot * scale - fin_m[h * P + p]) * fin_il[h * P + p];
+    }
+  }
+  s[j] = tot;
+}
+
+// One 64-lane block per (query, head); lane e owns dh elements e and e+64.
+__global__ void attn_f32_kernel(const float* q, const int32_t* idx, const float* k, const float* v,
+                                int kq, int n, int Hq, int Hkv, int dh, float scale, float* o) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int g = h / (Hq / Hkv), row = idx[i];
+  const float* qr = q + ((long)i * Hq + h) * dh;
+  const float q0 = lane < dh ? qr[lane] : 0.f;
+  const float q1 = lane + 64 < dh ? qr[lane + 64] : 0.f;
+  float mx = -INFINITY, sum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int j = 0; j <= row; ++j) {
+    const float* kr = k + ((long)j * Hkv + g) * dh;
+    const float* vr = v + ((long)j * Hkv + g) * dh;
+    float part = (lane < dh ? q0 * kr[lane] : 0.f) + (lane + 64 < dh ? q1 * kr[lane + 64] : 0.f);
+    const float x = wave_sum(part) * scale;
+    const float mnew = fmaxf(mx, x);
+    const float a = expf(mx - mnew), p = expf(x - mnew);
+    sum = sum * a + p;
+    o0 = o0 * a + (lane < dh ? p * vr[lane] : 0.f);
+    o1 = o1 * a + (lane + 64 < dh ? p * vr[lane + 64] : 0.f);
+    mx = mnew;
+  }
+  float* orow = o + ((long)i * Hq + h) * dh;
+  if (lane < dh) orow[lane] = o0 / sum;
+  if (lane + 64 < dh) orow[lane + 64] = o1 / sum;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+size_t probe_workspace(int n, int P, int Hq) {
+  const size_t nchunks = (size_t)(n + CHUNK - 1) / CHUNK;
+  const size_t HP = (size_t)Hq * P;
+  // part_m, part_l [nchunks*HP]; fin_m, fin_il [HP]; quad_sum [Hq/4 * n]
+  size_t b = 2 * nchunks * HP * 4 + 2 * HP * 4 + (size_t)((Hq + 3) / 4) * n * 4;
+  return (b + 255) & ~(size_t)255;
+}
+
+hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P, int Hq, int Hkv,
+                             float scale, float* scores, void* ws, hipStream_t s) {
+  const int nchunks = (n + CHUNK - 1) / CHUNK;
+  const long HP = (long)Hq * P;
+  float* part_m = reinterpret_cast<float*>(ws);
+  float* part_l = part_m + nchunks * HP;
+  float* fin_m = part_l + nchunks * HP;
+  float* fin_il = fin_m + HP;
+  float* quad = fin_il + HP;
+  const float sl2 = scale * kLog2e;
+  const dim3 grid(nchunks, Hq / 4);
+  switch (P / 32) {
+#define SPTS_PROBE_CASE(PT)                                                                        \
+  case PT:                                                                                         \
+    hipLaunchKernelGGL(probe_stats_kernel<PT>, grid, dim3(256), 0, s, q, k, n, Hq, Hkv, sl2,      \
+                       part_m, part_l);                                                            \
+    hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 255) / 256), dim3(256), 0, s, part_m,     \
+                       part_l, nchunks, (int)HP, fin_m, fin_il);                                   \
+    hipLaunchKernelGGL(probe_colsum_kernel<PT>, grid, dim3(256), 0, s, q, k, n, Hq, Hkv, sl2,     \
+                       fin_m, fin_il, quad);                                                       \
+    break;
+    SPTS_PROBE_CASE(1)
+    SPTS_PROBE_CASE(2)
+    SPTS_PROBE_CASE(4)
+#undef SPTS_PROBE_CASE
+    default: return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(quad_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, quad, Hq / 4, n, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_f32(const float* q, const float* k, int n, int P, int Hq, int Hkv, int dh,
+                            float scale, float* scores, void* ws, hipStream_t s) {
+  float* fin_m = reinterpret_cast<float*>(ws);
+  float* fin_il = fin_m + Hq * P;
+  hipLaunchKernelGGL(probe_stats_f32_kernel, dim3((Hq * P + 127) / 128), dim3(128), 0, s, q, k, n, P,
+                     Hq, Hkv, dh, scale, fin_m, fin_il);
+  hipLaunchKernelGGL(probe_colsum_f32_kernel, dim3((n + 127) / 128), dim3(128), 0, s, q, k, n, P, Hq,
+                     Hkv, dh, scale, fin_m, fin_il, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const uint16_t* q, const int32_t* idx, const uint16_t* k,
+                            const uint16_t* v, int kq, int n, int Hq, int Hkv, float scale,
+                            uint16_t* o, hipStream_t s) {
+  const dim3 grid((kq + 63) / 64, Hq / 4);
+  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(256), 0, s, q, idx, k, v, kq, n, Hq, Hkv,
+                     scale * kLog2e, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const float* q, const int32_t* idx, const float* k, const float* v,
+                           int kq, int n, int Hq, int Hkv, int dh, float scale, float* o,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(kq, Hq), dim3(64), 0, s, q, idx, k, v, kq, n, Hq, Hkv, dh,
+                     scale, o);
+  return hipGetLastError();
+}
+
+}  // namespace spts

@@ -1,0 +1,74 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Every launcher enqueues on the given stream and returns the
+// launch status; shapes have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spts {
+
+// ------------------------------------------------------------------ GEMM
+// C = A * B^T, A [m, k] bf16 (rows optionally gathered), B [n, k] bf16.
+enum GemmEpilogue : int {
+  EPI_STORE = 0,   // bf16 out[o(i), c] (= or +=), o(i) = out_rows ? out_rows[i] : i
+  EPI_ROPE = 1,    // bf16 out with rotary embedding on 128-wide heads
+  EPI_SWIGLU = 2,  // bf16 out = silu(A Wg^T) * (A Wu^T); b0 = Wg, b1 = Wu
+  EPI_SPLIT = 3,   // fp32 result t written as bf16 pair hi=bf16(t), lo=bf16(t-hi)
+  EPI_SUMSQ = 4,   // fp32 out[i, tile_n] = sum over the tile's 256 columns of c^2
+};
+
+struct GemmArgs {
+  const uint16_t* a;        // A base
+  const int32_t* a_rows;    // gather rows of A (nullable)
+  int m, k, lda;
+  const uint16_t* b0;       // B (or gate weight)
+  const uint16_t* b1;       // up weight (SWIGLU only)
+  int ldb;
+  int kwrap;                // if > 0: B column = (k index) mod kwrap
+  int n;                    // B rows covered (SWIGLU: output columns * 2)
+  void* out;
+  int ldc;
+  const int32_t* out_rows;  // scatter rows of out (nullable)
+  int accumulate;
+  const int32_t* pos;       // ROPE: original position per A row (indexed like A rows)
+  const float* rope_table;  // ROPE: [max_pos, 64, 2]
+};
+
+hipError_t launch_gemm(const GemmArgs& g, int epilogue, hipStream_t s);
+
+// ------------------------------------------------------------ attention
+hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P, int Hq, int Hkv,
+                             float scale, float* scores, void* ws, hipStream_t s);
+hipError_t launch_probe_f32(const float* q, const float* k, int n, int P, int Hq, int Hkv, int dh,
+                            float scale, float* scores, void* ws, hipStream_t s);
+size_t probe_workspace(int n, int P, int Hq);
+
+hipError_t launch_attn_bf16(const uint16_t* q, const int32_t* idx, const uint16_t* k,
+                            const uint16_t* v, int kq, int n, int Hq, int Hkv, float scale,
+                            uint16_t* o, hipStream_t s);
+hipError_t launch_attn_f32(const float* q, const int32_t* idx, const float* k, const float* v,
+                           int kq, int n, int Hq, int Hkv, int dh, float scale, float* o,
+                           hipStream_t s);
+
+// --------------------------------------------------------------- select
+size_t topk_workspace(int n);
+hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, int n, int k,
+                       int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s);
+
+// ------------------------------------------------------------- row ops
+hipError_t launch_gather(const void* src, const int32_t* idx, int k, long row_bytes, void* dst,
+                         hipStream_t s);
+hipError_t launch_scatter(const void* src, const int32_t* idx, int k, long row_bytes, void* dst,
+                          hipStream_t s);
+hipError_t launch_scatter_add_bf16(const uint16_t* src, const int32_t* idx, int k, int row_elems,
+                                   uint16_t* dst, hipStream_t s);
+hipError_t launch_scatter_add_f32(const float* src, const int32_t* idx, int k, int row_elems,
+                                  float* dst, hipStream_t s);
+hipError_t launch_scatter_add_i32(const int32_t* src, const int32_t* idx, int k, int row_elems,
+                                  int32_t* dst, hipStream_t s);
+hipError_t launch_rmsnorm(const uint16_t* x, int n, int d, float eps, uint16_t* out, hipStream_t s);
+hipError_t launch_rope_table(int max_pos, int dh, double theta, float* table, hipStream_t s);
+hipError_t launch_rowsum_sqrt(const float* partial, int n, int parts, float* out, hipStream_t s);
+
+}  // namespace spts

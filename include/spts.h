@@ -1,0 +1,215 @@
+/*
+ * spts.h -- C ABI of the SPTS prefill hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Probe and Skip: Self-Predictive Token Skipping for Efficient
+ * Long-Context LLM Inference" (Wu, Wang, Jin, Chen, Wang), cited as [SPTS].
+ * Partial Attention Probing (PAP) scores tokens for the attention block,
+ * Low-rank Transformation Probing (LTP) scores them for the FFN block, the
+ * selected tokens run a reduced attention / reduced SwiGLU, skipped tokens
+ * keep their residual, and Multi-Stage Delayed Pruning (MSDP) shrinks the
+ * candidate set at stage boundaries ([SPTS] abstract, Fig. 2).
+ *
+ * Conventions shared by every call
+ *   - Tensors are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or retains them beyond the call's stream work.
+ *   - Layouts are row-major and token-major.  Weights use the nn.Linear
+ *     layout [out_features, in_features].  "bf16" is IEEE bfloat16 stored in
+ *     16 bits; accumulation is fp32.
+ *   - Index arrays are int32, strictly ascending, in [0, n).
+ *   - Every compute call is asynchronous on the context's stream (a HIP
+ *     stream borrowed from the caller, never destroyed here) and returns a
+ *     status.  Arguments are validated on the host before anything is
+ *     launched; a failing validation launches nothing.  A launch failure
+ *     returns SPTS_ERR_HIP; faults inside kernels surface at the caller's
+ *     next synchronisation or at spts_check().
+ *   - Calls that need temporary device memory take it from the context's
+ *     workspace (spts_set_workspace); the required size is given by the
+ *     matching *_workspace() query, and a smaller workspace returns
+ *     SPTS_ERR_NOMEM.  Each call uses the workspace from offset 0, so calls
+ *     on one context must not run concurrently (one context per stream).
+ *   - Pointers must be 16-byte aligned (SPTS_ERR_ALIGN otherwise).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef SPTS_H
+#define SPTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spts_status {
+    SPTS_OK = 0,
+    SPTS_ERR_INVALID = 1,      /* null pointer, bad context, bad enum      */
+    SPTS_ERR_SHAPE = 2,        /* sizes inconsistent or out of range       */
+    SPTS_ERR_DTYPE = 3,        /* dtype not accepted by this call          */
+    SPTS_ERR_ALIGN = 4,        /* pointer not 16-byte aligned              */
+    SPTS_ERR_NOMEM = 5,        /* workspace smaller than the call needs    */
+    SPTS_ERR_HIP = 6,          /* HIP runtime reported an error            */
+    SPTS_ERR_UNSUPPORTED = 7   /* valid, but outside what the kernels do   */
+} spts_status;
+
+typedef enum spts_dtype { SPTS_BF16 = 0, SPTS_F32 = 1, SPTS_I32 = 2 } spts_dtype;
+
+typedef struct spts_ctx spts_ctx;
+
+/* ------------------------------------------------------------- context */
+
+/* Create a context bound to `hip_stream` (a hipStream_t; NULL = default
+ * stream).  The stream is borrowed.  Returns SPTS_ERR_INVALID if ctx is NULL. */
+spts_status spts_create(spts_ctx** ctx, void* hip_stream);
+/* Destroy a context (does not synchronise or destroy the stream). */
+spts_status spts_destroy(spts_ctx* ctx);
+/* Rebind the context to another borrowed stream. */
+spts_status spts_set_stream(spts_ctx* ctx, void* hip_stream);
+/* Give the context `bytes` of caller-owned device memory for temporaries. */
+spts_status spts_set_workspace(spts_ctx* ctx, void* dev_ptr, size_t bytes);
+/* Text of the last error on this context ("" if none).  Owned by ctx. */
+const char* spts_last_error(const spts_ctx* ctx);
+/* Name of a status code, e.g. "SPTS_ERR_SHAPE". */
+const char* spts_status_name(spts_status s);
+/* Synchronise the context's stream and report any pending HIP error. */
+spts_status spts_check(spts_ctx* ctx);
+
+/* ------------------------------------------------------ workspace sizes */
+
+size_t spts_probe_attention_workspace(int n, int P, int Hq);
+size_t spts_score_topk_workspace(int n);
+size_t spts_ltp_probe_workspace(int n, int d, int r);
+size_t spts_reduced_ffn_workspace(int k, int f);
+size_t spts_msdp_stage_workspace(int n_prev);
+
+/* ----------------------------------------------------------------- PAP */
+
+/* Partial Attention Probing score ([SPTS] Fig. 2(a), abstract).
+ * The probe rows are the last P of the n current candidate rows; probe p
+ * (row n-P+p) attends keys 0..n-P+p with softmax(scale * q.k), query head h
+ * using key head h / (Hq/Hkv).  Output, for every row j:
+ *     scores[j] = sum over heads h and probes p of that softmax weight.
+ *   q_probe [P, Hq, dh]   dtype
+ *   k       [n, Hkv, dh]  dtype
+ *   scores  [n]           float32, written
+ * dtype SPTS_BF16: dh == 128, P % 32 == 0, (Hq/Hkv) % 4 == 0 (MFMA path).
+ * dtype SPTS_F32 : dh <= 128, any P (plain fp32 path for small cases).
+ * Workspace: spts_probe_attention_workspace(n, P, Hq). */
+spts_status spts_probe_attention(spts_ctx* ctx, spts_dtype dtype, const void* q_probe,
+                                 const void* k, int n, int P, int Hq, int Hkv, int dh,
+                                 float scale, float* scores);
+
+/* --------------------------------------------------------------- select */
+
+/* Top-k token selection ([SPTS] Fig. 2(a)(b); fusion: Table D "MaxNorm-Add").
+ * Ranking score: s_a if s_b == NULL, else the float32 value
+ *     c = fl(fl(w_a*fl(s_a/max s_a)) + fl(w_b*fl(s_b/max s_b)))
+ * (a term is 0 when its max is not positive).  The last n_forced rows are
+ * always kept and count toward k; the other k-n_forced rows are the largest
+ * ranking scores among rows 0..n-n_forced-1, ties to the lower index; NaN
+ * ranks lowest and -0 equals +0.  idx[0..min(k,n)-1] receives the kept rows
+ * in ascending order.  fused_out [n] (optional) receives c.
+ * Requires 0 <= n_forced <= k, n_forced <= n, n >= 1.
+ * Workspace: spts_score_topk_workspace(n). */
+spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, float w_a,
+                            float w_b, int n, int k, int n_forced, int32_t* idx,
+                            float* fused_out);
+
+/* --------------------------------------------------------- gather/scatter */
+
+/* dst[i, :] = src[idx[i], :] for i < k; rows of row_elems elements.
+ * dtype BF16, F32 or I32.  src and dst must not overlap. */
+spts_status spts_gather(spts_ctx* ctx, spts_dtype dtype, const void* src, const int32_t* idx,
+                        int k, int row_elems, void* dst);
+
+/* accumulate == 0:  dst[idx[i], :] = src[i, :]
+ * accumulate == 1:  dst[idx[i], :] = dst[idx[i], :] + src[i, :]  (bf16: the
+ *                   sum is formed in fp32 and rounded to bf16 once).
+ * Rows of dst not named in idx are untouched -- the skipped tokens' residual
+ * passes through unchanged ([SPTS] Fig. 2 top).  idx entries distinct. */
+spts_status spts_scatter(spts_ctx* ctx, spts_dtype dtype, const void* src, const int32_t* idx,
+                         int k, int row_elems, void* dst, int accumulate);
+
+/* ----------------------------------------------------- reduced attention */
+
+/* Reduced attention of the selected rows ([SPTS] Fig. 2(a)).  Query i sits
+ * at candidate row idx[i] and attends, causally, rows 0..idx[i] of the keys
+ * and values of ALL n current candidates:
+ *     o_sel[i,h] = sum_{j<=idx[i]} softmax_j(scale*q_sel[i,h].k[j,g]) v[j,g],
+ *     g = h / (Hq/Hkv).
+ *   q_sel [kq, Hq, dh], k and v [n, Hkv, dh], o_sel [kq, Hq, dh]; all dtype.
+ * dtype SPTS_BF16: dh == 128, (Hq/Hkv) % 4 == 0.  SPTS_F32: dh <= 128. */
+spts_status spts_reduced_attention(spts_ctx* ctx, spts_dtype dtype, const void* q_sel,
+                                   const int32_t* idx, const void* k, const void* v, int kq,
+                                   int n, int Hq, int Hkv, int dh, float scale, void* o_sel);
+
+/* ------------------------------------------------------------------ LTP */
+
+/* Low-rank Transformation Probing score ([SPTS] Fig. 2(b), abstract):
+ *     score[m] = || (z[m,:] U) V ||_2,   U = u_t^T (d x r), V = v_t^T (r x d)
+ * with z U kept near fp32 precision (split into two bf16 terms).
+ *   z [n, d] bf16, u_t [r, d] bf16, v_t [d, r] bf16, score [n] float32.
+ * Requires d % 256 == 0, r % 256 == 0.  Workspace: spts_ltp_probe_workspace. */
+spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const void* v_t,
+                           int n, int d, int r, float* score);
+
+/* ------------------------------------------------------------- reduced FFN */
+
+/* Reduced SwiGLU feed-forward ([SPTS] Fig. 2(b)) on k selected rows:
+ *     H = bf16(silu(Z Wg^T) * (Z Wu^T)),  Y = bf16(H Wd^T)
+ * where Z[i] = z[rows[i]] if rows != NULL (gather on load), else z[i].
+ * Output row i goes to y[o(i)], o(i) = y_rows[i] if y_rows != NULL (scatter
+ * on store), else i; accumulate == 1 stores bf16(y[o(i)] + Y[i]) (the
+ * residual add of the selected tokens), accumulate == 0 stores Y[i].
+ *   z [*, d] bf16, w_gate, w_up [f, d], w_down [d, f], y [*, d] bf16.
+ * y must not alias the rows of z being read when y_rows == NULL.
+ * Requires d % 256 == 0, f % 128 == 0.  Workspace (H): spts_reduced_ffn_workspace. */
+spts_status spts_reduced_ffn(spts_ctx* ctx, const void* z, const int32_t* rows, const void* w_gate,
+                             const void* w_up, const void* w_down, int k, int d, int f, void* y,
+                             const int32_t* y_rows, int accumulate);
+
+/* ------------------------------------------------------------------- MSDP */
+
+/* Stage-boundary pruning ([SPTS] Fig. 2(c), Fig. A(c)): keep the `budget`
+ * candidates of the n_prev current ones ranked by `scores` (last n_forced
+ * forced, same rule as spts_score_topk), write
+ *     keep[0..budget-1]  ascending indices into the previous candidate list,
+ *     pos_new[i] = pos_prev[keep[i]],
+ *     x_new[i,:] = x_prev[keep[i],:]   (bf16 rows of d, if x_prev != NULL).
+ * Workspace: spts_msdp_stage_workspace(n_prev). */
+spts_status spts_msdp_stage(spts_ctx* ctx, const float* scores, int n_prev, int budget,
+                            int n_forced, const int32_t* pos_prev, int32_t* keep,
+                            int32_t* pos_new, const void* x_prev, void* x_new, int d);
+
+/* ------------------------------------- projections and layer glue (bf16) */
+
+/* out = A W^T on bf16 MFMA, fp32 accumulate, bf16 result.
+ *   A row i = a[a_rows[i]] if a_rows != NULL (gather on load), else a[i]; A is
+ *   [m, kdim], W is [n, kdim].
+ *   accumulate == 0: out[o(i), :] = bf16(A W^T)[i]
+ *   accumulate == 1: out[o(i), :] = bf16(out[o(i), :] + bf16(A W^T)[i])
+ *   with o(i) = out_rows[i] if out_rows != NULL (scatter on store), else i.
+ * Requires kdim % 64 == 0, n % 256 == 0.  These projections are needed because
+ * every step of the path runs in this library. */
+spts_status spts_linear(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
+                        const void* w, int n, void* out, const int32_t* out_rows, int accumulate);
+
+/* As spts_linear (accumulate 0, no out_rows) with rotary embedding applied to
+ * the fp32 result before rounding: heads of 128 columns, pair (c, c+64) of a
+ * head rotated by table[p, c] = (cos, sin) of p * theta^(-2c/128), where p =
+ * pos[a_rows ? a_rows[i] : i].  table from spts_rope_table. */
+spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m,
+                             int kdim, const void* w, int n, void* out, const int32_t* pos,
+                             const float* table);
+
+/* table[p, c, 0..1] = (cos, sin)(p * theta^(-2c/dh)) for p < max_pos, c < dh/2,
+ * angle formed in fp64 and rounded to fp32. */
+spts_status spts_rope_table(spts_ctx* ctx, int max_pos, int dh, double theta, float* table);
+
+/* out[i,:] = bf16(x[i,:] / sqrt(mean(x[i,:]^2) + eps)), unit gain.  d % 8 == 0. */
+spts_status spts_rmsnorm(spts_ctx* ctx, const void* x, int n, int d, float eps, void* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPTS_H */

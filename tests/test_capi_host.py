@@ -1,0 +1,119 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/spts.h declares, and rejects bad arguments with the documented
+status before launching anything.  No GPU is touched: every call below
+fails validation (fake but aligned pointers never reach a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from free_token_skipping_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spts.h")
+
+OK, INVALID, SHAPE, DTYPE, ALIGN, NOMEM, HIP, UNSUPPORTED = range(8)
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced
+MIS = ctypes.c_void_p(0x10002)        # misaligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spts_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return capi.lib()
+
+
+@pytest.fixture
+def ctx(L):
+    h = ctypes.c_void_p()
+    assert L.spts_create(ctypes.byref(h), None) == OK
+    yield h
+    assert L.spts_destroy(h) == OK
+
+
+def test_every_declared_function_is_exported(L):
+    declared = header_functions()
+    assert len(declared) >= 20
+    assert sorted(capi.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_names(L):
+    assert L.spts_status_name(SHAPE) == b"SPTS_ERR_SHAPE"
+    assert L.spts_status_name(OK) == b"SPTS_OK"
+    assert L.spts_create(None, None) == INVALID
+    assert L.spts_destroy(None) == INVALID
+
+
+def test_workspace_queries(L):
+    assert L.spts_score_topk_workspace(32768) >= 32768 * 4
+    assert L.spts_reduced_ffn_workspace(11469, 14336) >= 11469 * 14336 * 2
+    assert L.spts_ltp_probe_workspace(100, 4096, 256) >= 100 * 512 * 2
+    assert L.spts_probe_attention_workspace(0, 64, 32) == 0
+
+
+def test_probe_validation(L, ctx):
+    f = L.spts_probe_attention
+    assert f(ctx, capi.BF16, None, FAKE, 100, 64, 32, 8, 128, 0.1, FAKE) == INVALID
+    assert f(ctx, capi.BF16, FAKE, FAKE, 50, 64, 32, 8, 128, 0.1, FAKE) == SHAPE          # P > n
+    assert f(ctx, capi.BF16, FAKE, FAKE, 100, 64, 30, 8, 128, 0.1, FAKE) == SHAPE         # Hq % Hkv
+    assert f(ctx, capi.BF16, MIS, FAKE, 100, 64, 32, 8, 128, 0.1, FAKE) == ALIGN
+    assert f(ctx, capi.BF16, FAKE, FAKE, 100, 64, 32, 8, 128, 0.1, FAKE) == NOMEM         # no workspace
+    L.spts_set_workspace(ctx, FAKE, 1 << 30)
+    assert f(ctx, capi.BF16, FAKE, FAKE, 100, 64, 32, 8, 64, 0.1, FAKE) == UNSUPPORTED    # dh
+    assert f(ctx, capi.BF16, FAKE, FAKE, 100, 48, 32, 8, 128, 0.1, FAKE) == UNSUPPORTED   # P
+    assert f(ctx, capi.BF16, FAKE, FAKE, 100, 64, 8, 8, 128, 0.1, FAKE) == UNSUPPORTED    # group of 1
+    assert f(ctx, 7, FAKE, FAKE, 100, 64, 32, 8, 128, 0.1, FAKE) == DTYPE
+    assert b"dtype" in L.spts_last_error(ctx)
+
+
+def test_select_validation(L, ctx):
+    f = L.spts_score_topk
+    assert f(ctx, None, None, 0.5, 0.5, 10, 4, 1, FAKE, None) == INVALID
+    assert f(ctx, FAKE, None, 0.5, 0.5, 10, 4, 5, FAKE, None) == SHAPE     # forced > k
+    assert f(ctx, FAKE, None, 0.5, 0.5, 0, 0, 0, FAKE, None) == SHAPE      # n = 0
+    assert f(ctx, FAKE, None, 0.5, 0.5, 10, 4, 1, FAKE, None) == NOMEM
+    assert f(ctx, FAKE, MIS, 0.5, 0.5, 10, 4, 1, FAKE, None) == ALIGN
+    assert L.spts_msdp_stage(ctx, FAKE, 100, 120, 4, FAKE, FAKE, FAKE, None, None, 0) == SHAPE
+    assert L.spts_msdp_stage(ctx, FAKE, 100, 50, 60, FAKE, FAKE, FAKE, None, None, 0) == SHAPE
+
+
+def test_gemm_family_validation(L, ctx):
+    assert L.spts_linear(ctx, FAKE, None, 100, 100, FAKE, 256, FAKE, None, 0) == UNSUPPORTED   # k % 64
+    assert L.spts_linear(ctx, FAKE, None, 100, 128, FAKE, 200, FAKE, None, 0) == UNSUPPORTED   # n % 256
+    assert L.spts_linear(ctx, FAKE, None, 100, 128, FAKE, 256, FAKE, None, 2) == INVALID
+    assert L.spts_linear(ctx, None, None, 100, 128, FAKE, 256, FAKE, None, 0) == INVALID
+    assert L.spts_linear(ctx, FAKE, None, 0, 128, FAKE, 256, FAKE, None, 0) == OK             # empty: no-op
+    assert L.spts_ltp_probe(ctx, FAKE, FAKE, FAKE, 10, 4096, 100, FAKE) == UNSUPPORTED
+    assert L.spts_ltp_probe(ctx, FAKE, FAKE, FAKE, 10, 4096, 256, FAKE) == NOMEM
+    assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 10, 4096, 100, FAKE, None, 0) == UNSUPPORTED
+    assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 10, 4096, 14336, FAKE, None, 0) == NOMEM
+    assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 0, 4096, 14336, FAKE, None, 0) == OK
+    assert L.spts_rmsnorm(ctx, FAKE, 10, 12, 1e-5, FAKE) == SHAPE
+
+
+def test_attention_and_rows_validation(L, ctx):
+    f = L.spts_reduced_attention
+    assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 10, 5, 32, 8, 128, 0.1, FAKE) == SHAPE   # kq > n
+    assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 5, 10, 32, 8, 64, 0.1, FAKE) == UNSUPPORTED
+    assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 0, 10, 32, 8, 128, 0.1, FAKE) == OK       # empty
+    assert f(ctx, capi.I32, FAKE, FAKE, FAKE, FAKE, 5, 10, 32, 8, 128, 0.1, FAKE) == DTYPE
+    assert L.spts_gather(ctx, 9, FAKE, FAKE, 4, 8, FAKE) == DTYPE
+    assert L.spts_gather(ctx, capi.BF16, FAKE, FAKE, 0, 8, FAKE) == OK
+    assert L.spts_scatter(ctx, capi.BF16, FAKE, FAKE, 4, 8, FAKE, 3) == INVALID
+    assert L.spts_scatter(ctx, capi.BF16, FAKE, MIS, 4, 8, FAKE, 1) == ALIGN
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The binding refuses CPU tensors instead of computing on the host."""
+    import torch
+    with pytest.raises(ValueError):
+        capi.spts_rmsnorm(torch.zeros(4, 8, dtype=torch.bfloat16))

@@ -211,6 +211,34 @@ def make_stack(sh: LayerShape, layers: int, seed=0, x_std=1.0):
     return dict(x=x, layers=ws)
 
 
+def randn(shape, seed=0, std=1.0, bf16=True):
+    """One tensor of i.i.d. N(0, std^2) draws (bf16 by default, else fp32)."""
+    x = _normal(np.random.default_rng(seed), tuple(shape), std)
+    return to_bf16(x) if bf16 else torch.from_numpy(x)
+
+
+def clustered_keys(n, Hkv, dh, n_centroids=256, sigma=0.3, seed=0):
+    """Keys [n, Hkv, dh] (bf16): per KV head, n_centroids centroids ~ N(0, I)
+    and each key = a uniformly drawn centroid + N(0, sigma^2 I).
+    Draw order per head: centroids, assignments, noise."""
+    rng = np.random.default_rng(seed)
+    k = np.empty((n, Hkv, dh), dtype=np.float32)
+    for g in range(Hkv):
+        cent = _normal(rng, (n_centroids, dh), 1.0)
+        assign = rng.integers(0, n_centroids, size=n)
+        k[:, g, :] = cent[assign] + _normal(rng, (n, dh), sigma)
+    return to_bf16(k)
+
+
+def sorted_rows(n, k, n_forced, seed=0):
+    """k ascending distinct rows of [0, n) that include the last n_forced
+    (a stand-in selection for per-op tests); int32 tensor."""
+    rng = np.random.default_rng(seed)
+    free = rng.choice(n - n_forced, size=k - n_forced, replace=False)
+    rows = np.sort(np.concatenate([free, np.arange(n - n_forced, n)]))
+    return torch.from_numpy(rows.astype(np.int32))
+
+
 def make_scores(n, seed=0, ties=0, dist="exp"):
     """Synthetic non-negative fp32 score vectors for selection tests.
 
