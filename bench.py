@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""SPTS prefill benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+(inputs resident in HBM before timing starts):
+
+  msdp_stack_32k (default): the 8-layer LLaMA-3.1-8B-shaped stack at 32768
+      tokens -- RMSNorm, K/V/probe-Q projections with RoPE, PAP probe, MSDP
+      stage pruning (budgets 0.6/0.45/0.35/0.25 of N every 2 layers), top-k,
+      reduced attention, O projection + residual, LTP probe, fused top-k,
+      reduced SwiGLU + residual -- every row of the hot path.
+  layer_32k: one bare attention + FFN layer at 32768 tokens (PAP + LTP).
+
+The metric is prefill tokens/s per layer: layers * N / seconds per step.
+One JSON line is printed.  It also carries the roofline of the dominant
+kernel (timed with HIP events on its own stream inside the timed region),
+a per-call breakdown, the single-layer figure and the CPU oracle's rate on a
+bounded row sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_CALLS = {"k_proj", "v_proj", "probe_q_proj", "q_proj", "reduced_attention", "o_proj_add",
+              "ffn_gate_up", "ffn_down_add", "ltp_probe", "pap_probe", "o_proj", "reduced_ffn"}
+SINGLE_KERNEL_CALLS = {"k_proj", "v_proj", "probe_q_proj", "q_proj", "reduced_attention", "o_proj_add",
+                       "ffn_gate_up", "ffn_down_add"}
+KERNEL_OF_CALL = {"reduced_attention": "attn_bf16_kernel", "ffn_gate_up": "gemm_tn_kernel<EPI_SWIGLU,gather>",
+                  "ffn_down_add": "gemm_tn_kernel<EPI_STORE,scatter>", "q_proj": "gemm_tn_kernel<EPI_ROPE/STORE,gather>",
+                  "o_proj_add": "gemm_tn_kernel<EPI_STORE,scatter>", "k_proj": "gemm_tn_kernel",
+                  "v_proj": "gemm_tn_kernel"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="msdp_stack_32k", choices=["msdp_stack_32k", "layer_32k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-layer", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
+    ap.add_argument("--cpu-sample", type=float, default=1.0 / 32,
+                    help="fraction of row-separable oracle work timed for the CPU baseline")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------- inputs
+
+def stack_inputs(dev, n_layers=8):
+    import workloads as W
+    cfgd = W.CONFIGS["msdp_stack_32k"]
+    sh = cfgd["shape"]
+    t0 = time.time()
+    st = W.make_stack(sh, n_layers, seed=cfgd["seed"])
+    keys = ["wq", "wk", "wv", "wo", "wg", "wu", "wd", "u_t", "v_t"]
+    layers = [{k: w[k].to(dev) for k in keys} for w in st["layers"]]
+    log(f"generated stack inputs in {time.time() - t0:.1f}s")
+    return cfgd, sh, st, st["x"].to(dev), layers
+
+
+# ------------------------------------------------------------------ timing
+
+def timed(run_step, steps, warmup):
+    import torch
+    from free_token_skipping_amd.pipeline import CallTimer, NO_TIMER
+    for _ in range(warmup):
+        run_step(NO_TIMER)
+    torch.cuda.synchronize()
+    tm = CallTimer()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run_step(tm)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    return e0.elapsed_time(e1), wall_ms, tm.summary()
+
+
+def breakdown(summary, steps):
+    out = {}
+    for name, (calls, ms, work) in sorted(summary.items(), key=lambda kv: -kv[1][1]):
+        row = {"ms_per_step": round(ms / steps, 4), "calls_per_step": calls // steps}
+        if ms > 0 and work:
+            rate = work / (ms * 1e-3)
+            if name in MFMA_CALLS:
+                row["tflops"] = round(rate / 1e12, 1)
+                row["frac_mfma_peak"] = round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)
+            else:
+                row["gbs"] = round(rate / 1e9, 1)
+                row["frac_hbm_peak"] = round(rate / 1e9 / PEAK_HBM_GBS, 4)
+        out[name] = row
+    return out
+
+
+def roofline(summary, steps):
+    """Dominant single-kernel call by time: achieved = algorithmic FLOPs per
+    launch / average launch time (events on the launching stream)."""
+    cands = [(ms, name, calls, work) for name, (calls, ms, work) in summary.items() if name in SINGLE_KERNEL_CALLS]
+    ms, name, calls, work = max(cands)
+    avg_ms = ms / calls
+    flops_per_launch = work / calls
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": KERNEL_OF_CALL.get(name, name), "call": name,
+            "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_ms, 4),
+            "launches_per_step": calls // steps}
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(sh, st, n_layers, points, frac):
+    """The CPU oracle timed on a bounded sample of the stack workload.
+
+    For each MSDP stage (2 layers, c_s candidates) one oracle layer is run on
+    c_s rows of the inputs with that stage's first-layer weights: the steps
+    that need every row (norm, K/V projection, probe score, selections) run
+    in full; the row-separable steps (selected-query projection and
+    attention, O projection, LTP, SwiGLU) run on a fraction `frac` of their
+    rows and are scaled by 1/frac.  Stack time = 2 * sum over stages."""
+    import numpy as np
+    import workloads as W
+    from oracle import numerics, normrope, pap, select, attention, ltp, ffn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count()
+    P, Hq, Hkv, dh, d = sh.P, sh.Hq, sh.Hkv, sh.dh, sh.d
+    scale = dh ** -0.5
+    theta = 500000.0
+    rng = np.random.default_rng(0)
+    t_stack = 0.0
+    measured = 0.0
+    starts = sorted(points)
+    c_prev = sh.n
+    for si, layer_idx in enumerate(starts):
+        c = points[layer_idx]
+        w = {k: W.as_f64(v) for k, v in st["layers"][layer_idx].items()}
+        x = W.as_f64(st["x"][:c])
+        pos = np.arange(c)
+        t_full = 0.0
+        t_rows = 0.0
+        t0 = time.perf_counter()
+        xt = numerics.bf16(normrope.rmsnorm(x))
+        K = numerics.bf16(normrope.rope(numerics.f32(xt @ w["wk"].T).reshape(c, Hkv, dh), pos, theta))
+        V = numerics.bf16(xt @ w["wv"].T).reshape(c, Hkv, dh)
+        Qp = numerics.bf16(normrope.rope(numerics.f32(xt[-P:] @ w["wq"].T).reshape(P, Hq, dh), pos[-P:], theta))
+        S = pap.pap_scores(Qp, K, scale)
+        t_kvp = time.perf_counter() - t0
+        k_a = numerics.keep_count(0.35, c)
+        idx = select.select_topk(numerics.f32(S), k_a, P)
+        t_full += time.perf_counter() - t0
+        m = max(1, int(round(k_a * frac)))
+        rows = np.sort(rng.choice(k_a, m, replace=False))
+        t0 = time.perf_counter()
+        qi = idx[rows]
+        Qs = numerics.bf16(normrope.rope(numerics.f32(xt[qi] @ w["wq"].T).reshape(m, Hq, dh), qi, theta))
+        O = numerics.bf16(attention.reduced_attention(Qs, qi, K, V, scale))
+        delta = numerics.bf16(O.reshape(m, -1) @ w["wo"].T)
+        _ = numerics.bf16(x[qi] + delta)
+        mz = max(1, int(round(c * frac)))
+        zr = np.sort(rng.choice(c, mz, replace=False))
+        z = numerics.bf16(normrope.rmsnorm(x[zr]))
+        _ = ltp.ltp_scores(z, w["u_t"], w["v_t"])
+        _, y = ffn.swiglu_rows(z[: min(mz, m)], w["wg"], w["wu"], w["wd"])
+        t_rows += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        L = np.abs(rng.standard_normal(c))                   # stands in for the full-row LTP score
+        _ = select.select_topk(select.fuse_maxnorm(numerics.f32(S), numerics.f32(L)), k_a, P)
+        t_full += time.perf_counter() - t0
+        # scale: attention/Q/O rows by k_a/m, LTP rows by c/mz, FFN rows by k_f/min(mz, m)
+        t_layer = t_full + t_rows / frac
+        measured += t_full + t_rows
+        # the stage's first layer projects and probes the outgoing c_prev rows
+        t_stack += 2 * t_layer + t_kvp * (c_prev / c - 1.0)
+        c_prev = c
+        log(f"cpu oracle stage {si}: {c} candidates, measured {t_full + t_rows:.1f}s, layer est {t_layer:.1f}s")
+    value = n_layers * sh.n / t_stack
+    return {"value": round(value, 1), "unit": "tokens/s/layer", "cores": int(cores), "kind": "oracle",
+            "sample": (f"one oracle layer per MSDP stage at its candidate count (19661/14746/11469/8192 of "
+                       f"32768 rows); full-row steps (RMSNorm, K/V projection, probe score, selections) in full, "
+                       f"row-separable steps (Q projection + reduced attention + O projection, LTP, SwiGLU) on "
+                       f"{frac:.4f} of their rows scaled by 1/{frac:.4f}; stack = 2 x sum over stages, the "
+                       f"first layer's K/V + probe scaled to the outgoing row count; "
+                       f"{measured:.1f}s measured on {cores} BLAS threads"),
+            "seconds_per_step_est": round(t_stack, 2)}
+
+
+# --------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of "
+              f"this build -- the sharding design is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from free_token_skipping_amd import capi, pipeline
+    from free_token_skipping_amd.pipeline import LayerConfig, keep_count
+    capi.lib()                                               # no library -> fail loudly
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fused = not args.unfused
+
+    cfgd, sh, st, x0, layers = stack_inputs(dev)
+    N = sh.n
+    budgets = [keep_count(r, N) for r in cfgd["budget_ratios"]]
+    points = pipeline.prune_points(0, cfgd["stage_ends"], budgets)
+    stack_cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=cfgd["keep_attn"],
+                            keep_ffn=cfgd["keep_ffn"], w_fuse=cfgd["w_fuse"], prenorm=True, eps=cfgd["eps"],
+                            theta=cfgd["theta"])
+    layer_cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=0.35, keep_ffn=0.35)
+    pos0 = torch.arange(N, dtype=torch.int32, device=dev)
+    n_layers = len(layers)
+
+    def stack_step(tm):
+        pipeline.msdp_stack(x0, layers, stack_cfg, points, fused=fused, tm=tm)
+
+    def layer_step(tm):
+        # one bare 32K layer (PAP + LTP); the layer-0 weights of the stack are the
+        # 32K layer workload's inputs (same seed and draw order)
+        with tm("layer_setup", 4.0 * x0.numel()):
+            x = x0.clone()
+        pipeline.spts_layer(x, pos0, layers[0], layer_cfg, fused=fused, tm=tm)
+
+    results = {}
+    for name, fn, nl in (("msdp_stack_32k", stack_step, n_layers), ("layer_32k", layer_step, 1)):
+        if name != args.workload and (args.no_single_layer or name == "msdp_stack_32k"):
+            continue
+        log(f"timing {name}: warmup {args.warmup}, steps {args.steps}")
+        total_ms, wall_ms, summ = timed(fn, args.steps, args.warmup)
+        ms = total_ms / args.steps
+        results[name] = dict(ms_per_step=ms, wall_ms_per_step=wall_ms / args.steps,
+                             tokens_per_s_per_layer=nl * N / (ms * 1e-3),
+                             breakdown=breakdown(summ, args.steps), roofline=roofline(summ, args.steps))
+        log(f"{name}: {ms:.3f} ms/step, {nl * N / (ms * 1e-3):,.0f} tokens/s/layer")
+
+    head = results[args.workload]
+    rec = {
+        "metric": "SPTS prefill tokens/s per layer at 32K",
+        "value": round(head["tokens_per_s_per_layer"], 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": ({"workload": "msdp_stack_32k", "tokens": N, "layers": n_layers, "stages": "2 layers each",
+                    "candidate_budgets": budgets, "keep_attn": cfgd["keep_attn"], "keep_ffn": cfgd["keep_ffn"],
+                    "probes": sh.P, "shape": "LLaMA-3.1-8B (d 4096, 32/8 heads, d_head 128, SwiGLU 14336)",
+                    "ltp_rank": sh.r, "fused_gather_scatter": fused}
+                   if args.workload == "msdp_stack_32k" else
+                   {"workload": "layer_32k", "tokens": N, "layers": 1, "keep_attn": 0.35, "keep_ffn": 0.35,
+                    "probes": sh.P, "ltp_rank": sh.r, "fused_gather_scatter": fused}),
+        "roofline": head["roofline"],
+        "breakdown": head["breakdown"],
+        "wall_ms_per_step": round(head["wall_ms_per_step"], 4),
+    }
+    for name, r in results.items():
+        if name != args.workload:
+            rec.setdefault("also", {})[name] = {"tokens_per_s_per_layer": round(r["tokens_per_s_per_layer"], 1),
+                                                "ms_per_step": round(r["ms_per_step"], 4),
+                                                "roofline": r["roofline"], "breakdown": r["breakdown"]}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(sh, st, n_layers, points, args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -303,6 +303,22 @@ spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows
   return hip_status(ctx, launch_gemm(g, EPI_ROPE, ctx->stream), "linear_rope");
 }
 
+spts_status spts_linear_swiglu(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
+                               const void* w_gate, const void* w_up, int f, void* h_out) {
+  CHECK_CTX();
+  REQUIRE(m >= 0 && kdim > 0 && f > 0, SPTS_ERR_SHAPE, "bad SwiGLU GEMM sizes");
+  REQUIRE(kdim % 64 == 0 && f % 128 == 0, SPTS_ERR_UNSUPPORTED, "SwiGLU GEMM needs kdim %% 64 == 0, f %% 128 == 0");
+  if (m == 0) return SPTS_OK;
+  REQUIRE_PTR(a); REQUIRE_PTR(w_gate); REQUIRE_PTR(w_up); REQUIRE_PTR(h_out);
+  REQUIRE_ALIGN(a); REQUIRE_ALIGN(w_gate); REQUIRE_ALIGN(w_up); REQUIRE_ALIGN(h_out);
+  if (a_rows) REQUIRE_ALIGN(a_rows);
+  GemmArgs g{};
+  g.a = reinterpret_cast<const uint16_t*>(a); g.a_rows = a_rows; g.m = m; g.k = kdim; g.lda = kdim;
+  g.b0 = reinterpret_cast<const uint16_t*>(w_gate); g.b1 = reinterpret_cast<const uint16_t*>(w_up);
+  g.ldb = kdim; g.n = 2 * f; g.out = h_out; g.ldc = f;
+  return hip_status(ctx, launch_gemm(g, EPI_SWIGLU, ctx->stream), "linear_swiglu");
+}
+
 spts_status spts_rope_table(spts_ctx* ctx, int max_pos, int dh, double theta, float* table) {
   CHECK_CTX();
   REQUIRE_PTR(table);

@@ -28,6 +28,57 @@ import torch
 from . import capi
 
 
+class _NoTimer:
+    def __call__(self, name, work=None):
+        return self
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+NO_TIMER = _NoTimer()
+
+
+class CallTimer:
+    """Records a start/end HIP event pair on the current stream around each
+    named library call (the stream the call's kernels run on), with an
+    optional algorithmic work figure for the call."""
+
+    def __init__(self):
+        self.records = []
+        self._cur = None
+
+    def __call__(self, name, work=None):
+        self._cur = (name, work)
+        return self
+
+    def __enter__(self):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self._start = e0
+        return self
+
+    def __exit__(self, *exc):
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        name, work = self._cur
+        self.records.append((name, work, self._start, e1))
+        return False
+
+    def summary(self):
+        """{name: (calls, total_ms, total_work)} after a synchronize."""
+        out = {}
+        for name, work, a, b in self.records:
+            if callable(work):
+                work = work()
+            c, t, w = out.get(name, (0, 0.0, 0.0))
+            out[name] = (c + 1, t + a.elapsed_time(b), w + (work or 0.0))
+        return out
+
+
 def keep_count(ratio: float, n: int) -> int:
     """floor(ratio * n + 0.5), capped to [0, n]."""
     return int(min(n, max(0, math.floor(float(ratio) * float(n) + 0.5))))
@@ -47,92 +98,133 @@ class LayerConfig:
     theta: Optional[float] = None         # None: no rotary embedding
 
 
+def _attn_flops(idx, Hq, dh):
+    """Algorithmic reduced-attention FLOPs: 4*Hq*dh per (query, visible key)."""
+    return lambda: 4.0 * Hq * dh * float((idx.to(torch.float64) + 1).sum().item())
+
+
 def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_table=None,
-                    k_given=None, prune_to=None, fused=True, trace=None):
+                    k_given=None, prune_to=None, fused=True, trace=None, tm=NO_TIMER):
     """x [n, d] bf16 residual (updated in place unless pruned), pos [n] int32.
 
     Returns (x_out, pos_out, S) where x_out/pos_out are the (possibly pruned)
-    candidates and S their PAP score (float32)."""
+    candidates and S their PAP score (float32).  `tm` (a CallTimer) brackets
+    each library call with events; work figures are algorithmic FLOPs or bytes."""
     n, d = x.shape
     Hq, Hkv, dh, P = cfg.Hq, cfg.Hkv, cfg.dh, cfg.P
     rope = cfg.theta is not None
-    xt = capi.spts_rmsnorm(x, cfg.eps) if cfg.prenorm else x
-    # a1: K, V over all current candidates
+    if cfg.prenorm:
+        with tm("rmsnorm", 4.0 * n * d):
+            xt = capi.spts_rmsnorm(x, cfg.eps)
+    else:
+        xt = x
+    # a1: K, V over all current candidates (+ RoPE on K)
     if k_given is None:
-        K = (capi.spts_linear_rope(xt, w["wk"], pos, rope_table) if rope else capi.spts_linear(xt, w["wk"]))
+        with tm("k_proj", 2.0 * n * d * Hkv * dh):
+            K = (capi.spts_linear_rope(xt, w["wk"], pos, rope_table) if rope else capi.spts_linear(xt, w["wk"]))
         K = K.view(n, Hkv, dh)
     else:
         K = k_given
-    V = capi.spts_linear(xt, w["wv"]).view(n, Hkv, dh)
+    with tm("v_proj", 2.0 * n * d * Hkv * dh):
+        V = capi.spts_linear(xt, w["wv"]).view(n, Hkv, dh)
     # a2: probe queries (last P rows)
     xp = xt[n - P:]
-    Qp = (capi.spts_linear_rope(xp, w["wq"], pos[n - P:], rope_table) if rope else capi.spts_linear(xp, w["wq"]))
+    with tm("probe_q_proj", 2.0 * P * d * Hq * dh):
+        Qp = (capi.spts_linear_rope(xp, w["wq"], pos[n - P:], rope_table) if rope
+              else capi.spts_linear(xp, w["wq"]))
     # a3: PAP score
-    S = capi.spts_probe_attention(Qp.view(P, Hq, dh), K)
+    with tm("pap_probe", 2.0 * Hq * dh * P * n):
+        S = capi.spts_probe_attention(Qp.view(P, Hq, dh), K)
     if trace is not None:
         trace.update(S_pre=S, K_pre=K, V_pre=V)
     # a14: MSDP boundary -- prune, then compact every per-candidate tensor
     if prune_to is not None and prune_to < n:
-        keep, pos, x = capi.spts_msdp_stage(S, prune_to, P, pos, x)
-        xt = capi.spts_gather(xt, keep) if cfg.prenorm else x
-        K = capi.spts_gather(K, keep)
-        V = capi.spts_gather(V, keep)
-        S = capi.spts_gather(S, keep)
+        with tm("msdp_stage", 4.0 * n + 2.0 * prune_to * (4 + 2 * d * 2)):
+            keep, pos, x = capi.spts_msdp_stage(S, prune_to, P, pos, x)
+        with tm("msdp_compact", 2.0 * prune_to * (2 * Hkv * dh * 2 + 4 + (2 * d if cfg.prenorm else 0)) * 2):
+            xt = capi.spts_gather(xt, keep) if cfg.prenorm else x
+            K = capi.spts_gather(K, keep)
+            V = capi.spts_gather(V, keep)
+            S = capi.spts_gather(S, keep)
         n = prune_to
         if trace is not None:
             trace.update(keep=keep)
     # a4: select the attention rows
     k_a = keep_count(cfg.keep_attn, n)
-    idx = capi.spts_score_topk(S, k_a, P)
+    with tm("select_attn", 4.0 * n + 4.0 * k_a):
+        idx = capi.spts_score_topk(S, k_a, P)
     # a5 + a6: gather selected rows, Q projection
     if fused:
-        Qs = (capi.spts_linear_rope(xt, w["wq"], pos, rope_table, a_rows=idx) if rope
-              else capi.spts_linear(xt, w["wq"], a_rows=idx))
+        with tm("q_proj", 2.0 * k_a * d * Hq * dh):
+            Qs = (capi.spts_linear_rope(xt, w["wq"], pos, rope_table, a_rows=idx) if rope
+                  else capi.spts_linear(xt, w["wq"], a_rows=idx))
     else:
-        xs = capi.spts_gather(xt, idx)
-        Qs = (capi.spts_linear_rope(xs, w["wq"], capi.spts_gather(pos, idx), rope_table) if rope
-              else capi.spts_linear(xs, w["wq"]))
+        with tm("gather_x", 4.0 * k_a * d):
+            xs = capi.spts_gather(xt, idx)
+        with tm("q_proj", 2.0 * k_a * d * Hq * dh):
+            Qs = (capi.spts_linear_rope(xs, w["wq"], capi.spts_gather(pos, idx), rope_table) if rope
+                  else capi.spts_linear(xs, w["wq"]))
     # a7: reduced attention over all candidates' K/V
-    O = capi.spts_reduced_attention(Qs.view(k_a, Hq, dh), idx, K, V)
+    with tm("reduced_attention", _attn_flops(idx, Hq, dh)):
+        O = capi.spts_reduced_attention(Qs.view(k_a, Hq, dh), idx, K, V)
     # a8: O projection + residual add into the selected rows
     if fused:
-        capi.spts_linear(O.view(k_a, Hq * dh), w["wo"], out=x, out_rows=idx, accumulate=True)
+        with tm("o_proj_add", 2.0 * k_a * Hq * dh * d):
+            capi.spts_linear(O.view(k_a, Hq * dh), w["wo"], out=x, out_rows=idx, accumulate=True)
     else:
-        delta = capi.spts_linear(O.view(k_a, Hq * dh), w["wo"])
-        capi.spts_scatter(delta, idx, x, accumulate=True)
+        with tm("o_proj", 2.0 * k_a * Hq * dh * d):
+            delta = capi.spts_linear(O.view(k_a, Hq * dh), w["wo"])
+        with tm("scatter_add_x", 6.0 * k_a * d):
+            capi.spts_scatter(delta, idx, x, accumulate=True)
     if trace is not None:
         trace.update(S=S, idx=idx, K=K, V=V, Qp=Qp, Qs=Qs, O=O, pos=pos)
     return x, pos, S
 
 
-def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None):
+def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None, tm=NO_TIMER):
     """h [n, d] residual (updated in place), S [n] PAP score of this layer."""
     n, d = h.shape
-    z = capi.spts_rmsnorm(h, cfg.eps) if cfg.prenorm else h
+    f = w["wg"].shape[0]
+    r = w["u_t"].shape[0]
+    if cfg.prenorm:
+        with tm("rmsnorm", 4.0 * n * d):
+            z = capi.spts_rmsnorm(h, cfg.eps)
+    else:
+        z = h
     # a9: LTP proxy score
-    L = capi.spts_ltp_probe(z, w["u_t"], w["v_t"])
+    with tm("ltp_probe", 4.0 * n * d * r):
+        L = capi.spts_ltp_probe(z, w["u_t"], w["v_t"])
     # a10: fused score -> select the FFN rows
     k_f = keep_count(cfg.keep_ffn, n)
     fused_score = torch.empty(n, dtype=torch.float32, device=h.device) if trace is not None else None
-    idx_f = capi.spts_score_topk(S, k_f, cfg.P, s_b=L, w_a=cfg.w_fuse[0], w_b=cfg.w_fuse[1], fused_out=fused_score)
+    with tm("select_ffn", 8.0 * n + 4.0 * k_f):
+        idx_f = capi.spts_score_topk(S, k_f, cfg.P, s_b=L, w_a=cfg.w_fuse[0], w_b=cfg.w_fuse[1],
+                                     fused_out=fused_score)
     # a11 + a12 + a13: gather, reduced SwiGLU, residual add
     if fused:
-        capi.spts_reduced_ffn(z, w["wg"], w["wu"], w["wd"], rows=idx_f, y=h, y_rows=idx_f, accumulate=True)
+        # the two GEMMs of spts_reduced_ffn as separate calls, so each is timed
+        with tm("ffn_gate_up", 4.0 * k_f * d * f):
+            H = capi.spts_linear_swiglu(z, w["wg"], w["wu"], a_rows=idx_f)
+        with tm("ffn_down_add", 2.0 * k_f * d * f):
+            capi.spts_linear(H, w["wd"], out=h, out_rows=idx_f, accumulate=True)
     else:
-        zs = capi.spts_gather(z, idx_f)
-        y = capi.spts_reduced_ffn(zs, w["wg"], w["wu"], w["wd"])
-        capi.spts_scatter(y, idx_f, h, accumulate=True)
+        with tm("gather_z", 4.0 * k_f * d):
+            zs = capi.spts_gather(z, idx_f)
+        with tm("reduced_ffn", 6.0 * k_f * d * f):
+            y = capi.spts_reduced_ffn(zs, w["wg"], w["wu"], w["wd"])
+        with tm("scatter_add_h", 6.0 * k_f * d):
+            capi.spts_scatter(y, idx_f, h, accumulate=True)
     if trace is not None:
         trace.update(L=L, fused=fused_score, idx_f=idx_f, z=z)
     return h
 
 
 def spts_layer(x, pos, w, cfg: LayerConfig, rope_table=None, k_given=None, prune_to=None, fused=True,
-               trace=None):
+               trace=None, tm=NO_TIMER):
     """Attention block then (if cfg.keep_ffn is set) FFN block."""
-    x, pos, S = attention_block(x, pos, w, cfg, rope_table, k_given, prune_to, fused, trace)
+    x, pos, S = attention_block(x, pos, w, cfg, rope_table, k_given, prune_to, fused, trace, tm)
     if cfg.keep_ffn is not None:
-        x = ffn_block(x, S, w, cfg, fused, trace)
+        x = ffn_block(x, S, w, cfg, fused, trace, tm)
     return x, pos
 
 
@@ -145,18 +237,19 @@ def prune_points(first_skip_layer, stage_end_layers, budgets, final_budget=None)
     return pts
 
 
-def msdp_stack(x0, layers, cfg: LayerConfig, points, fused=True, traces=None):
+def msdp_stack(x0, layers, cfg: LayerConfig, points, fused=True, traces=None, tm=NO_TIMER):
     """Run the stack on embeddings x0 [N, d] (not modified).  Returns the
     residual over the final candidates and their original positions."""
     N = x0.shape[0]
-    x = x0.clone()
-    pos = torch.arange(N, dtype=torch.int32, device=x0.device)
-    table = capi.spts_rope_table(N, cfg.dh, cfg.theta, x0.device) if cfg.theta is not None else None
+    with tm("stack_setup", 4.0 * x0.numel()):
+        x = x0.clone()
+        pos = torch.arange(N, dtype=torch.int32, device=x0.device)
+        table = capi.spts_rope_table(N, cfg.dh, cfg.theta, x0.device) if cfg.theta is not None else None
     for li, w in enumerate(layers):
         budget = points.get(li)
         prune = budget if budget is not None and budget < x.shape[0] else None
         tr = {} if traces is not None else None
-        x, pos = spts_layer(x, pos, w, cfg, table, prune_to=prune, fused=fused, trace=tr)
+        x, pos = spts_layer(x, pos, w, cfg, table, prune_to=prune, fused=fused, trace=tr, tm=tm)
         if traces is not None:
             traces.append(tr)
     return x, pos

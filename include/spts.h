@@ -201,6 +201,13 @@ spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows
                              int kdim, const void* w, int n, void* out, const int32_t* pos,
                              const float* table);
 
+/* The first half of the reduced FFN as its own call:
+ *     h_out[i, :] = bf16(silu(A Wg^T) * (A Wu^T))[i],  A row i = a[a_rows ? a_rows[i] : i]
+ *   a [*, kdim] bf16, w_gate, w_up [f, kdim] bf16, h_out [m, f] bf16.
+ * Requires kdim % 64 == 0, f % 128 == 0.  ([SPTS] Fig. 2(b), reduced feed-forward.) */
+spts_status spts_linear_swiglu(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
+                               const void* w_gate, const void* w_up, int f, void* h_out);
+
 /* table[p, c, 0..1] = (cos, sin)(p * theta^(-2c/dh)) for p < max_pos, c < dh/2,
  * angle formed in fp64 and rounded to fp32. */
 spts_status spts_rope_table(spts_ctx* ctx, int max_pos, int dh, double theta, float* table);

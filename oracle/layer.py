@@ -74,6 +74,7 @@ def attention_block(x, pos, w, cfg, k_given=None, prune_to=None):
     V = _proj(xt, w["wv"], Hkv, dh)
     Qp = _proj(xt[-P:], w["wq"], Hq, dh, pos[-P:], theta)
     S = pap_scores(Qp, K, scale)
+    S_full = S
     keep = None
     if prune_to is not None:
         keep = select_topk(f32(S), prune_to, P)
@@ -86,7 +87,7 @@ def attention_block(x, pos, w, cfg, k_given=None, prune_to=None):
     delta = bf16(O.reshape(len(idx), Hq * dh) @ np.asarray(w["wo"], dtype=np.float64).T)
     y = x.copy()
     y[idx] = bf16(x[idx] + delta)
-    state = dict(S=S, idx=idx, K=K, V=V, Qp=Qp, Qs=Qs, O=O, pos=pos, keep=keep, xt=xt)
+    state = dict(S=S, S_full=S_full, idx=idx, K=K, V=V, Qp=Qp, Qs=Qs, O=O, pos=pos, keep=keep, xt=xt)
     return y, state
 
 

@@ -347,3 +347,17 @@ def test_msdp_stage_bit_exact():
     assert np.array_equal(keep.cpu().numpy(), ref)
     assert np.array_equal(pos_new.cpu().numpy(), pos.numpy()[ref])
     assert torch.equal(x_new.cpu(), x[ref])
+
+
+def test_linear_swiglu():
+    _log("swiglu GEMM")
+    a = W.randn((600, 512), seed=52)
+    wg = W.randn((384, 512), seed=53, std=0.05)
+    wu = W.randn((384, 512), seed=54, std=0.05)
+    rows = W.sorted_rows(600, 301, 4, seed=55)
+    h = capi.spts_linear_swiglu(_cuda(a), _cuda(wg), _cuda(wu), a_rows=_cuda(rows))
+    z = W.as_f64(a)[rows.long().numpy()]
+    g = numerics.f32(z @ W.as_f64(wg).T)
+    u = numerics.f32(z @ W.as_f64(wu).T)
+    ref = numerics.bf16(ffn.silu(g) * u)
+    assert_close(np64(h), ref, BF16_REL, "swiglu GEMM")
