@@ -243,6 +243,7 @@ spts_status spts_reduced_attention(spts_ctx* ctx, spts_dtype dtype, const void* 
   REQUIRE_ALIGN(q_sel); REQUIRE_ALIGN(idx); REQUIRE_ALIGN(k); REQUIRE_ALIGN(v); REQUIRE_ALIGN(o_sel);
   if (dtype == SPTS_BF16) {
     REQUIRE(dh == 128, SPTS_ERR_UNSUPPORTED, "bf16 attention needs dh == 128");
+    REQUIRE((long)n * Hkv * dh < (1L << 31), SPTS_ERR_UNSUPPORTED, "K/V larger than 2^31 elements");
     REQUIRE((Hq / Hkv) % 4 == 0, SPTS_ERR_UNSUPPORTED, "bf16 attention needs Hq/Hkv %% 4 == 0");
     return hip_status(ctx, launch_attn_bf16(reinterpret_cast<const uint16_t*>(q_sel), idx,
                                             reinterpret_cast<const uint16_t*>(k),

@@ -12,6 +12,8 @@
 // rounding, the MFMA B operand of O^T = V^T P^T with no lane exchange, and
 // the matching V^T fragment is a single 16-byte LDS read from a transposed
 // V tile.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -79,9 +81,16 @@ __device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* ks, uint
 }
 
 // ============================================================ reduced attention
-// grid: (ceil(kq/64), Hq/4); block 256 = 4 waves = 4 heads of one KV group.
-// Each wave: 64 queries (two 32-query column tiles) of one head.
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const uint16_t* __restrict__ q,
+// grid: (ceil(kq/64), Hq/4); block 512 = 8 waves: wave w serves query head
+// 4*blockIdx.y + (w & 3) for the 32 queries q0 + 32*(w >> 2) ..  +31.  Two
+// waves per SIMD, so one wave's softmax (VALU) overlaps the other's MFMA.
+// Softmax statistics use a lazily updated running max: the reference max only
+// moves when a lane's logits exceed it by more than 2^8 (in exp2 units), so
+// the O rescale is rare; p = exp2(s*scale*log2e - m) then stays <= 256 and
+// the final O / l is exact whatever reference max was used.
+constexpr float kLazyMax = 8.0f;
+
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __restrict__ q,
                                                            const int32_t* __restrict__ idx,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v, int kq,
@@ -93,136 +102,146 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const uint16_t* __res
   const int l32 = lane & 31, half = lane >> 5;
   const int nqb = (kq + 63) >> 6;
   const int qb = nqb - 1 - (int)blockIdx.x;          // latest (longest) query blocks first
-  const int h = blockIdx.y * 4 + wave;
+  const int h = blockIdx.y * 4 + (wave & 3);
   const int g = (blockIdx.y * 4) / (Hq / Hkv);
   const int q0 = qb * 64;
+  const int qw = q0 + (wave >> 2) * 32;              // this wave's first query
 
-  int qi[2], qpos[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int i = q0 + c * 32 + l32;
-    qi[c] = i < kq ? i : kq - 1;
-    qpos[c] = idx[qi[c]];
-  }
+  const int qi_raw = qw + l32;
+  const int qi = qi_raw < kq ? qi_raw : kq - 1;
+  const int qpos = idx[qi];
   const int kmax = idx[min(q0 + 63, kq - 1)];
   const int ntiles = kmax / KT + 1;
+  const int nfull = (idx[q0] + 1) / KT;             // tiles entirely below every query of the block
 
-  bf16x8 qf[2][8];
+  bf16x8 qf[8];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)qi[c] * Hq + h) * DH + kk * 16 + half * 8);
+  for (int kk = 0; kk < 8; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8*>(q + ((long)qi * Hq + h) * DH + kk * 16 + half * 8);
 
-  f32x16 oacc[2][4];
+  f32x16 oacc[4];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[c][d][r] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+  float m_ref = -INFINITY, l_part = 0.f;             // l_part: this half-wave's keys only
+  const f32x16 zero16 = {};
 
-  TileRegs tr;
-  load_tile(tr, k, v, 0, n, Hkv, g, tid, true);
-  store_tile(tr, Ks[0], Vs[0], tid, true);
-  __syncthreads();
+  // ---- tile staging: K rows (2 x 16 B / thread), V as 2-key x 8-dh blocks.
+  // Element offsets fit in 32 bits (n * Hkv * 128 < 2^31 is checked on the host).
+  const int row_stride = Hkv * DH;
+  const uint16_t* kbase = k + g * DH + (tid & 15) * 8;
+  const int kp = tid & 31, dc = tid >> 5;            // V: key pair, dh chunk
+  const uint16_t* vbase = v + g * DH + dc * 8;
+  u32x4 kr[2], vr[2];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = min(j0 + (tid >> 4) + 32 * i, n - 1);
+      kr[i] = ld16(kbase + j * row_stride);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = min(j0 + 2 * kp + e, n - 1);
+      vr[e] = ld16(vbase + j * row_stride);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st16(Ks[buf] + kswz((tid >> 4) + 32 * i, tid & 15), kr[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const uint32_t a = (e & 1) ? (vr[0][w] >> 16) : (vr[0][w] & 0xFFFFu);
+      const uint32_t b = (e & 1) ? (vr[1][w] >> 16) : (vr[1][w] & 0xFFFFu);
+      *reinterpret_cast<uint32_t*>(Vs[buf] + vswz(dc * 8 + e, kp >> 2) + (kp & 3) * 2) = a | (b << 16);
+    }
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, bool MASK) {
     const int buf = t & 1;
     const int j0 = t * KT;
-    if (t + 1 < ntiles) load_tile(tr, k, v, j0 + KT, n, Hkv, g, tid, true);
     const uint16_t* ks = Ks[buf];
     const uint16_t* vs = Vs[buf];
-
-    // S^T tiles: rows = keys (permuted), cols = queries
-    f32x16 s[2][2];
+    // S^T = K Q^T for 64 keys (rows permuted) x 32 queries
+    f32x16 s[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[c][kt][r] = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kswz(kt * 32 + perm32(l32), kk * 2 + half));
-#pragma unroll
-        for (int c = 0; c < 2; ++c) s[c][kt] = mfma32x32x16(kf, qf[c][kk], s[c][kt]);
+        s[kt] = mfma32x32x16(kf, qf[kk], kk == 0 ? zero16 : s[kt]);
       }
-
-    // online softmax per query (lane); key of reg r = j0 + kt*32 + (r>>3)*16 + half*8 + (r&7)
-    bf16x8 pf[2][4];
-    const bool need_mask = (j0 + KT - 1) > idx[min(q0, kq - 1)];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float mx = -INFINITY;
+    }
+    if (MASK) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[c][kt][r] * sl2;
-          if (need_mask) {
-            const int key = j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7);
-            if (key > qpos[c]) x = -INFINITY;
-          }
-          s[c][kt][r] = x;
-          mx = fmaxf(mx, x);
+          const int key = j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7);
+          if (key > qpos) s[kt][r] = -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[c], mx);
-      const float alpha = exp2f(m[c] - mnew);
-      float rs = 0.f;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          bf16x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = exp2f(s[c][kt][sub * 8 + e] - mnew);
-            rs += p;
-            pv[e] = (__bf16)p;
-          }
-          pf[c][kt * 2 + sub] = pv;
-        }
-      rs += __shfl_xor(rs, 32);
-      l[c] = l[c] * alpha + rs;
-      m[c] = mnew;
+      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kt][r]), s[kt][r + 1]);
+    mx *= sl2;
+    if (__any(mx > m_ref + kLazyMax)) {
+      const float m_new = fmaxf(m_ref, fmaxf(mx, __shfl_xor(mx, 32)));
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_part *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[c][d][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      m_ref = m_new;
     }
-
-    // O^T += V^T P^T : rows = dh, cols = queries, k = 64 keys in 4 steps
+    bf16x8 pf[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ks4 = 0; ks4 < 4; ++ks4) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + vswz(d * 32 + l32, ks4 * 2 + half));
+      for (int sub = 0; sub < 2; ++sub) {
+        f32x8 pv;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) oacc[c][d] = mfma32x32x16(vf, pf[c][ks4], oacc[c][d]);
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][sub * 8 + e], sl2, -m_ref));
+          l_part += pv[e];
+        }
+        pf[kt * 2 + sub] = __builtin_convertvector(pv, bf16x8);
       }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks4 = 0; ks4 < 4; ++ks4)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + vswz(d * 32 + l32, ks4 * 2 + half));
+        oacc[d] = mfma32x32x16(vf, pf[ks4], oacc[d]);
+      }
+  };
 
-    if (t + 1 < ntiles) store_tile(tr, Ks[buf ^ 1], Vs[buf ^ 1], tid, true);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) load((t + 1) * KT);
+    tile(t, t >= nfull);
+    if (t + 1 < ntiles) store((t + 1) & 1);
     __syncthreads();
   }
 
   // normalise and store: lane = query, reg r of dh tile d -> dh d*32 + (r>>2)*8 + half*4 + (r&3)
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    if (q0 + c * 32 + l32 >= kq) continue;
-    const float inv = 1.0f / l[c];
-    uint16_t* orow = o + ((long)qi[c] * Hq + h) * DH;
+  if (qi_raw < kq) {
+    const float inv = 1.0f / (l_part + __shfl_xor(l_part, 32));
+    uint16_t* orow = o + ((long)qi * Hq + h) * DH;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         u32x2 w;
-        w[0] = pack2bf(oacc[c][d][qd * 4 + 0] * inv, oacc[c][d][qd * 4 + 1] * inv);
-        w[1] = pack2bf(oacc[c][d][qd * 4 + 2] * inv, oacc[c][d][qd * 4 + 3] * inv);
+        w[0] = pack2bf(oacc[d][qd * 4 + 0] * inv, oacc[d][qd * 4 + 1] * inv);
+        w[1] = pack2bf(oacc[d][qd * 4 + 2] * inv, oacc[d][qd * 4 + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + d * 32 + qd * 8 + half * 4) = w;
       }
   }
@@ -547,7 +566,7 @@ hipError_t launch_attn_bf16(const uint16_t* q, const int32_t* idx, const uint16_
                             const uint16_t* v, int kq, int n, int Hq, int Hkv, float scale,
                             uint16_t* o, hipStream_t s) {
   const dim3 grid((kq + 63) / 64, Hq / 4);
-  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(256), 0, s, q, idx, k, v, kq, n, Hq, Hkv,
+  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(512), 0, s, q, idx, k, v, kq, n, Hq, Hkv,
                      scale * kLog2e, o);
   return hipGetLastError();
 }

@@ -29,7 +29,8 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // element offset in a
 }
 
 template <int EPI, bool GATHER>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_tn_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* As = smem;                       // [2][BM*BK]
   uint16_t* Bs = smem + 2 * TILE_ELEMS;      // [2][BN*BK]
@@ -44,55 +45,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(GemmArgs g) {
   const int tile_m = blockIdx.x % tiles_m;
   const int tile_n = blockIdx.x / tiles_m;
 
-  // ---- per-thread global source offsets for the 8 A rows and 8 B rows it stages
-  const int ld_row = tid >> 3;   // + 32 * i
-  const int ld_ch = tid & 7;
-  long a_off[8], b_off[8];
-  unsigned b_from_up = 0;   // SWIGLU: bit i set when staged B row i comes from the up weight
+  // ---- direct global -> LDS staging.  Wave `wave`, instruction i writes the
+  // 1 KiB block of tile rows rb*8 .. rb*8+7, rb = 4*i + wave; lane L lands at
+  // row rb*8 + L/8, physical chunk L%8, so it fetches the logical chunk
+  // (L%8) ^ (L/8) -- the XOR swizzle applied on the global side.
+  const int ld_sub = lane >> 3;                       // row within the 8-row block
+  const int ld_ch = (lane & 7) ^ ld_sub;              // logical 16-byte chunk fetched
+  uint32_t a_off[8], b_off[8];                        // byte offsets of the staged rows
+  unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int r = tile_m * BM + ld_row + 32 * i;
-    if (r >= g.m) r = g.m - 1;
-    if (GATHER) r = g.a_rows[r];
-    a_off[i] = (long)r * g.lda + ld_ch * 8;
-    const int br = ld_row + 32 * i;
+    const int rb = 4 * i + wave;
+    const int r = rb * 8 + ld_sub;                    // row within the 256-row tile
+    int ar = tile_m * BM + r;
+    if (ar >= g.m) ar = g.m - 1;
+    if (GATHER) ar = g.a_rows[ar];
+    a_off[i] = ((uint32_t)ar * (uint32_t)g.lda + ld_ch * 8) * 2u;
     if (EPI == EPI_SWIGLU) {
-      // wave column block wn = br / 128: rows 0..63 gate, 64..127 up, same 64 outputs
-      const int bw = br >> 7, within = br & 127;
-      const long brow = (long)tile_n * 128 + bw * 64 + (within & 63);
+      // wave column block r / 128: rows 0..63 gate, 64..127 up, same 64 outputs
+      const int within = r & 127;
+      const uint32_t brow = (uint32_t)tile_n * 128 + (r >> 7) * 64 + (within & 63);
       if (within >= 64) b_from_up |= 1u << i;
-      b_off[i] = brow * g.ldb + ld_ch * 8;
+      b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
     } else {
-      b_off[i] = ((long)tile_n * BN + br) * g.ldb + ld_ch * 8;
+      b_off[i] = (((uint32_t)tile_n * BN + r) * (uint32_t)g.ldb + ld_ch * 8) * 2u;
     }
   }
-
-  u32x4 ra[8], rb[8];
+  const char* abase = reinterpret_cast<const char*>(g.a);
+  const char* b0base = reinterpret_cast<const char*>(g.b0);
+  const char* b1base = reinterpret_cast<const char*>(g.b1);
   const int KT = g.k / BK;
 
-  auto load_global = [&](int kt) {
-    const long ka = (long)kt * BK;
-    const long kb = g.kwrap > 0 ? (ka % g.kwrap) : ka;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = ld16(g.a + a_off[i] + ka);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (EPI == EPI_SWIGLU) {
-        const uint16_t* base = ((b_from_up >> i) & 1u) ? g.b1 : g.b0;
-        rb[i] = ld16(base + b_off[i] + kb);
-      } else {
-        rb[i] = ld16(g.b0 + b_off[i] + kb);
-      }
-    }
-  };
-  auto store_lds = [&](int buf) {
-    uint16_t* a_s = As + buf * TILE_ELEMS;
-    uint16_t* b_s = Bs + buf * TILE_ELEMS;
+  auto issue = [&](int kt, int stage) {
+    const uint32_t ka = (uint32_t)kt * BK * 2u;
+    const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
+    uint16_t* a_s = As + stage * TILE_ELEMS;
+    uint16_t* b_s = Bs + stage * TILE_ELEMS;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = ld_row + 32 * i;
-      st16(a_s + swz(r, ld_ch), ra[i]);
-      st16(b_s + swz(r, ld_ch), rb[i]);
+      const int rb = 4 * i + wave;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(abase + a_off[i] + ka),
+          (__attribute__((address_space(3))) void*)(a_s + rb * 512), 16, 0, 0);
+      const char* bb = (EPI == EPI_SWIGLU && ((b_from_up >> i) & 1u)) ? b1base : b0base;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(bb + b_off[i] + kb),
+          (__attribute__((address_space(3))) void*)(b_s + rb * 512), 16, 0, 0);
     }
   };
 
@@ -104,32 +102,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-
+  issue(0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) load_global(kt + 1);
+    __builtin_amdgcn_s_waitcnt(0);    // this wave's loads for stage `cur` have landed
+    __syncthreads();                  // ... and every wave's; stage cur^1 is free again
+    if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
     const uint16_t* a_s = As + cur * TILE_ELEMS;
     const uint16_t* b_s = Bs + cur * TILE_ELEMS;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[4], bfm[4];
+    bf16x8 af[2][4], bfm[2][4];
+    auto frag = [&](int kk, int set) {
       const int ch = kk * 2 + half;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 128 + i * 32 + l32, ch));
+        af[set][i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 128 + i * 32 + l32, ch));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfm[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
+        bfm[set][j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) frag(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[j], af[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[kk & 1][j], af[kk & 1][i], acc[i][j]);
     }
-    if (kt + 1 < KT) store_lds(cur ^ 1);
-    __syncthreads();
+    // schedule: the first 8 fragment reads, then per sub-step 8 reads of the
+    // next fragments spread one per 2 MFMAs, global->LDS loads spread over the
+    // first two sub-steps.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (kk < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
   }
 
   // ------------------------------------------------------------ epilogues
