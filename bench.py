@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
     ap.add_argument("--cpu-sample", type=float, default=1.0 / 32,
                     help="fraction of row-separable oracle work timed for the CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run spts_gather over 1 GiB with identity rows (a plain copy of known size, "
+                         "to scale HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -113,6 +116,28 @@ def breakdown(summary, steps):
     return out
 
 
+def measured_traffic(call):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if that summary was taken on the
+    current kernel source (else None)."""
+    import hashlib
+    import re
+    if call != "ffn_gate_up":
+        return None
+    path = os.path.join(ROOT, "profiles", "ffn_gate_up_gemm_traffic.md")
+    src = os.path.join(ROOT, "free_token_skipping_amd", "csrc", "gemm.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+    if not m_sha or not m_tr or m_sha.group(1) != sha:
+        return None
+    return float(m_tr.group(1))
+
+
 def roofline(summary, steps):
     """Dominant single-kernel call by time: achieved = algorithmic FLOPs per
     launch / average launch time (events on the launching stream)."""
@@ -122,7 +147,7 @@ def roofline(summary, steps):
     flops_per_launch = work / calls
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
             "kernel": KERNEL_OF_CALL.get(name, name), "call": name,
             "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_ms, 4),
             "launches_per_step": calls // steps}
@@ -224,6 +249,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fused = not args.unfused
+    if args.calibrate_copy:
+        rows, width = 131072, 4096                       # 1 GiB of bf16 read + 1 GiB written
+        src = torch.ones((rows, width), dtype=torch.bfloat16, device=dev)
+        ident = torch.arange(rows, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            capi.spts_gather(src, ident, dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": rows * width * 2, "bytes_written": rows * width * 2,
+                          "dispatches": 3}), flush=True)
+        return
 
     cfgd, sh, st, x0, layers = stack_inputs(dev)
     N = sh.n

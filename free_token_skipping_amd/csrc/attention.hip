@@ -23,14 +23,13 @@ namespace {
 constexpr int KT = 64;          // keys per LDS tile
 constexpr int DH = 128;
 
-// K tile [64 keys][128] in LDS: 16-byte chunk XOR-swizzled with bits {0,1,3}
-// of the key row (the rows 8 neighbouring lanes read under the permutation).
-__device__ __forceinline__ int kswz(int key, int chunk) {
-  const int f = (key & 3) | ((key & 8) >> 1);
-  return key * DH + ((chunk ^ f) << 3);
-}
-// V^T tile [128 dh][64 keys] in LDS: chunk XOR (dh & 7).
-__device__ __forceinline__ int vswz(int d, int chunk) { return d * KT + ((chunk ^ (d & 7)) << 3); }
+// LDS swizzles.  gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a
+// time across 64 banks (256 bytes); the 16 rows read together must fall in
+// 16 distinct 16-byte slots of that window.
+// K tile [64 keys][128] (256-byte rows): chunk XOR (key & 15).
+__device__ __forceinline__ int kswz(int key, int chunk) { return key * DH + ((chunk ^ (key & 15)) << 3); }
+// V^T tile [128 dh][64 keys] (128-byte rows, two rows per window): chunk XOR ((dh >> 1) & 7).
+__device__ __forceinline__ int vswz(int d, int chunk) { return d * KT + ((chunk ^ ((d >> 1) & 7)) << 3); }
 // MFMA A-row -> key row within a 32-key tile: swap index bits 2 and 3.
 __device__ __forceinline__ int perm32(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
@@ -335,21 +334,28 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
   }
 }
 
-// Pass 1b: combine chunk partials -> per (head, probe) max and 1/sum.
-__global__ void probe_combine_kernel(const float* __restrict__ part_m, const float* __restrict__ part_l,
-                                     int nchunks, int HP, float* __restrict__ fin_m,
-                                     float* __restrict__ fin_il) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// Pass 1b: combine chunk partials -> per (head, probe) max and 1/sum.  One
+// wave per (head, probe); lanes stride over chunks, fixed-order wave tree.
+__global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restrict__ part_m,
+                                                            const float* __restrict__ part_l, int nchunks,
+                                                            int HP, float* __restrict__ fin_m,
+                                                            float* __restrict__ fin_il) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (i >= HP) return;
   float mt = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) mt = fmaxf(mt, part_m[(long)c * HP + i]);
+  for (int c = lane; c < nchunks; c += 64) mt = fmaxf(mt, part_m[(long)c * HP + i]);
+  mt = wave_max(mt);
   float lt = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = lane; c < nchunks; c += 64) {
     const float mc = part_m[(long)c * HP + i];
     if (mc != -INFINITY) lt += part_l[(long)c * HP + i] * exp2f(mc - mt);
   }
-  fin_m[i] = mt;
-  fin_il[i] = 1.0f / lt;
+  lt = wave_sum(lt);
+  if (lane == 0) {
+    fin_m[i] = mt;
+    fin_il[i] = 1.0f / lt;
+  }
 }
 
 // Pass 2: column sums of the normalised probe softmax for one key chunk and
@@ -536,7 +542,7 @@ hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P,
   case PT:                                                                                         \
     hipLaunchKernelGGL(probe_stats_kernel<PT>, grid, dim3(256), 0, s, q, k, n, Hq, Hkv, sl2,      \
                        part_m, part_l);                                                            \
-    hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 255) / 256), dim3(256), 0, s, part_m,     \
+    hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_m,         \
                        part_l, nchunks, (int)HP, fin_m, fin_il);                                   \
     hipLaunchKernelGGL(probe_colsum_kernel<PT>, grid, dim3(256), 0, s, q, k, n, Hq, Hkv, sl2,     \
                        fin_m, fin_il, quad);                                                       \

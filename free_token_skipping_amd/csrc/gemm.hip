@@ -24,8 +24,13 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 256;
 constexpr int TILE_ELEMS = BM * BK;  // per operand per stage
 
-__device__ __forceinline__ int swz(int row, int chunk) {  // element offset in a 64-wide LDS tile
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+// Element offset in a 64-wide (128-byte-row) LDS tile.  gfx950 serves a
+// 16-byte-per-lane LDS read 16 lanes at a time across 64 banks (256 bytes), so
+// the 16 rows read together must land in 16 distinct 16-byte slots: rows of
+// equal parity share a 128-byte half, and XOR-ing the chunk with (row >> 1)
+// spreads each half's 8 rows over its 8 slots.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 template <int EPI, bool GATHER>
@@ -41,22 +46,36 @@ void gemm_tn_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, half = lane >> 5;
 
+  // ---- tile order.  Workgroups are dealt round-robin to the 8 XCDs, so
+  // workgroup b runs on XCD b % 8.  Each XCD gets a contiguous run of the
+  // logical tile order, and that order walks groups of GROUP_M row tiles
+  // across all column tiles, so the ~32 tiles resident on one XCD at a time
+  // form a 4 x 8 block that shares A and B k-slices in that XCD's L2.
   const int tiles_m = (g.m + BM - 1) / BM;
-  const int tile_m = blockIdx.x % tiles_m;
-  const int tile_n = blockIdx.x / tiles_m;
+  const int tiles_n = (EPI == EPI_SWIGLU) ? (g.n / 2) / 128 : g.n / BN;
+  const int total = tiles_m * tiles_n;
+  const int per_xcd = (total + 7) / 8;
+  const int logical = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+  if (logical >= total) return;                       // padding workgroups of the last XCD run
+  constexpr int GROUP_M = 4;
+  const int in_group = GROUP_M * tiles_n;
+  const int first_m = (logical / in_group) * GROUP_M;
+  const int gm = min(GROUP_M, tiles_m - first_m);
+  const int tile_m = first_m + (logical % in_group) % gm;
+  const int tile_n = (logical % in_group) / gm;
 
   // ---- direct global -> LDS staging.  Wave `wave`, instruction i writes the
   // 1 KiB block of tile rows rb*8 .. rb*8+7, rb = 4*i + wave; lane L lands at
-  // row rb*8 + L/8, physical chunk L%8, so it fetches the logical chunk
-  // (L%8) ^ (L/8) -- the XOR swizzle applied on the global side.
+  // row r = rb*8 + L/8, physical chunk L%8, so it fetches the logical chunk
+  // (L%8) ^ ((r >> 1) & 7) -- the swizzle of swz() applied on the global side.
   const int ld_sub = lane >> 3;                       // row within the 8-row block
-  const int ld_ch = (lane & 7) ^ ld_sub;              // logical 16-byte chunk fetched
   uint32_t a_off[8], b_off[8];                        // byte offsets of the staged rows
   unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int rb = 4 * i + wave;
     const int r = rb * 8 + ld_sub;                    // row within the 256-row tile
+    const int ld_ch = (lane & 7) ^ ((r >> 1) & 7);    // logical 16-byte chunk fetched
     int ar = tile_m * BM + r;
     if (ar >= g.m) ar = g.m - 1;
     if (GATHER) ar = g.a_rows[ar];
@@ -102,47 +121,63 @@ void gemm_tn_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // ---- software pipeline, one barrier per k-step.  Within k-step kt (stage
+  // cur): sub-steps 0..2 run their MFMAs while the next sub-step's fragments
+  // are read and the global->LDS loads of k-step kt+1 (stage nxt) are issued;
+  // then wait + barrier; then the first fragments of stage nxt are read while
+  // sub-step 3's MFMAs (fragments already in registers) run.  After the
+  // barrier no wave reads stage cur any more, so the next k-step may refill it.
+  bf16x8 af[2][4], bfm[2][4];
+  auto frag = [&](const uint16_t* a_s, const uint16_t* b_s, int kk, int set) {
+    const int ch = kk * 2 + half;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[set][i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 128 + i * 32 + l32, ch));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bfm[set][j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
+  };
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[set][j], af[set][i], acc[i][j]);
+  };
+
   issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  frag(As, Bs, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    __builtin_amdgcn_s_waitcnt(0);    // this wave's loads for stage `cur` have landed
-    __syncthreads();                  // ... and every wave's; stage cur^1 is free again
-    if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
+    const int cur = kt & 1, nxt = cur ^ 1;
     const uint16_t* a_s = As + cur * TILE_ELEMS;
     const uint16_t* b_s = Bs + cur * TILE_ELEMS;
-    bf16x8 af[2][4], bfm[2][4];
-    auto frag = [&](int kk, int set) {
-      const int ch = kk * 2 + half;
+    // the last k-step reloads its own tile into the idle stage (never read)
+    issue(kt + 1 < KT ? kt + 1 : kt, nxt);
+    frag(a_s, b_s, 1, 1);
+    mma(0);
+    frag(a_s, b_s, 2, 0);
+    mma(1);
+    frag(a_s, b_s, 3, 1);
+    mma(0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);     // global->LDS loads first
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[set][i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 128 + i * 32 + l32, ch));
+    for (int q = 0; q < 3; ++q) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfm[set][j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
-    };
-    frag(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) frag(kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[kk & 1][j], af[kk & 1][i], acc[i][j]);
-    }
-    // schedule: the first 8 fragment reads, then per sub-step 8 reads of the
-    // next fragments spread one per 2 MFMAs, global->LDS loads spread over the
-    // first two sub-steps.
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (kk < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      for (int r = 0; r < 8; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): stage nxt has landed
+    __syncthreads();
+    frag(As + nxt * TILE_ELEMS, Bs + nxt * TILE_ELEMS, 0, 0);
+    mma(1);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
   }
 
   // ------------------------------------------------------------ epilogues
@@ -168,7 +203,6 @@ void gemm_tn_kernel(GemmArgs g) {
     __syncthreads();
     if (wn == 0 && half == 0) {
       float* out = reinterpret_cast<float*>(g.out);
-      const int tiles_n = g.n / BN;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = tile_m * BM + wm * 128 + i * 32 + l32;
@@ -277,7 +311,8 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_tn_kernel<EPI, GATHER>), dim3(tiles_m * tiles_n), dim3(NTHREADS), lds, s, g);
+  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;     // a multiple of the 8 XCDs
+  hipLaunchKernelGGL((gemm_tn_kernel<EPI, GATHER>), dim3(grid), dim3(NTHREADS), lds, s, g);
   return hipGetLastError();
 }
 

@@ -69,24 +69,25 @@ __device__ float block_max(float v, float* sh) {
   return r;
 }
 
+// IPT > 0: each thread keeps the keys of its IPT contiguous rows in
+// registers across all passes (n <= 1024 * IPT).  IPT == 0: keys are re-read
+// from the workspace (any n).
+template <int IPT>
 __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a,
                                                    const float* __restrict__ s_b, float wa, float wb,
                                                    int n, int k, int nf, int32_t* __restrict__ idx,
                                                    float* __restrict__ fused_out,
                                                    uint32_t* __restrict__ keys) {
-  __shared__ int hist[256];
+  __shared__ int hist[NW][256];          // one histogram per wave (less atomic contention)
+  __shared__ int tot_hist[256];
   __shared__ int scan_sh[2 * NW];
   __shared__ float red[NW];
   __shared__ int sel[2];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6;
 
   if (k >= n) {
     for (int i = tid; i < n; i += TPB) idx[i] = i;
-    if (fused_out && s_b) {
-      // still report the fused score
-    } else {
-      return;
-    }
+    if (!(fused_out && s_b)) return;
   }
 
   float ma = 0.f, mb = 0.f;
@@ -96,14 +97,33 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     ma = block_max(la, red);
     mb = block_max(lb, red);
   }
-  for (int i = tid; i < n; i += TPB) {
-    const float x = s_b ? fuse(s_a[i], s_b[i], ma, mb, wa, wb) : s_a[i];
-    if (fused_out) fused_out[i] = x;
-    keys[i] = order_key(x);
+  const int per = IPT > 0 ? IPT : (n + TPB - 1) / TPB;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  uint32_t kr[IPT > 0 ? IPT : 1];
+  if (IPT > 0) {
+#pragma unroll
+    for (int j = 0; j < (IPT > 0 ? IPT : 1); ++j) {
+      const int i = lo + j;
+      uint32_t key = 0u;
+      if (i < hi) {
+        const float x = s_b ? fuse(s_a[i], s_b[i], ma, mb, wa, wb) : s_a[i];
+        if (fused_out) fused_out[i] = x;
+        key = order_key(x);
+      }
+      kr[j] = key;
+    }
+  } else {
+    for (int i = tid; i < n; i += TPB) {
+      const float x = s_b ? fuse(s_a[i], s_b[i], ma, mb, wa, wb) : s_a[i];
+      if (fused_out) fused_out[i] = x;
+      keys[i] = order_key(x);
+    }
+    __threadfence_block();
   }
   if (k >= n) return;
-  __threadfence_block();
   __syncthreads();
+
+  auto key_at = [&](int j, int i) -> uint32_t { return IPT > 0 ? kr[j] : keys[i]; };
 
   const int nfree = n - nf;
   const int kp = k - nf;            // rows to choose among the free ones
@@ -113,17 +133,23 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     uint32_t prefix = 0, mask = 0;
     int rem = kp;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += TPB) hist[i] = 0;
+      for (int i = tid; i < NW * 256; i += TPB) (&hist[0][0])[i] = 0;
       __syncthreads();
-      for (int i = tid; i < nfree; i += TPB) {
-        const uint32_t key = keys[i];
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      for (int j = 0, i = lo; i < min(hi, nfree); ++j, ++i) {
+        const uint32_t key = key_at(j, i);
+        if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        int t = 0;
+        for (int q = 0; q < NW; ++q) t += hist[q][tid];
+        tot_hist[tid] = t;
       }
       __syncthreads();
       if (tid < 64) {
         // suffix sums over 256 bins, 4 bins per lane, highest digit first
         const int b0 = 255 - tid * 4;
-        const int c0 = hist[b0], c1 = hist[b0 - 1], c2 = hist[b0 - 2], c3 = hist[b0 - 3];
+        const int c0 = tot_hist[b0], c1 = tot_hist[b0 - 1], c2 = tot_hist[b0 - 2], c3 = tot_hist[b0 - 3];
         const int part = c0 + c1 + c2 + c3;
         int incl = part;
 #pragma unroll
@@ -131,9 +157,8 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
           const int y = __shfl_up(incl, o);
           if (tid >= o) incl += y;
         }
-        const int excl = incl - part;   // count of keys with a larger digit than b0
-        // the digit holding the rem-th largest lies in this lane's 4 bins iff
-        // excl < rem <= incl
+        const int excl = incl - part;   // keys with a larger digit than b0
+        // the digit holding the rem-th largest lies in this lane's 4 bins iff excl < rem <= incl
         if (excl < rem && rem <= incl) {
           int above = excl, d = b0;
           const int cs[4] = {c0, c1, c2, c3};
@@ -156,21 +181,19 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     need_eq = rem;
   }
 
-  // compaction in index order; thread t owns rows [t*per, min(n, (t+1)*per))
-  const int per = (n + TPB - 1) / TPB;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  // compaction in index order over each thread's contiguous rows
   int n_eq = 0;
-  for (int i = lo; i < min(hi, nfree); ++i) n_eq += (keys[i] == T);
+  for (int j = 0, i = lo; i < min(hi, nfree); ++j, ++i) n_eq += (key_at(j, i) == T);
   int tot;
-  int eq_rank = block_exclusive_scan(n_eq, scan_sh, &tot);
+  const int eq_rank = block_exclusive_scan(n_eq, scan_sh, &tot);
   int n_sel = 0;
   {
     int r = eq_rank;
-    for (int i = lo; i < hi; ++i) {
+    for (int j = 0, i = lo; i < hi; ++j, ++i) {
       bool take;
       if (i >= nfree) take = true;
       else {
-        const uint32_t key = keys[i];
+        const uint32_t key = key_at(j, i);
         take = key > T || (key == T && r < need_eq);
         r += (key == T);
       }
@@ -180,11 +203,11 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   int out = block_exclusive_scan(n_sel, scan_sh, &tot);
   {
     int r = eq_rank;
-    for (int i = lo; i < hi; ++i) {
+    for (int j = 0, i = lo; i < hi; ++j, ++i) {
       bool take;
       if (i >= nfree) take = true;
       else {
-        const uint32_t key = keys[i];
+        const uint32_t key = key_at(j, i);
         take = key > T || (key == T && r < need_eq);
         r += (key == T);
       }
@@ -199,8 +222,13 @@ size_t topk_workspace(int n) { return (((size_t)n * 4) + 255) & ~(size_t)255; }
 
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, int n, int k,
                        int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, n, k, n_forced, idx,
-                     fused_out, reinterpret_cast<uint32_t*>(ws));
+  uint32_t* keys = reinterpret_cast<uint32_t*>(ws);
+  if (n <= TPB * 8)
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, keys);
+  else if (n <= TPB * 32)
+    hipLaunchKernelGGL(topk_kernel<32>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, keys);
+  else
+    hipLaunchKernelGGL(topk_kernel<0>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, keys);
   return hipGetLastError();
 }
 
