@@ -81,13 +81,27 @@ __device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* ks, uint
 
 // ============================================================ reduced attention
 // grid: (ceil(kq/64), Hq/4); block 512 = 8 waves: wave w serves query head
-// 4*blockIdx.y + (w & 3) for the 32 queries q0 + 32*(w >> 2) ..  +31.  Two
-// waves per SIMD, so one wave's softmax (VALU) overlaps the other's MFMA.
-// Softmax statistics use a lazily updated running max: the reference max only
-// moves when a lane's logits exceed it by more than 2^8 (in exp2 units), so
-// the O rescale is rare; p = exp2(s*scale*log2e - m) then stays <= 256 and
-// the final O / l is exact whatever reference max was used.
+// 4*blockIdx.y + (w & 3) for the 32 queries q0 + 32*(w >> 2) .. +31 (two
+// waves per SIMD).
+//
+// Software pipeline inside each wave: while the VALU turns the logits of
+// tile t into bf16 probabilities, the MFMA unit already forms the logits of
+// tile t+1 (K runs one tile ahead of V in the double-buffered LDS); then
+// O += V_t P_t.  Masking of tile t+1 and the reference-max update happen
+// after that, so the MFMA/VALU-overlapped region is one basic block.
+//
+// The reference max is updated lazily: only when a lane's logits exceed it
+// by more than 2^8 (exp2 units), so the O rescale is rare; p = exp2(s*scale*
+// log2e - m) then stays <= 256 and O / l is exact whatever reference was used.
+//
+// LDS rows are padded by 16 bytes instead of XOR-swizzled: gfx950 serves a
+// 16-byte-per-lane read 16 lanes at a time over a 256-byte bank window, and a
+// row stride of 17 (K) or 9 (V^T) 16-byte slots puts the 16 rows read together
+// in 16 distinct slots, while every fragment sits at a constant offset from
+// one per-lane base address.
 constexpr float kLazyMax = 8.0f;
+constexpr int KROW = DH + 8;     // K tile row: 128 dh + 8 pad elements (272 B)
+constexpr int VROW = KT + 8;     // V^T tile row: 64 keys + 8 pad elements (144 B)
 
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __restrict__ q,
                                                            const int32_t* __restrict__ idx,
@@ -95,8 +109,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ v, int kq,
                                                            int n, int Hq, int Hkv, float sl2,
                                                            uint16_t* __restrict__ o) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][DH * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][DH * VROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int nqb = (kq + 63) >> 6;
@@ -126,66 +140,73 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   float m_ref = -INFINITY, l_part = 0.f;             // l_part: this half-wave's keys only
   const f32x16 zero16 = {};
 
-  // ---- tile staging: K rows (2 x 16 B / thread), V as 2-key x 8-dh blocks.
+  // per-lane LDS fragment bases (elements); fragments are at constant offsets
+  const int kfrag = perm32(l32) * KROW + half * 8;   // + kt*32*KROW + kk*16
+  const int vfrag = l32 * VROW + half * 8;           // + d*32*VROW + ks4*16
+
+  // ---- staging: K rows (2 x 16 B / thread), V as 2-key x 8-dh blocks.
   // Element offsets fit in 32 bits (n * Hkv * 128 < 2^31 is checked on the host).
   const int row_stride = Hkv * DH;
   const uint16_t* kbase = k + g * DH + (tid & 15) * 8;
   const int kp = tid & 31, dc = tid >> 5;            // V: key pair, dh chunk
   const uint16_t* vbase = v + g * DH + dc * 8;
   u32x4 kr[2], vr[2];
-  auto load = [&](int j0) {
+  auto load_k = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = min(j0 + (tid >> 4) + 32 * i, n - 1);
       kr[i] = ld16(kbase + j * row_stride);
     }
+  };
+  auto load_v = [&](int j0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int j = min(j0 + 2 * kp + e, n - 1);
       vr[e] = ld16(vbase + j * row_stride);
     }
   };
-  auto store = [&](int buf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) st16(Ks[buf] + kswz((tid >> 4) + 32 * i, tid & 15), kr[i]);
+    for (int i = 0; i < 2; ++i) st16(Ks[buf] + ((tid >> 4) + 32 * i) * KROW + (tid & 15) * 8, kr[i]);
+  };
+  auto store_v = [&](int buf) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1;
       const uint32_t a = (e & 1) ? (vr[0][w] >> 16) : (vr[0][w] & 0xFFFFu);
       const uint32_t b = (e & 1) ? (vr[1][w] >> 16) : (vr[1][w] & 0xFFFFu);
-      *reinterpret_cast<uint32_t*>(Vs[buf] + vswz(dc * 8 + e, kp >> 2) + (kp & 3) * 2) = a | (b << 16);
+      *reinterpret_cast<uint32_t*>(Vs[buf] + (dc * 8 + e) * VROW + kp * 2) = a | (b << 16);
     }
   };
-
-  auto tile = [&](int t, bool MASK) {
-    const int buf = t & 1;
-    const int j0 = t * KT;
-    const uint16_t* ks = Ks[buf];
-    const uint16_t* vs = Vs[buf];
-    // S^T = K Q^T for 64 keys (rows permuted) x 32 queries
-    f32x16 s[2];
+  // logits S^T = K_t Q^T (64 keys, rows permuted, x 32 queries)
+  auto logits = [&](int buf, f32x16 (&sd)[2]) {
+    const uint16_t* ks = Ks[buf] + kfrag;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kswz(kt * 32 + perm32(l32), kk * 2 + half));
-        s[kt] = mfma32x32x16(kf, qf[kk], kk == 0 ? zero16 : s[kt]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kt * 32 * KROW + kk * 16);
+        sd[kt] = mfma32x32x16(kf, qf[kk], kk == 0 ? zero16 : sd[kt]);
       }
-    }
-    if (MASK) {
+  };
+  // mask tile t's keys beyond each query, then move the reference max if needed;
+  // key of reg r = t*64 + kt*32 + (r>>3)*16 + half*8 + (r&7)
+  auto prepare = [&](int t, f32x16 (&sd)[2]) {
+    if (t >= nfull) {
+      const int j0 = t * KT;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7);
-          if (key > qpos) s[kt][r] = -INFINITY;
+          if (key > qpos) sd[kt][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kt][r]), s[kt][r + 1]);
+      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sd[kt][r]), sd[kt][r + 1]);
     mx *= sl2;
     if (__any(mx > m_ref + kLazyMax)) {
       const float m_new = fmaxf(m_ref, fmaxf(mx, __shfl_xor(mx, 32)));
@@ -197,6 +218,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
         for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
       m_ref = m_new;
     }
+  };
+
+  // one pipeline step: tile t's logits are in sc (masked, reference max set)
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    if (t + 2 < ntiles) load_k((t + 2) * KT);
+    if (t + 1 < ntiles) load_v((t + 1) * KT);
+    // MFMA: logits of tile t+1 (stale data past the last tile; unused)  ||  VALU: P_t
+    logits((t + 1) & 1, sn);
     bf16x8 pf[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -205,30 +234,64 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
         f32x8 pv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][sub * 8 + e], sl2, -m_ref));
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][sub * 8 + e], sl2, -m_ref));
           l_part += pv[e];
         }
         pf[kt * 2 + sub] = __builtin_convertvector(pv, bf16x8);
       }
-    // O^T += V^T P^T
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);          // first K fragments
+#pragma unroll
+    for (int r = 0; r < 12; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one logit MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // next K fragment
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);        // softmax VALU
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    // O^T += V_t^T P_t^T
+    const uint16_t* vs = Vs[t & 1] + vfrag;
 #pragma unroll
     for (int ks4 = 0; ks4 < 4; ++ks4)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + vswz(d * 32 + l32, ks4 * 2 + half));
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + d * 32 * VROW + ks4 * 16);
         oacc[d] = mfma32x32x16(vf, pf[ks4], oacc[d]);
       }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int r = 0; r < 12; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    if (t + 2 < ntiles) store_k(t & 1);
+    if (t + 1 < ntiles) store_v((t + 1) & 1);
+    if (t + 1 < ntiles) prepare(t + 1, sn);
+    __syncthreads();
   };
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load((t + 1) * KT);
-    tile(t, t >= nfull);
-    if (t + 1 < ntiles) store((t + 1) & 1);
-    __syncthreads();
+  // prologue: K_0, V_0, K_1 staged; logits of tile 0
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (ntiles > 1) {
+    load_k(KT);
+    store_k(1);
   }
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  logits(0, sa);
+  prepare(0, sa);
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < ntiles) step(t, sa, sb);
 
   // normalise and store: lane = query, reg r of dh tile d -> dh d*32 + (r>>2)*8 + half*4 + (r&3)
   if (qi_raw < kq) {
