@@ -23,7 +23,7 @@ EXPORTS = [
     "spts_create", "spts_destroy", "spts_set_stream", "spts_set_workspace", "spts_last_error",
     "spts_status_name", "spts_check",
     "spts_probe_attention_workspace", "spts_score_topk_workspace", "spts_ltp_probe_workspace",
-    "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace",
+    "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
     "spts_probe_attention", "spts_score_topk", "spts_gather", "spts_scatter",
     "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
     "spts_linear", "spts_linear_rope", "spts_linear_swiglu", "spts_rope_table", "spts_rmsnorm",
@@ -44,6 +44,7 @@ _SIGS = {
     "spts_ltp_probe_workspace": (_SZ, [_I, _I, _I]),
     "spts_reduced_ffn_workspace": (_SZ, [_I, _I]),
     "spts_msdp_stage_workspace": (_SZ, [_I]),
+    "spts_linear_workspace": (_SZ, [_I, _I, _I]),
     "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
     "spts_gather": (_I, [_P, _I, _P, _P, _I, _I, _P]),
@@ -283,7 +284,7 @@ def spts_linear(a, w, a_rows=None, out=None, out_rows=None, accumulate=False):
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     ctx = context()
-    h = ctx.bind(0, a.device)
+    h = ctx.bind(lib().spts_linear_workspace(m, kdim, n), a.device)
     bf = torch.bfloat16
     _check(ctx, lib().spts_linear(h, _ptr(a, bf, "a"), _ptr(a_rows, torch.int32, "a_rows"), m, kdim,
                                   _ptr(w, bf, "w"), n, _ptr(out, bf, "out"), _ptr(out_rows, torch.int32, "out_rows"),
@@ -298,7 +299,7 @@ def spts_linear_rope(a, w, pos, table, a_rows=None, out=None):
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     ctx = context()
-    h = ctx.bind(0, a.device)
+    h = ctx.bind(lib().spts_linear_workspace(m, kdim, n), a.device)
     bf = torch.bfloat16
     _check(ctx, lib().spts_linear_rope(h, _ptr(a, bf, "a"), _ptr(a_rows, torch.int32, "a_rows"), m, kdim,
                                        _ptr(w, bf, "w"), n, _ptr(out, bf, "out"), _ptr(pos, torch.int32, "pos"),

@@ -124,11 +124,17 @@ size_t spts_probe_attention_workspace(int n, int P, int Hq) {
   return probe_workspace(n, P, Hq);
 }
 size_t spts_score_topk_workspace(int n) { return n > 0 ? topk_workspace(n) : 0; }
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 size_t spts_ltp_probe_workspace(int n, int d, int r) {
   if (n <= 0 || d <= 0 || r <= 0) return 0;
-  const size_t t2 = ((size_t)n * 2 * r * 2 + 255) & ~(size_t)255;      // z U as bf16 hi/lo
-  const size_t part = ((size_t)n * (d / 256) * 4 + 255) & ~(size_t)255; // row sums of squares
-  return t2 + part;
+  const size_t t2 = round256((size_t)n * 2 * r * 2);              // z U as bf16 hi/lo
+  const size_t part = round256((size_t)n * (d / 256) * 4);        // row sums of squares
+  return t2 + part + gemm_split_workspace(n, d, r, EPI_SPLIT);    // split-K partials of z U
+}
+size_t spts_linear_workspace(int m, int kdim, int n) {
+  if (m <= 0 || kdim <= 0 || n <= 0) return 0;
+  return gemm_split_workspace(m, kdim, n, EPI_STORE);
 }
 size_t spts_reduced_ffn_workspace(int k, int f) {
   if (k <= 0 || f <= 0) return 0;
@@ -286,6 +292,7 @@ spts_status spts_linear(spts_ctx* ctx, const void* a, const int32_t* a_rows, int
   g.a = reinterpret_cast<const uint16_t*>(a); g.a_rows = a_rows; g.m = m; g.k = kdim; g.lda = kdim;
   g.b0 = reinterpret_cast<const uint16_t*>(w); g.ldb = kdim; g.n = n;
   g.out = out; g.ldc = n; g.out_rows = out_rows; g.accumulate = accumulate;
+  g.partial = reinterpret_cast<float*>(ctx->ws); g.partial_bytes = ctx->ws_bytes;
   return hip_status(ctx, launch_gemm(g, EPI_STORE, ctx->stream), "linear");
 }
 
@@ -301,6 +308,7 @@ spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows
   g.a = reinterpret_cast<const uint16_t*>(a); g.a_rows = a_rows; g.m = m; g.k = kdim; g.lda = kdim;
   g.b0 = reinterpret_cast<const uint16_t*>(w); g.ldb = kdim; g.n = n;
   g.out = out; g.ldc = n; g.pos = pos; g.rope_table = table;
+  g.partial = reinterpret_cast<float*>(ctx->ws); g.partial_bytes = ctx->ws_bytes;
   return hip_status(ctx, launch_gemm(g, EPI_ROPE, ctx->stream), "linear_rope");
 }
 
@@ -350,13 +358,16 @@ spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const 
   const size_t need = spts_ltp_probe_workspace(n, d, r);
   REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
   uint16_t* t2 = reinterpret_cast<uint16_t*>(ctx->ws);
-  const size_t t2_bytes = ((size_t)n * 2 * r * 2 + 255) & ~(size_t)255;
+  const size_t t2_bytes = round256((size_t)n * 2 * r * 2);
+  const size_t part_bytes = round256((size_t)n * (d / 256) * 4);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + t2_bytes);
+  float* split_ws = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + t2_bytes + part_bytes);
   // T = z U, stored as bf16 hi + lo halves [n, 2r]
   GemmArgs g1{};
   g1.a = reinterpret_cast<const uint16_t*>(z); g1.m = n; g1.k = d; g1.lda = d;
   g1.b0 = reinterpret_cast<const uint16_t*>(u_t); g1.ldb = d; g1.n = r;
   g1.out = t2; g1.ldc = 2 * r;
+  g1.partial = split_ws; g1.partial_bytes = ctx->ws_bytes - t2_bytes - part_bytes;
   hipError_t e = launch_gemm(g1, EPI_SPLIT, ctx->stream);
   if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe (z U)");
   // (T_hi + T_lo) V: inner dimension 2r with V's columns read modulo r

@@ -15,6 +15,8 @@
 // The MFMA is issued as (B fragment, A fragment) so each lane's accumulators
 // hold ONE row of C and 4 groups of 4 consecutive columns; every epilogue
 // (row scatter, RoPE pairs, SwiGLU pairs, row norms) is then lane-local.
+#include <cmath>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -53,10 +55,13 @@ void gemm_tn_kernel(GemmArgs g) {
   // form a 4 x 8 block that shares A and B k-slices in that XCD's L2.
   const int tiles_m = (g.m + BM - 1) / BM;
   const int tiles_n = (EPI == EPI_SWIGLU) ? (g.n / 2) / 128 : g.n / BN;
-  const int total = tiles_m * tiles_n;
+  const int ksplit = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
+  const int total = tiles_m * tiles_n * ksplit;
   const int per_xcd = (total + 7) / 8;
-  const int logical = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
-  if (logical >= total) return;                       // padding workgroups of the last XCD run
+  const int logical_k = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+  if (logical_k >= total) return;                     // padding workgroups of the last XCD run
+  const int kslice = logical_k % ksplit;              // split-K slice (0 without split)
+  const int logical = logical_k / ksplit;
   constexpr int GROUP_M = 4;
   const int in_group = GROUP_M * tiles_n;
   const int first_m = (logical / in_group) * GROUP_M;
@@ -93,9 +98,11 @@ void gemm_tn_kernel(GemmArgs g) {
   const char* abase = reinterpret_cast<const char*>(g.a);
   const char* b0base = reinterpret_cast<const char*>(g.b0);
   const char* b1base = reinterpret_cast<const char*>(g.b1);
-  const int KT = g.k / BK;
+  const int KT = g.k / BK / ksplit;                    // k-steps of this slice
+  const int kt_base = kslice * KT;
 
-  auto issue = [&](int kt, int stage) {
+  auto issue = [&](int kt_local, int stage) {
+    const int kt = kt_base + kt_local;
     const uint32_t ka = (uint32_t)kt * BK * 2u;
     const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
     uint16_t* a_s = As + stage * TILE_ELEMS;
@@ -183,6 +190,26 @@ void gemm_tn_kernel(GemmArgs g) {
   // ------------------------------------------------------------ epilogues
   // lane holds C[row][col] for row = tile_m*BM + wm*128 + i*32 + l32 and
   // col = (tile base) + wn*128 + j*32 + q*8 + half*4 + e, r = q*4 + e.
+  if (EPI == EPI_PARTIAL) {
+    float* part = g.partial + (long)kslice * g.m * g.n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile_m * BM + wm * 128 + i * 32 + l32;
+      if (row >= g.m) continue;
+      float* prow = part + (long)row * g.n;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
+          *reinterpret_cast<f32x4*>(prow + col) = v;
+        }
+    }
+    return;
+  }
   if (EPI == EPI_SUMSQ) {
     float* red = reinterpret_cast<float*>(smem);   // [2 wm][4 i][32 rows] from wn == 1
     float ss[4];
@@ -299,6 +326,69 @@ void gemm_tn_kernel(GemmArgs g) {
   }
 }
 
+// Split-K finish: sum the fp32 slices in slice order and apply the epilogue.
+// Thread = (row, 4-column group); for RoPE only groups in the first half of
+// a 128-wide head work, each handling its pair group c+64.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
+  const long groups = (long)g.m * (g.n / 4);
+  for (long u = (long)blockIdx.x * blockDim.x + threadIdx.x; u < groups; u += (long)gridDim.x * blockDim.x) {
+    const int row = (int)(u / (g.n / 4));
+    const int col = (int)(u % (g.n / 4)) * 4;
+    if (EPI == EPI_ROPE && (col & 127) >= 64) continue;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < g.ksplit; ++ks) {
+      const float* prow = g.partial + ((long)ks * g.m + row) * g.n;
+      a += *reinterpret_cast<const f32x4*>(prow + col);
+      if (EPI == EPI_ROPE) b += *reinterpret_cast<const f32x4*>(prow + col + 64);
+    }
+    if (EPI == EPI_ROPE) {
+      const int arow = g.a_rows ? g.a_rows[row] : row;
+      const float* tab = g.rope_table + (long)g.pos[arow] * 128;
+      const int c0 = col & 127;
+      f32x4 y1, y2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float cs = tab[2 * (c0 + e)], sn = tab[2 * (c0 + e) + 1];
+        y1[e] = a[e] * cs - b[e] * sn;
+        y2[e] = b[e] * cs + a[e] * sn;
+      }
+      uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)row * g.ldc;
+      u32x2 w1, w2;
+      w1[0] = pack2bf(y1[0], y1[1]); w1[1] = pack2bf(y1[2], y1[3]);
+      w2[0] = pack2bf(y2[0], y2[1]); w2[1] = pack2bf(y2[2], y2[3]);
+      *reinterpret_cast<u32x2*>(out + col) = w1;
+      *reinterpret_cast<u32x2*>(out + col + 64) = w2;
+    } else if (EPI == EPI_SPLIT) {
+      uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)row * g.ldc;
+      float hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = bf2f(f2bf(a[e]));
+        lo[e] = a[e] - hi[e];
+      }
+      u32x2 wh, wl;
+      wh[0] = pack2bf(hi[0], hi[1]); wh[1] = pack2bf(hi[2], hi[3]);
+      wl[0] = pack2bf(lo[0], lo[1]); wl[1] = pack2bf(lo[2], lo[3]);
+      *reinterpret_cast<u32x2*>(out + col) = wh;
+      *reinterpret_cast<u32x2*>(out + g.n + col) = wl;
+    } else {   // EPI_STORE
+      const int orow = g.out_rows ? g.out_rows[row] : row;
+      uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)orow * g.ldc;
+      u32x2 w;
+      if (g.accumulate) {
+        const u32x2 old = *reinterpret_cast<const u32x2*>(out + col);
+        w[0] = pack2bf(lo_bf(old[0]) + bf2f(f2bf(a[0])), hi_bf(old[0]) + bf2f(f2bf(a[1])));
+        w[1] = pack2bf(lo_bf(old[1]) + bf2f(f2bf(a[2])), hi_bf(old[1]) + bf2f(f2bf(a[3])));
+      } else {
+        w[0] = pack2bf(a[0], a[1]);
+        w[1] = pack2bf(a[2], a[3]);
+      }
+      *reinterpret_cast<u32x2*>(out + col) = w;
+    }
+  }
+}
+
 template <int EPI, bool GATHER>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.m + BM - 1) / BM;
@@ -311,15 +401,58 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;     // a multiple of the 8 XCDs
+  const int ks = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
+  const int grid = ((tiles_m * tiles_n * ks + 7) / 8) * 8;     // a multiple of the 8 XCDs
   hipLaunchKernelGGL((gemm_tn_kernel<EPI, GATHER>), dim3(grid), dim3(NTHREADS), lds, s, g);
   return hipGetLastError();
 }
 
+// Cost model for the split count: workgroup waves over 256 CUs times the time
+// of one 256x256 tile over its k range, plus the partial-sum round trip.
+int choose_ksplit(int m, int k, int n) {
+  const double tiles = (double)((m + BM - 1) / BM) * (n / BN);
+  const double per_tile_s = 2.0 * BM * BN * (double)k / 3.9e12;     // ~1 PFLOP/s over 256 CUs
+  int best = 1;
+  double best_t = std::ceil(tiles / 256.0) * per_tile_s;
+  for (int ks = 2; ks <= 16; ++ks) {
+    if (k % (ks * BK) != 0) continue;
+    const double t = std::ceil(tiles * ks / 256.0) * per_tile_s / ks + (double)ks * m * n * 8.0 / 5.0e12 + 4e-6;
+    if (t < 0.9 * best_t) { best = ks; best_t = t; }
+  }
+  return best;
+}
+
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
-  const bool gather = g.a_rows != nullptr;
+int gemm_ksplit(int m, int k, int n, int epi) {
+  if (epi != EPI_STORE && epi != EPI_ROPE && epi != EPI_SPLIT) return 1;
+  return choose_ksplit(m, k, n);
+}
+
+size_t gemm_split_workspace(int m, int k, int n, int epi) {
+  const int ks = gemm_ksplit(m, k, n, epi);
+  return ks > 1 ? (size_t)ks * m * n * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm(const GemmArgs& g0, int epi, hipStream_t s) {
+  const bool gather = g0.a_rows != nullptr;
+  GemmArgs g = g0;
+  g.ksplit = 1;
+  const int ks = gemm_ksplit(g.m, g.k, g.n, epi);
+  if (ks > 1 && g.partial && g.partial_bytes >= (size_t)ks * g.m * g.n * sizeof(float)) {
+    g.ksplit = ks;
+    hipError_t e = gather ? launch_one<EPI_PARTIAL, true>(g, s) : launch_one<EPI_PARTIAL, false>(g, s);
+    if (e != hipSuccess) return e;
+    const long groups = (long)g.m * (g.n / 4);
+    long blocks = (groups + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL(gemm_reduce_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s, g); break;
+      case EPI_ROPE: hipLaunchKernelGGL(gemm_reduce_kernel<EPI_ROPE>, dim3(blocks), dim3(256), 0, s, g); break;
+      default: hipLaunchKernelGGL(gemm_reduce_kernel<EPI_SPLIT>, dim3(blocks), dim3(256), 0, s, g); break;
+    }
+    return hipGetLastError();
+  }
   switch (epi) {
     case EPI_STORE: return gather ? launch_one<EPI_STORE, true>(g, s) : launch_one<EPI_STORE, false>(g, s);
     case EPI_ROPE: return gather ? launch_one<EPI_ROPE, true>(g, s) : launch_one<EPI_ROPE, false>(g, s);

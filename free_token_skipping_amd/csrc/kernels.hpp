@@ -16,6 +16,7 @@ enum GemmEpilogue : int {
   EPI_SWIGLU = 2,  // bf16 out = silu(A Wg^T) * (A Wu^T); b0 = Wg, b1 = Wu
   EPI_SPLIT = 3,   // fp32 result t written as bf16 pair hi=bf16(t), lo=bf16(t-hi)
   EPI_SUMSQ = 4,   // fp32 out[i, tile_n] = sum over the tile's 256 columns of c^2
+  EPI_PARTIAL = 5, // split-K pass: fp32 partial[ks][i][c] (internal)
 };
 
 struct GemmArgs {
@@ -33,8 +34,15 @@ struct GemmArgs {
   int accumulate;
   const int32_t* pos;       // ROPE: original position per A row (indexed like A rows)
   const float* rope_table;  // ROPE: [max_pos, 64, 2]
+  float* partial;           // split-K workspace (nullable: never split)
+  size_t partial_bytes;
+  int ksplit;               // set by the launcher
 };
 
+// Split count the launcher would use for this problem (1 = no split) and the
+// workspace it then needs.
+int gemm_ksplit(int m, int k, int n, int epilogue);
+size_t gemm_split_workspace(int m, int k, int n, int epilogue);
 hipError_t launch_gemm(const GemmArgs& g, int epilogue, hipStream_t s);
 
 // ------------------------------------------------------------ attention

@@ -80,6 +80,11 @@ size_t spts_score_topk_workspace(int n);
 size_t spts_ltp_probe_workspace(int n, int d, int r);
 size_t spts_reduced_ffn_workspace(int k, int f);
 size_t spts_msdp_stage_workspace(int n_prev);
+/* Workspace with which spts_linear / spts_linear_rope split the inner
+ * dimension across workgroups (fp32 partial sums, then a fixed-order
+ * reduction); 0 when the problem is not split.  Smaller workspaces make the
+ * call run unsplit (same result, possibly slower). */
+size_t spts_linear_workspace(int m, int kdim, int n);
 
 /* ----------------------------------------------------------------- PAP */
 
