@@ -5,12 +5,12 @@
 // the reduced SwiGLU FFN).  Both operands are k-contiguous, so a wave reads
 // each MFMA fragment as one 16-byte LDS load.
 //
-// Tiling: 256 x 256 x 64 per workgroup, 4 waves in a 2 x 2 grid, each wave
-// owns a 128 x 128 block = 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32
-// accumulators per lane).  Global -> registers -> LDS staging, double-buffered
-// LDS (2 x 64 KiB), one barrier per k-step.  LDS rows are 128 B with the
-// 16-byte chunk index XOR-ed with (row & 7), so the 8 lanes that share a bank
-// window always hit 8 distinct chunks.
+// Tiling: 256 x 256 x 64 per workgroup, 8 waves in a 4 (M) x 2 (N) grid, each
+// wave owns a 64 x 128 block = 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (128
+// fp32 accumulators per lane), two waves per SIMD.  Operands go straight from
+// global memory into double-buffered LDS (2 x 64 KiB), one barrier per
+// k-step; while one wave of a SIMD waits on its loads or the barrier, the
+// other keeps the matrix core busy.
 //
 // The MFMA is issued as (B fragment, A fragment) so each lane's accumulators
 // hold ONE row of C and 4 groups of 4 consecutive columns; every epilogue
@@ -23,7 +23,7 @@
 namespace spts {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 256;
+constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512;
 constexpr int TILE_ELEMS = BM * BK;  // per operand per stage
 
 // Element offset in a 64-wide (128-byte-row) LDS tile.  gfx950 serves a
@@ -36,7 +36,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 template <int EPI, bool GATHER>
-__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NTHREADS, 1)
 void gemm_tn_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* As = smem;                       // [2][BM*BK]
@@ -45,7 +45,7 @@ void gemm_tn_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;          // 4 x 2 waves
   const int l32 = lane & 31, half = lane >> 5;
 
   // ---- tile order.  Workgroups are dealt round-robin to the 8 XCDs, so
@@ -70,15 +70,15 @@ void gemm_tn_kernel(GemmArgs g) {
   const int tile_n = (logical % in_group) / gm;
 
   // ---- direct global -> LDS staging.  Wave `wave`, instruction i writes the
-  // 1 KiB block of tile rows rb*8 .. rb*8+7, rb = 4*i + wave; lane L lands at
+  // 1 KiB block of tile rows rb*8 .. rb*8+7, rb = 8*i + wave; lane L lands at
   // row r = rb*8 + L/8, physical chunk L%8, so it fetches the logical chunk
   // (L%8) ^ ((r >> 1) & 7) -- the swizzle of swz() applied on the global side.
   const int ld_sub = lane >> 3;                       // row within the 8-row block
-  uint32_t a_off[8], b_off[8];                        // byte offsets of the staged rows
+  uint32_t a_off[4], b_off[4];                        // byte offsets of the staged rows
   unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rb = 4 * i + wave;
+  for (int i = 0; i < 4; ++i) {
+    const int rb = 8 * i + wave;
     const int r = rb * 8 + ld_sub;                    // row within the 256-row tile
     const int ld_ch = (lane & 7) ^ ((r >> 1) & 7);    // logical 16-byte chunk fetched
     int ar = tile_m * BM + r;
@@ -108,8 +108,8 @@ void gemm_tn_kernel(GemmArgs g) {
     uint16_t* a_s = As + stage * TILE_ELEMS;
     uint16_t* b_s = Bs + stage * TILE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rb = 4 * i + wave;
+    for (int i = 0; i < 4; ++i) {
+      const int rb = 8 * i + wave;
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(abase + a_off[i] + ka),
           (__attribute__((address_space(3))) void*)(a_s + rb * 512), 16, 0, 0);
@@ -120,81 +120,52 @@ void gemm_tn_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // ---- software pipeline, one barrier per k-step.  Within k-step kt (stage
-  // cur): sub-steps 0..2 run their MFMAs while the next sub-step's fragments
-  // are read and the global->LDS loads of k-step kt+1 (stage nxt) are issued;
-  // then wait + barrier; then the first fragments of stage nxt are read while
-  // sub-step 3's MFMAs (fragments already in registers) run.  After the
-  // barrier no wave reads stage cur any more, so the next k-step may refill it.
-  bf16x8 af[2][4], bfm[2][4];
-  auto frag = [&](const uint16_t* a_s, const uint16_t* b_s, int kk, int set) {
-    const int ch = kk * 2 + half;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[set][i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 128 + i * 32 + l32, ch));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bfm[set][j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
-  };
-  auto mma = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[set][j], af[set][i], acc[i][j]);
-  };
-
+  // k-step kt reads stage kt & 1 while the loads of k-step kt+1 fill the
+  // other stage; the wait + barrier at its end hands both stages over.
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  frag(As, Bs, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
+    const int cur = kt & 1;
+    // the last k-step reloads its own tile into the idle stage (never read)
+    issue(kt + 1 < KT ? kt + 1 : kt, cur ^ 1);
     const uint16_t* a_s = As + cur * TILE_ELEMS;
     const uint16_t* b_s = Bs + cur * TILE_ELEMS;
-    // the last k-step reloads its own tile into the idle stage (never read)
-    issue(kt + 1 < KT ? kt + 1 : kt, nxt);
-    frag(a_s, b_s, 1, 1);
-    mma(0);
-    frag(a_s, b_s, 2, 0);
-    mma(1);
-    frag(a_s, b_s, 3, 1);
-    mma(0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);     // global->LDS loads first
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int ch = kk * 2 + half;
+      bf16x8 af[2], bfm[4];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-      }
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 64 + i * 32 + l32, ch));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfm[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[j], af[i], acc[i][j]);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0): stage nxt has landed
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    frag(As + nxt * TILE_ELEMS, Bs + nxt * TILE_ELEMS, 0, 0);
-    mma(1);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
   }
 
   // ------------------------------------------------------------ epilogues
-  // lane holds C[row][col] for row = tile_m*BM + wm*128 + i*32 + l32 and
+  // lane holds C[row][col] for row = tile_m*BM + wm*64 + i*32 + l32 and
   // col = (tile base) + wn*128 + j*32 + q*8 + half*4 + e, r = q*4 + e.
   if (EPI == EPI_PARTIAL) {
     float* part = g.partial + (long)kslice * g.m * g.n;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = tile_m * BM + wm * 128 + i * 32 + l32;
+    for (int i = 0; i < 2; ++i) {
+      const int row = tile_m * BM + wm * 64 + i * 32 + l32;
       if (row >= g.m) continue;
       float* prow = part + (long)row * g.n;
 #pragma unroll
@@ -211,10 +182,10 @@ void gemm_tn_kernel(GemmArgs g) {
     return;
   }
   if (EPI == EPI_SUMSQ) {
-    float* red = reinterpret_cast<float*>(smem);   // [2 wm][4 i][32 rows] from wn == 1
-    float ss[4];
+    float* red = reinterpret_cast<float*>(smem);   // [4 wm][2 i][32 rows] from wn == 1
+    float ss[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       float t = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -225,23 +196,23 @@ void gemm_tn_kernel(GemmArgs g) {
     }
     if (wn == 1 && half == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[(wm * 4 + i) * 32 + l32] = ss[i];
+      for (int i = 0; i < 2; ++i) red[(wm * 2 + i) * 32 + l32] = ss[i];
     }
     __syncthreads();
     if (wn == 0 && half == 0) {
       float* out = reinterpret_cast<float*>(g.out);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = tile_m * BM + wm * 128 + i * 32 + l32;
-        if (row < g.m) out[(long)row * tiles_n + tile_n] = ss[i] + red[(wm * 4 + i) * 32 + l32];
+      for (int i = 0; i < 2; ++i) {
+        const int row = tile_m * BM + wm * 64 + i * 32 + l32;
+        if (row < g.m) out[(long)row * tiles_n + tile_n] = ss[i] + red[(wm * 2 + i) * 32 + l32];
       }
     }
     return;
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = tile_m * BM + wm * 128 + i * 32 + l32;
+  for (int i = 0; i < 2; ++i) {
+    const int row = tile_m * BM + wm * 64 + i * 32 + l32;
     if (row >= g.m) continue;
     if (EPI == EPI_SWIGLU) {
       uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)row * g.ldc;
@@ -411,7 +382,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
 // of one 256x256 tile over its k range, plus the partial-sum round trip.
 int choose_ksplit(int m, int k, int n) {
   const double tiles = (double)((m + BM - 1) / BM) * (n / BN);
-  const double per_tile_s = 2.0 * BM * BN * (double)k / 3.9e12;     // ~1 PFLOP/s over 256 CUs
+  const double per_tile_s = 2.0 * BM * BN * (double)k / 4.4e12;     // ~1.1 PFLOP/s over 256 CUs
   int best = 1;
   double best_t = std::ceil(tiles / 256.0) * per_tile_s;
   for (int ks = 2; ks <= 16; ++ks) {
