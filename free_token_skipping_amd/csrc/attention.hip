@@ -80,9 +80,9 @@ __device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* ks, uint
 }
 
 // ============================================================ reduced attention
-// grid: (ceil(kq/64), Hq/4); block 512 = 8 waves: wave w serves query head
-// 4*blockIdx.y + (w & 3) for the 32 queries q0 + 32*(w >> 2) .. +31 (two
-// waves per SIMD).
+// grid: ceil(kq/64) * Hq/4 workgroups, one per (64-query block, group of 4
+// query heads); block 512 = 8 waves: wave w serves query head 4*hg + (w & 3)
+// for the 32 queries q0 + 32*(w >> 2) .. +31 (two waves per SIMD).
 //
 // Software pipeline inside each wave: while the VALU turns the logits of
 // tile t into bf16 probabilities, the MFMA unit already forms the logits of
@@ -113,10 +113,17 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][DH * VROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
+  // Workgroup id -> (query block, 4-head group): all head groups of the
+  // latest (longest) query block first, so the causal work shrinks
+  // monotonically over the dispatch and the tail holds the short blocks.
+  // Workgroup b runs on XCD b % 8, so with 8 head groups each XCD's L2 serves
+  // one KV head.
   const int nqb = (kq + 63) >> 6;
-  const int qb = nqb - 1 - (int)blockIdx.x;          // latest (longest) query blocks first
-  const int h = blockIdx.y * 4 + (wave & 3);
-  const int g = (blockIdx.y * 4) / (Hq / Hkv);
+  const int hgs = Hq >> 2;
+  const int qb = nqb - 1 - (int)blockIdx.x / hgs;
+  const int hg = (int)blockIdx.x % hgs;
+  const int h = hg * 4 + (wave & 3);
+  const int g = (hg * 4) / (Hq / Hkv);
   const int q0 = qb * 64;
   const int qw = q0 + (wave >> 2) * 32;              // this wave's first query
 
@@ -634,7 +641,7 @@ hipError_t launch_probe_f32(const float* q, const float* k, int n, int P, int Hq
 hipError_t launch_attn_bf16(const uint16_t* q, const int32_t* idx, const uint16_t* k,
                             const uint16_t* v, int kq, int n, int Hq, int Hkv, float scale,
                             uint16_t* o, hipStream_t s) {
-  const dim3 grid((kq + 63) / 64, Hq / 4);
+  const dim3 grid(((kq + 63) / 64) * (Hq / 4));
   hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(512), 0, s, q, idx, k, v, kq, n, Hq, Hkv,
                      scale * kLog2e, o);
   return hipGetLastError();

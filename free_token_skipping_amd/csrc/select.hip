@@ -1,13 +1,19 @@
 // Top-k token selection with forced probe rows, gfx950.
 //
 // Scores (or the MaxNorm-Add fusion of two scores) are mapped to unsigned
-// keys whose integer order is the float order (NaN lowest, -0 == +0).  A
-// 4-pass, 8-bit radix select over the non-forced rows finds the threshold
-// key T of the (k - n_forced)-th largest and how many rows equal to T to
-// take; a block-wide scan in index order then writes exactly k ascending
-// indices: forced rows, rows above T, and the lowest-index rows equal to T.
+// keys whose integer order is the float order (NaN lowest, -0 == +0).  An
+// MSB-first radix select over the non-forced rows finds the threshold key T
+// of the (k - n_forced)-th largest and how many rows equal to T to take; a
+// ballot compaction in index order then writes exactly k ascending indices:
+// forced rows, rows above T, and the lowest-index rows equal to T.
+//
 // One 1024-thread workgroup does the whole selection: at 32K-128K scores the
-// input is 128-512 KiB and the call is bound by latency, not bandwidth.
+// input is 128-512 KiB and the call is bound by latency, not bandwidth.  Wave
+// w owns the contiguous rows [w*C, (w+1)*C) and its lanes walk them 64 at a
+// time, so every load is one coalesced 256-byte access.  The radix passes
+// skip the leading key bits that all free rows share (found by an OR/AND
+// reduction), so the first 8-bit digit already spreads the keys over many
+// histogram bins instead of piling them onto one sign/exponent bin.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,33 +37,6 @@ __device__ __forceinline__ float fuse(float a, float b, float ma, float mb, floa
   return __fadd_rn(ta, tb);
 }
 
-// Exclusive scan over the block; returns this thread's prefix, *total = sum.
-__device__ int block_exclusive_scan(int v, int* sh, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[w] = x;
-  __syncthreads();
-  if (w == 0) {
-    int t = lane < NW ? sh[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(t, o);
-      if (lane >= o) t += y;
-    }
-    if (lane < NW) sh[NW + lane] = t;      // inclusive wave prefix
-  }
-  __syncthreads();
-  const int wave_base = w ? sh[NW + w - 1] : 0;
-  *total = sh[NW + NW - 1];
-  __syncthreads();
-  return wave_base + x - v;
-}
-
 __device__ float block_max(float v, float* sh) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -69,9 +48,12 @@ __device__ float block_max(float v, float* sh) {
   return r;
 }
 
-// IPT > 0: each thread keeps the keys of its IPT contiguous rows in
-// registers across all passes (n <= 1024 * IPT).  IPT == 0: keys are re-read
-// from the workspace (any n).
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// IPT > 0: each lane keeps the keys of its IPT rows in registers across all
+// passes (n <= 1024 * IPT).  IPT == 0: keys are re-read from the workspace.
 template <int IPT>
 __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a,
                                                    const float* __restrict__ s_b, float wa, float wb,
@@ -80,10 +62,11 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
                                                    uint32_t* __restrict__ keys) {
   __shared__ int hist[NW][256];          // one histogram per wave (less atomic contention)
   __shared__ int tot_hist[256];
-  __shared__ int scan_sh[2 * NW];
   __shared__ float red[NW];
+  __shared__ uint32_t bits_sh[2][NW];
+  __shared__ int cnt_sh[2][NW];
   __shared__ int sel[2];
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
 
   if (k >= n) {
     for (int i = tid; i < n; i += TPB) idx[i] = i;
@@ -97,47 +80,64 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     ma = block_max(la, red);
     mb = block_max(lb, red);
   }
-  const int per = IPT > 0 ? IPT : (n + TPB - 1) / TPB;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  constexpr int UNROLL_J = IPT > 0 ? IPT : 1;
+  const int nfree = n - nf;
+  const int J = IPT > 0 ? IPT : (n + TPB - 1) / TPB;   // rows per lane (a constant if IPT > 0)
+  const int base = w * J * 64 + lane;                  // row of (w, j, lane) = base + 64 j
   uint32_t kr[IPT > 0 ? IPT : 1];
-  if (IPT > 0) {
-#pragma unroll
-    for (int j = 0; j < (IPT > 0 ? IPT : 1); ++j) {
-      const int i = lo + j;
-      uint32_t key = 0u;
-      if (i < hi) {
-        const float x = s_b ? fuse(s_a[i], s_b[i], ma, mb, wa, wb) : s_a[i];
-        if (fused_out) fused_out[i] = x;
-        key = order_key(x);
-      }
-      kr[j] = key;
-    }
-  } else {
-    for (int i = tid; i < n; i += TPB) {
+  uint32_t k_or = 0u, k_and = 0xFFFFFFFFu;             // over the free rows
+#pragma unroll UNROLL_J
+  for (int j = 0; j < J; ++j) {
+    const int i = base + 64 * j;
+    uint32_t key = 0u;
+    if (i < n) {
       const float x = s_b ? fuse(s_a[i], s_b[i], ma, mb, wa, wb) : s_a[i];
       if (fused_out) fused_out[i] = x;
-      keys[i] = order_key(x);
+      key = order_key(x);
+      if (i < nfree) { k_or |= key; k_and &= key; }
+      if (IPT == 0) keys[i] = key;
     }
-    __threadfence_block();
+    if (IPT > 0) kr[IPT > 0 ? j : 0] = key;
   }
   if (k >= n) return;
-  __syncthreads();
+  if (IPT == 0) __threadfence_block();
 
-  auto key_at = [&](int j, int i) -> uint32_t { return IPT > 0 ? kr[j] : keys[i]; };
+  auto key_at = [&](int j) -> uint32_t {
+    if (IPT > 0) return kr[j];
+    const int i = base + 64 * j;
+    return i < n ? keys[i] : 0u;                // the workspace holds n keys
+  };
 
-  const int nfree = n - nf;
   const int kp = k - nf;            // rows to choose among the free ones
-  uint32_t T = 0xFFFFFFFFu;         // no free row is selected when kp == 0
+  uint32_t T = 0xFFFFFFFFu;         // no free row is selected when kp == 0 (no key is all ones)
   int need_eq = 0;
   if (kp > 0) {
-    uint32_t prefix = 0, mask = 0;
+    // bits shared by every free key need no radix pass
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      k_or |= __shfl_xor(k_or, o);
+      k_and &= __shfl_xor(k_and, o);
+    }
+    if (lane == 0) { bits_sh[0][w] = k_or; bits_sh[1][w] = k_and; }
+    __syncthreads();
+    k_or = 0u; k_and = 0xFFFFFFFFu;
+    for (int q = 0; q < NW; ++q) { k_or |= bits_sh[0][q]; k_and &= bits_sh[1][q]; }
+    const uint32_t vary = k_or & ~k_and;
+    int R = vary ? 32 - __clz(vary) : 0;          // bits below the common prefix
+    uint32_t mask = R >= 32 ? 0u : ~((1u << R) - 1u);
+    uint32_t prefix = k_and & mask;
     int rem = kp;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    while (R > 0) {
+      const int width = R < 8 ? R : 8;
+      const int shift = R - width;
+      const uint32_t dmask = (1u << width) - 1u;
       for (int i = tid; i < NW * 256; i += TPB) (&hist[0][0])[i] = 0;
       __syncthreads();
-      for (int j = 0, i = lo; i < min(hi, nfree); ++j, ++i) {
-        const uint32_t key = key_at(j, i);
-        if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255], 1);
+#pragma unroll UNROLL_J
+      for (int j = 0; j < J; ++j) {
+        const int i = base + 64 * j;
+        const uint32_t key = key_at(j);
+        if (i < nfree && (key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & dmask], 1);
       }
       __syncthreads();
       if (tid < 256) {
@@ -171,48 +171,51 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
         }
       }
       __syncthreads();
-      const int d = sel[0];
+      prefix |= (uint32_t)sel[0] << shift;
       rem = sel[1];
-      prefix |= (uint32_t)d << shift;
-      mask |= 0xFFu << shift;
+      mask |= dmask << shift;
+      R = shift;
       __syncthreads();
     }
     T = prefix;
     need_eq = rem;
   }
 
-  // compaction in index order over each thread's contiguous rows
-  int n_eq = 0;
-  for (int j = 0, i = lo; i < min(hi, nfree); ++j, ++i) n_eq += (key_at(j, i) == T);
-  int tot;
-  const int eq_rank = block_exclusive_scan(n_eq, scan_sh, &tot);
-  int n_sel = 0;
-  {
-    int r = eq_rank;
-    for (int j = 0, i = lo; i < hi; ++j, ++i) {
-      bool take;
-      if (i >= nfree) take = true;
-      else {
-        const uint32_t key = key_at(j, i);
-        take = key > T || (key == T && r < need_eq);
-        r += (key == T);
-      }
-      n_sel += take;
-    }
+  // ---- compaction in index order.  Per wave: rows above T (and forced rows)
+  // and rows equal to T; then each wave knows how many equal rows precede it
+  // and so how many of its own equal rows it takes, and where its output starts.
+  int n_gt = 0, n_eq = 0;
+#pragma unroll UNROLL_J
+  for (int j = 0; j < J; ++j) {
+    const int i = base + 64 * j;
+    const uint32_t key = key_at(j);
+    const bool forced = i >= nfree && i < n;
+    const bool free_row = i < nfree;
+    n_gt += __popcll(__ballot(forced || (free_row && key > T)));
+    n_eq += __popcll(__ballot(free_row && key == T));
   }
-  int out = block_exclusive_scan(n_sel, scan_sh, &tot);
-  {
-    int r = eq_rank;
-    for (int j = 0, i = lo; i < hi; ++j, ++i) {
-      bool take;
-      if (i >= nfree) take = true;
-      else {
-        const uint32_t key = key_at(j, i);
-        take = key > T || (key == T && r < need_eq);
-        r += (key == T);
-      }
-      if (take && out < k) idx[out++] = i;   // exactly k are taken; the bound only guards memory
-    }
+  if (lane == 0) { cnt_sh[0][w] = n_gt; cnt_sh[1][w] = n_eq; }
+  __syncthreads();
+  int eq_before = 0, out = 0;
+  for (int q = 0; q < w; ++q) {
+    const int e = cnt_sh[1][q];
+    out += cnt_sh[0][q] + min(max(need_eq - eq_before, 0), e);
+    eq_before += e;
+  }
+#pragma unroll UNROLL_J
+  for (int j = 0; j < J; ++j) {
+    const int i = base + 64 * j;
+    const uint32_t key = key_at(j);
+    const bool free_row = i < nfree;
+    const bool eq = free_row && key == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = (i >= nfree && i < n) || (free_row && key > T) ||
+                      (eq && eq_before + lanes_below(eqm) < need_eq);
+    const uint64_t tm = __ballot(take);
+    const int pos = out + lanes_below(tm);
+    if (take && pos < k) idx[pos] = i;     // exactly k are taken; the bound only guards memory
+    out += __popcll(tm);
+    eq_before += __popcll(eqm);
   }
 }
 

@@ -139,9 +139,9 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
         trace.update(S_pre=S, K_pre=K, V_pre=V)
     # a14: MSDP boundary -- prune, then compact every per-candidate tensor
     if prune_to is not None and prune_to < n:
-        with tm("msdp_stage", 4.0 * n + 2.0 * prune_to * (4 + 2 * d * 2)):
+        with tm("msdp_stage", 4.0 * n + 4.0 * prune_to + 2.0 * prune_to * (4 + 2 * d)):
             keep, pos, x = capi.spts_msdp_stage(S, prune_to, P, pos, x)
-        with tm("msdp_compact", 2.0 * prune_to * (2 * Hkv * dh * 2 + 4 + (2 * d if cfg.prenorm else 0)) * 2):
+        with tm("msdp_compact", 2.0 * prune_to * (2 * Hkv * dh * 2 + 4 + (2 * d if cfg.prenorm else 0))):
             xt = capi.spts_gather(xt, keep) if cfg.prenorm else x
             K = capi.spts_gather(K, keep)
             V = capi.spts_gather(V, keep)
