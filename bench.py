@@ -33,14 +33,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-MFMA_CALLS = {"k_proj", "v_proj", "probe_q_proj", "q_proj", "reduced_attention", "o_proj_add",
+MFMA_CALLS = {"kv_proj", "k_proj", "v_proj", "probe_q_proj", "q_proj", "reduced_attention", "o_proj_add",
               "ffn_gate_up", "ffn_down_add", "ltp_probe", "pap_probe", "o_proj", "reduced_ffn"}
-SINGLE_KERNEL_CALLS = {"k_proj", "v_proj", "probe_q_proj", "q_proj", "reduced_attention", "o_proj_add",
+SINGLE_KERNEL_CALLS = {"kv_proj", "k_proj", "v_proj", "probe_q_proj", "q_proj", "reduced_attention", "o_proj_add",
                        "ffn_gate_up", "ffn_down_add"}
 KERNEL_OF_CALL = {"reduced_attention": "attn_bf16_kernel", "ffn_gate_up": "gemm_tn_kernel<EPI_SWIGLU,gather>",
                   "ffn_down_add": "gemm_tn_kernel<EPI_STORE,scatter>", "q_proj": "gemm_tn_kernel<EPI_ROPE/STORE,gather>",
                   "o_proj_add": "gemm_tn_kernel<EPI_STORE,scatter>", "k_proj": "gemm_tn_kernel",
-                  "v_proj": "gemm_tn_kernel"}
+                  "v_proj": "gemm_tn_kernel", "kv_proj": "gemm_tn_kernel<EPI_KV>"}
 
 
 def parse():

@@ -26,7 +26,8 @@ EXPORTS = [
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
     "spts_probe_attention", "spts_score_topk", "spts_gather", "spts_scatter",
     "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
-    "spts_linear", "spts_linear_rope", "spts_linear_swiglu", "spts_rope_table", "spts_rmsnorm",
+    "spts_linear", "spts_linear_rope", "spts_linear_kv", "spts_linear_swiglu", "spts_rope_table",
+    "spts_rmsnorm",
 ]
 
 _c = ctypes
@@ -55,6 +56,7 @@ _SIGS = {
     "spts_msdp_stage": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I]),
     "spts_linear": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P, _I]),
     "spts_linear_rope": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _P, _P]),
+    "spts_linear_kv": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P]),
     "spts_linear_swiglu": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _P]),
     "spts_rope_table": (_I, [_P, _I, _I, _D, _P]),
     "spts_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P]),
@@ -305,6 +307,23 @@ def spts_linear_rope(a, w, pos, table, a_rows=None, out=None):
                                        _ptr(w, bf, "w"), n, _ptr(out, bf, "out"), _ptr(pos, torch.int32, "pos"),
                                        _ptr(table, torch.float32, "table")), "spts_linear_rope")
     return out
+
+
+def spts_linear_kv(a, wk, wv, pos=None, table=None, a_rows=None):
+    """K = RoPE(A Wk^T) (plain if table is None) and V = A Wv^T in one launch."""
+    kdim = a.shape[1]
+    nk, nv = wk.shape[0], wv.shape[0]
+    m = a_rows.shape[0] if a_rows is not None else a.shape[0]
+    k_out = torch.empty((m, nk), dtype=torch.bfloat16, device=a.device)
+    v_out = torch.empty((m, nv), dtype=torch.bfloat16, device=a.device)
+    ctx = context()
+    h = ctx.bind(0, a.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_linear_kv(h, _ptr(a, bf, "a"), _ptr(a_rows, torch.int32, "a_rows"), m, kdim,
+                                     _ptr(wk, bf, "wk"), nk, _ptr(wv, bf, "wv"), nv, _ptr(k_out, bf, "k_out"),
+                                     _ptr(v_out, bf, "v_out"), _ptr(pos, torch.int32, "pos"),
+                                     _ptr(table, torch.float32, "table")), "spts_linear_kv")
+    return k_out, v_out
 
 
 def spts_linear_swiglu(a, w_gate, w_up, a_rows=None, out=None):

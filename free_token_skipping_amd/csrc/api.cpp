@@ -312,6 +312,30 @@ spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows
   return hip_status(ctx, launch_gemm(g, EPI_ROPE, ctx->stream), "linear_rope");
 }
 
+spts_status spts_linear_kv(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
+                           const void* wk, int nk, const void* wv, int nv, void* k_out, void* v_out,
+                           const int32_t* pos, const float* table) {
+  CHECK_CTX();
+  REQUIRE(nk > 0 && nv > 0, SPTS_ERR_SHAPE, "bad K/V widths nk=%d nv=%d", nk, nv);
+  spts_status st = gemm_shape_ok(ctx, m, kdim, nk);
+  if (st != SPTS_OK) return st;
+  st = gemm_shape_ok(ctx, m, kdim, nv);
+  if (st != SPTS_OK) return st;
+  REQUIRE((pos == nullptr) == (table == nullptr), SPTS_ERR_INVALID, "pos and table go together");
+  if (m == 0) return SPTS_OK;
+  REQUIRE_PTR(a); REQUIRE_PTR(wk); REQUIRE_PTR(wv); REQUIRE_PTR(k_out); REQUIRE_PTR(v_out);
+  REQUIRE_ALIGN(a); REQUIRE_ALIGN(wk); REQUIRE_ALIGN(wv); REQUIRE_ALIGN(k_out); REQUIRE_ALIGN(v_out);
+  if (a_rows) REQUIRE_ALIGN(a_rows);
+  if (table) REQUIRE_ALIGN(table);
+  GemmArgs g{};
+  g.a = reinterpret_cast<const uint16_t*>(a); g.a_rows = a_rows; g.m = m; g.k = kdim; g.lda = kdim;
+  g.b0 = reinterpret_cast<const uint16_t*>(wk); g.b1 = reinterpret_cast<const uint16_t*>(wv);
+  g.ldb = kdim; g.n = nk + nv; g.n0 = nk;
+  g.out = k_out; g.ldc = nk; g.out2 = v_out; g.ldc2 = nv;
+  g.pos = pos; g.rope_table = table;
+  return hip_status(ctx, launch_gemm(g, EPI_KV, ctx->stream), "linear_kv");
+}
+
 spts_status spts_linear_swiglu(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
                                const void* w_gate, const void* w_up, int f, void* h_out) {
   CHECK_CTX();

@@ -69,6 +69,9 @@ void gemm_tn_kernel(GemmArgs g) {
   const int tile_m = first_m + (logical % in_group) % gm;
   const int tile_n = (logical % in_group) / gm;
 
+  // KV: tiles at or past column n0 read b1 and write out2
+  const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
+
   // ---- direct global -> LDS staging.  Wave `wave`, instruction i writes the
   // 1 KiB block of tile rows rb*8 .. rb*8+7, rb = 8*i + wave; lane L lands at
   // row r = rb*8 + L/8, physical chunk L%8, so it fetches the logical chunk
@@ -92,11 +95,12 @@ void gemm_tn_kernel(GemmArgs g) {
       if (within >= 64) b_from_up |= 1u << i;
       b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
     } else {
-      b_off[i] = (((uint32_t)tile_n * BN + r) * (uint32_t)g.ldb + ld_ch * 8) * 2u;
+      const uint32_t brow = (uint32_t)(tile_n * BN - (part1 ? g.n0 : 0)) + r;
+      b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
     }
   }
   const char* abase = reinterpret_cast<const char*>(g.a);
-  const char* b0base = reinterpret_cast<const char*>(g.b0);
+  const char* b0base = reinterpret_cast<const char*>(part1 ? g.b1 : g.b0);
   const char* b1base = reinterpret_cast<const char*>(g.b1);
   const int KT = g.k / BK / ksplit;                    // k-steps of this slice
   const int kt_base = kslice * KT;
@@ -257,7 +261,7 @@ void gemm_tn_kernel(GemmArgs g) {
         }
       continue;
     }
-    if (EPI == EPI_ROPE) {
+    if (EPI == EPI_ROPE || (EPI == EPI_KV && !part1 && g.rope_table)) {
       const int arow = GATHER ? g.a_rows[row] : row;
       const float* tab = g.rope_table + (long)g.pos[arow] * 128;   // 64 (cos, sin) pairs
 #pragma unroll
@@ -271,14 +275,16 @@ void gemm_tn_kernel(GemmArgs g) {
           acc[i][j + 2][r] = x2 * cs + x1 * sn;
         }
     }
-    // EPI_STORE / EPI_ROPE
+    // EPI_STORE / EPI_ROPE / EPI_KV
     const int orow = g.out_rows ? g.out_rows[row] : row;
-    uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)orow * g.ldc;
+    uint16_t* out = part1 ? reinterpret_cast<uint16_t*>(g.out2) + (long)orow * g.ldc2
+                          : reinterpret_cast<uint16_t*>(g.out) + (long)orow * g.ldc;
+    const int cshift = part1 ? g.n0 : 0;                  // KV: b1 columns restart at 0
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4;
+        const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4 - cshift;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
@@ -428,6 +434,7 @@ hipError_t launch_gemm(const GemmArgs& g0, int epi, hipStream_t s) {
     case EPI_STORE: return gather ? launch_one<EPI_STORE, true>(g, s) : launch_one<EPI_STORE, false>(g, s);
     case EPI_ROPE: return gather ? launch_one<EPI_ROPE, true>(g, s) : launch_one<EPI_ROPE, false>(g, s);
     case EPI_SWIGLU: return gather ? launch_one<EPI_SWIGLU, true>(g, s) : launch_one<EPI_SWIGLU, false>(g, s);
+    case EPI_KV: return gather ? launch_one<EPI_KV, true>(g, s) : launch_one<EPI_KV, false>(g, s);
     case EPI_SPLIT: return launch_one<EPI_SPLIT, false>(g, s);
     case EPI_SUMSQ: return launch_one<EPI_SUMSQ, false>(g, s);
     default: return hipErrorInvalidValue;

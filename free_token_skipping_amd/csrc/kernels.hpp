@@ -17,6 +17,8 @@ enum GemmEpilogue : int {
   EPI_SPLIT = 3,   // fp32 result t written as bf16 pair hi=bf16(t), lo=bf16(t-hi)
   EPI_SUMSQ = 4,   // fp32 out[i, tile_n] = sum over the tile's 256 columns of c^2
   EPI_PARTIAL = 5, // split-K pass: fp32 partial[ks][i][c] (internal)
+  EPI_KV = 6,      // two-part B: columns < n0 from b0 into out (RoPE if rope_table),
+                   // the rest from b1 into out2 (ldc2 columns), both bf16
 };
 
 struct GemmArgs {
@@ -34,6 +36,9 @@ struct GemmArgs {
   int accumulate;
   const int32_t* pos;       // ROPE: original position per A row (indexed like A rows)
   const float* rope_table;  // ROPE: [max_pos, 64, 2]
+  int n0;                   // KV: columns taken from b0 (a multiple of 256)
+  void* out2;               // KV: output of the b1 columns
+  int ldc2;
   float* partial;           // split-K workspace (nullable: never split)
   size_t partial_bytes;
   int ksplit;               // set by the launcher

@@ -119,14 +119,20 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
     else:
         xt = x
     # a1: K, V over all current candidates (+ RoPE on K)
-    if k_given is None:
-        with tm("k_proj", 2.0 * n * d * Hkv * dh):
-            K = (capi.spts_linear_rope(xt, w["wk"], pos, rope_table) if rope else capi.spts_linear(xt, w["wk"]))
-        K = K.view(n, Hkv, dh)
+    if k_given is None and fused:
+        with tm("kv_proj", 4.0 * n * d * Hkv * dh):
+            K, V = capi.spts_linear_kv(xt, w["wk"], w["wv"], pos if rope else None, rope_table if rope else None)
+        K, V = K.view(n, Hkv, dh), V.view(n, Hkv, dh)
     else:
-        K = k_given
-    with tm("v_proj", 2.0 * n * d * Hkv * dh):
-        V = capi.spts_linear(xt, w["wv"]).view(n, Hkv, dh)
+        if k_given is None:
+            with tm("k_proj", 2.0 * n * d * Hkv * dh):
+                K = (capi.spts_linear_rope(xt, w["wk"], pos, rope_table) if rope
+                     else capi.spts_linear(xt, w["wk"]))
+            K = K.view(n, Hkv, dh)
+        else:
+            K = k_given
+        with tm("v_proj", 2.0 * n * d * Hkv * dh):
+            V = capi.spts_linear(xt, w["wv"]).view(n, Hkv, dh)
     # a2: probe queries (last P rows)
     xp = xt[n - P:]
     with tm("probe_q_proj", 2.0 * P * d * Hq * dh):

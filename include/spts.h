@@ -206,6 +206,19 @@ spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows
                              int kdim, const void* w, int n, void* out, const int32_t* pos,
                              const float* table);
 
+/* Keys and values of the same rows in one launch -- every current candidate
+ * keeps its K and V for the reduced attention ([SPTS] Fig. 2(a)):
+ *     k_out[i, :] = bf16(RoPE(A Wk^T))[i]   (no rotation if table == NULL)
+ *     v_out[i, :] = bf16(A Wv^T)[i],         A row i = a[a_rows ? a_rows[i] : i]
+ *   a [*, kdim] bf16; wk [nk, kdim], wv [nv, kdim] bf16; k_out [m, nk],
+ *   v_out [m, nv] bf16.  RoPE as in spts_linear_rope (pos, table required
+ *   together).  Results equal spts_linear_rope / spts_linear on the same
+ *   inputs; one launch fills the GPU better than two thin ones.
+ * Requires kdim % 64 == 0, nk % 256 == 0, nv % 256 == 0. */
+spts_status spts_linear_kv(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
+                           const void* wk, int nk, const void* wv, int nv, void* k_out,
+                           void* v_out, const int32_t* pos, const float* table);
+
 /* The first half of the reduced FFN as its own call:
  *     h_out[i, :] = bf16(silu(A Wg^T) * (A Wu^T))[i],  A row i = a[a_rows ? a_rows[i] : i]
  *   a [*, kdim] bf16, w_gate, w_up [f, kdim] bf16, h_out [m, f] bf16.

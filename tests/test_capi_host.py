@@ -98,6 +98,13 @@ def test_gemm_family_validation(L, ctx):
     assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 10, 4096, 14336, FAKE, None, 0) == NOMEM
     assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 0, 4096, 14336, FAKE, None, 0) == OK
     assert L.spts_rmsnorm(ctx, FAKE, 10, 12, 1e-5, FAKE) == SHAPE
+    kv = L.spts_linear_kv
+    assert kv(ctx, FAKE, None, 100, 128, FAKE, 1024, FAKE, 200, FAKE, FAKE, None, None) == UNSUPPORTED  # nv % 256
+    assert kv(ctx, FAKE, None, 100, 96, FAKE, 1024, FAKE, 1024, FAKE, FAKE, None, None) == UNSUPPORTED   # k % 64
+    assert kv(ctx, FAKE, None, 100, 128, FAKE, 0, FAKE, 1024, FAKE, FAKE, None, None) == SHAPE
+    assert kv(ctx, FAKE, None, 100, 128, FAKE, 1024, FAKE, 1024, FAKE, FAKE, FAKE, None) == INVALID       # pos w/o table
+    assert kv(ctx, FAKE, None, 100, 128, FAKE, 1024, FAKE, 1024, None, FAKE, None, None) == INVALID
+    assert kv(ctx, FAKE, None, 0, 128, FAKE, 1024, FAKE, 1024, FAKE, FAKE, None, None) == OK             # empty: no-op
 
 
 def test_attention_and_rows_validation(L, ctx):

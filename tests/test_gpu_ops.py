@@ -239,6 +239,30 @@ def test_linear_rope():
     assert_close(np64(out2), ref[rows.long().numpy()], BF16_REL, "gathered linear rope")
 
 
+@pytest.mark.parametrize("rope", [True, False])
+def test_linear_kv(rope):
+    _log(f"linear kv rope={rope}")
+    m, kd, nk, nv, theta = 600, 256, 512, 256, 500000.0
+    a = W.randn((m, kd), seed=70)
+    wk = W.randn((nk, kd), seed=71, std=0.05)
+    wv = W.randn((nv, kd), seed=72, std=0.05)
+    pos = torch.from_numpy(np.sort(np.random.default_rng(7).choice(131072, m, replace=False)).astype(np.int32))
+    table = capi.spts_rope_table(131072, 128, theta, DEV) if rope else None
+    k_out, v_out = capi.spts_linear_kv(_cuda(a), _cuda(wk), _cuda(wv), _cuda(pos) if rope else None, table)
+    kacc = numerics.f32(W.as_f64(a) @ W.as_f64(wk).T)
+    kref = numerics.bf16(normrope.rope(kacc.reshape(m, nk // 128, 128), pos.numpy(), theta).reshape(m, nk)
+                         if rope else kacc)
+    vref = numerics.bf16(W.as_f64(a) @ W.as_f64(wv).T)
+    assert_close(np64(k_out), kref, BF16_REL, "kv: K")
+    assert_close(np64(v_out), vref, BF16_REL, "kv: V")
+    rows = W.sorted_rows(m, 300, 4, seed=73)
+    k2, v2 = capi.spts_linear_kv(_cuda(a), _cuda(wk), _cuda(wv), _cuda(pos) if rope else None, table,
+                                 a_rows=_cuda(rows))
+    r = rows.long().numpy()
+    assert_close(np64(k2), kref[r], BF16_REL, "kv gathered: K")
+    assert_close(np64(v2), vref[r], BF16_REL, "kv gathered: V")
+
+
 def test_linear_full_size_sampled():
     m, kd, n = 11469, 4096, 4096
     _log("linear full size (sampled rows)")
