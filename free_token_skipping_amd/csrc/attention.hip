@@ -14,6 +14,8 @@
 // V tile.
 #include <type_traits>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -84,11 +86,13 @@ __device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* ks, uint
 // query heads); block 512 = 8 waves: wave w serves query head 4*hg + (w & 3)
 // for the 32 queries q0 + 32*(w >> 2) .. +31 (two waves per SIMD).
 //
-// Software pipeline inside each wave: while the VALU turns the logits of
-// tile t into bf16 probabilities, the MFMA unit already forms the logits of
-// tile t+1 (K runs one tile ahead of V in the double-buffered LDS); then
-// O += V_t P_t.  Masking of tile t+1 and the reference-max update happen
-// after that, so the MFMA/VALU-overlapped region is one basic block.
+// Software pipeline inside each wave, one 64-key tile per step: while the
+// VALU turns the logits of tile t into bf16 probabilities, the MFMA unit forms
+// the logits of tile t+1 and accumulates O += V_{t-1} P_{t-1} (the P of the
+// previous step).  The three streams share no data, so they interleave one
+// MFMA at a time; the exp2 stream hides almost entirely behind the matrix
+// core.  Masking of tile t+1 and the reference-max update follow in the same
+// step, after the overlapped block.
 //
 // The reference max is updated lazily: only when a lane's logits exceed it
 // by more than 2^8 (exp2 units), so the O rescale is rare; p = exp2(s*scale*
@@ -196,9 +200,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
         sd[kt] = mfma32x32x16(kf, qf[kk], kk == 0 ? zero16 : sd[kt]);
       }
   };
-  // mask tile t's keys beyond each query, then move the reference max if needed;
-  // key of reg r = t*64 + kt*32 + (r>>3)*16 + half*8 + (r&7)
-  auto prepare = [&](int t, f32x16 (&sd)[2]) {
+  // mask tile t's keys beyond each query, then move the reference max if
+  // needed; key of reg r = t*64 + kt*32 + (r>>3)*16 + half*8 + (r&7).  `pend`
+  // is the P of the previous tile, already formed against the old reference
+  // but not yet multiplied into O: a move rescales it together with O and l.
+  auto prepare = [&](int t, f32x16 (&sd)[2], bf16x8 (&pend)[4]) {
     if (t >= nfull) {
       const int j0 = t * KT;
 #pragma unroll
@@ -223,17 +229,17 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f32x8 pv = __builtin_convertvector(pend[c], f32x8);
+        pv *= alpha;
+        pend[c] = __builtin_convertvector(pv, bf16x8);
+      }
       m_ref = m_new;
     }
   };
-
-  // one pipeline step: tile t's logits are in sc (masked, reference max set)
-  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    if (t + 2 < ntiles) load_k((t + 2) * KT);
-    if (t + 1 < ntiles) load_v((t + 1) * KT);
-    // MFMA: logits of tile t+1 (stale data past the last tile; unused)  ||  VALU: P_t
-    logits((t + 1) & 1, sn);
-    bf16x8 pf[4];
+  // P_t = exp2(logit * scale * log2e - m_ref) as bf16 MFMA operands; l += P_t
+  auto softmax = [&](f32x16 (&sc)[2], bf16x8 (&pc)[4]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -244,61 +250,100 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
           pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][sub * 8 + e], sl2, -m_ref));
           l_part += pv[e];
         }
-        pf[kt * 2 + sub] = __builtin_convertvector(pv, bf16x8);
+        pc[kt * 2 + sub] = __builtin_convertvector(pv, bf16x8);
       }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);          // first K fragments
-#pragma unroll
-    for (int r = 0; r < 12; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one logit MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // next K fragment
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);        // softmax VALU
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-    // O^T += V_t^T P_t^T
-    const uint16_t* vs = Vs[t & 1] + vfrag;
+  };
+  // O^T += V_u^T P_u^T, V_u in buffer vb
+  auto pv_mma = [&](int vb, bf16x8 (&pp)[4]) {
+    const uint16_t* vs = Vs[vb] + vfrag;
 #pragma unroll
     for (int ks4 = 0; ks4 < 4; ++ks4)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + d * 32 * VROW + ks4 * 16);
-        oacc[d] = mfma32x32x16(vf, pf[ks4], oacc[d]);
+        oacc[d] = mfma32x32x16(vf, pp[ks4], oacc[d]);
       }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  };
+
+  // One pipeline step t.  sc holds tile t's logits (masked, reference max
+  // set), pp the P of tile t-1.  The matrix core forms the logits of tile t+1
+  // and O += P_{t-1} V_{t-1} while the VALU turns tile t's logits into P_t, so
+  // all three streams are independent and interleave one MFMA at a time.  V
+  // trails K by two tiles: V_t is staged during step t (into buffer t & 1)
+  // and read at step t+1, K_{t+2} is staged during step t.
+  auto step = [&](auto with_pv, int t, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pp)[4],
+                  bf16x8 (&pc)[4]) {
+    constexpr bool kPV = decltype(with_pv)::value;
+    // K/V staging is unconditional (rows clamp to n-1; past the last tile the
+    // K store lands in buffer t & 1, whose tile was read in step t-1), so no
+    // branch splits the MFMA / VALU block
+    load_k((t + 2) * KT);
+    load_v(t * KT);
+    logits((t + 1) & 1, sn);             // stale data past the last tile; unused
+    if constexpr (kPV) pv_mma((t - 1) & 1, pp);
+    softmax(sc, pc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);          // first K fragments
+    if constexpr (kPV) {
 #pragma unroll
-    for (int r = 0; r < 12; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int r = 0; r < 28; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next K / V fragment
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);      // softmax VALU + exp
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 12; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    if (t + 2 < ntiles) store_k(t & 1);
-    if (t + 1 < ntiles) store_v((t + 1) & 1);
-    if (t + 1 < ntiles) prepare(t + 1, sn);
+    // P_t is only read in the next step; without this anchor the compiler
+    // sinks the softmax below the masking of tile t+1, away from the MFMAs
+    asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(pc[2]), "+v"(pc[3]), "+v"(l_part));
+    store_k(t & 1);
+    store_v(t & 1);
+    if (t + 1 < ntiles) prepare(t + 1, sn, pc);
     __syncthreads();
   };
 
-  // prologue: K_0, V_0, K_1 staged; logits of tile 0
+  // prologue: K_0, K_1 staged; logits of tile 0
   load_k(0);
-  load_v(0);
   store_k(0);
-  store_v(0);
   if (ntiles > 1) {
     load_k(KT);
     store_k(1);
   }
   __syncthreads();
   f32x16 sa[2], sb[2];
-  logits(0, sa);
-  prepare(0, sa);
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+  bf16x8 pa[4], pb[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    pa[c] = bf16x8{};
+    pb[c] = bf16x8{};
   }
-  if (t < ntiles) step(t, sa, sb);
+  logits(0, sa);
+  prepare(0, sa, pb);                     // nothing pending yet (pb is zero)
+  step(std::false_type{}, 0, sa, sb, pb, pa);
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    step(std::true_type{}, t, sb, sa, pa, pb);
+    step(std::true_type{}, t + 1, sa, sb, pb, pa);
+  }
+  if (t < ntiles) step(std::true_type{}, t, sb, sa, pa, pb);
+  // the last tile's P: step t leaves P_t in pb for odd t, in pa for even t
+  if ((ntiles - 1) & 1) pv_mma((ntiles - 1) & 1, pb);
+  else pv_mma((ntiles - 1) & 1, pa);
 
   // normalise and store: lane = query, reg r of dh tile d -> dh d*32 + (r>>2)*8 + half*4 + (r&3)
   if (qi_raw < kq) {
