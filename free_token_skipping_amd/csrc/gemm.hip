@@ -9,8 +9,9 @@
 // wave owns a 64 x 128 block = 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (128
 // fp32 accumulators per lane), two waves per SIMD.  Operands go straight from
 // global memory into double-buffered LDS (2 x 64 KiB), one barrier per
-// k-step; while one wave of a SIMD waits on its loads or the barrier, the
-// other keeps the matrix core busy.
+// k-step.  Only waves 0-3 (one per SIMD) issue the global->LDS loads: a wave
+// stalled on issuing them cannot issue MFMAs, so each SIMD keeps one wave
+// that only computes.
 //
 // The MFMA is issued as (B fragment, A fragment) so each lane's accumulators
 // hold ONE row of C and 4 groups of 4 consecutive columns; every epilogue
@@ -44,7 +45,7 @@ void gemm_tn_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS addresses in SGPRs
   const int wm = wave >> 1, wn = wave & 1;          // 4 x 2 waves
   const int l32 = lane & 31, half = lane >> 5;
 
@@ -72,16 +73,19 @@ void gemm_tn_kernel(GemmArgs g) {
   // KV: tiles at or past column n0 read b1 and write out2
   const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
 
-  // ---- direct global -> LDS staging.  Wave `wave`, instruction i writes the
-  // 1 KiB block of tile rows rb*8 .. rb*8+7, rb = 8*i + wave; lane L lands at
-  // row r = rb*8 + L/8, physical chunk L%8, so it fetches the logical chunk
-  // (L%8) ^ ((r >> 1) & 7) -- the swizzle of swz() applied on the global side.
+  // ---- direct global -> LDS staging by waves 0-3.  Loading wave w,
+  // instruction i writes the 1 KiB block of tile rows rb*8 .. rb*8+7,
+  // rb = 4*i + w; lane L lands at row r = rb*8 + L/8, physical chunk L%8, so
+  // it fetches the logical chunk (L%8) ^ ((r >> 1) & 7) -- the swizzle of
+  // swz() applied on the global side.
+  const bool loader = wave < 4;
+  const int lw = wave & 3;
   const int ld_sub = lane >> 3;                       // row within the 8-row block
-  uint32_t a_off[4], b_off[4];                        // byte offsets of the staged rows
+  uint32_t a_off[8], b_off[8];                        // byte offsets of the staged rows
   unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rb = 8 * i + wave;
+  for (int i = 0; i < 8; ++i) {
+    const int rb = 4 * i + lw;
     const int r = rb * 8 + ld_sub;                    // row within the 256-row tile
     const int ld_ch = (lane & 7) ^ ((r >> 1) & 7);    // logical 16-byte chunk fetched
     int ar = tile_m * BM + r;
@@ -106,14 +110,15 @@ void gemm_tn_kernel(GemmArgs g) {
   const int kt_base = kslice * KT;
 
   auto issue = [&](int kt_local, int stage) {
+    if (!loader) return;
     const int kt = kt_base + kt_local;
     const uint32_t ka = (uint32_t)kt * BK * 2u;
     const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
     uint16_t* a_s = As + stage * TILE_ELEMS;
     uint16_t* b_s = Bs + stage * TILE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rb = 8 * i + wave;
+    for (int i = 0; i < 8; ++i) {
+      const int rb = 4 * i + lw;
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(abase + a_off[i] + ka),
           (__attribute__((address_space(3))) void*)(a_s + rb * 512), 16, 0, 0);
