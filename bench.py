@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--workload", default="msdp_stack_32k", choices=["msdp_stack_32k", "layer_32k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single-layer", action="store_true")
+    ap.add_argument("--no-ttft", action="store_true", help="skip the 32-layer prefill schedule vs dense table")
     ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
     ap.add_argument("--cpu-sample", type=float, default=1.0 / 32,
                     help="fraction of row-separable oracle work timed for the CPU baseline")
@@ -151,6 +152,51 @@ def roofline(summary, steps):
             "kernel": KERNEL_OF_CALL.get(name, name), "call": name,
             "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_ms, 4),
             "launches_per_step": calls // steps}
+
+
+# ------------------------------------------------- 32-layer prefill schedule
+
+# The LLaMA-3.1-8B schedule of [SPTS] Table B: 32 layers, layers 0-9 dense,
+# stages ending at layers 13/18/23/28 with 9K/7K/4K/2K candidates, 1K after
+# the last stage (K = 1024 tokens).
+LLAMA_SCHEDULE = dict(n_layers=32, first_skip_layer=10, stage_ends=(13, 18, 23, 28),
+                      budgets=(9216, 7168, 4096, 2048), final_budget=1024)
+
+
+def ttft_table(x0, layers, cfg, reps=2):
+    """Prefill time of the 32-layer schedule against the same 32 layers run
+    dense, at 8K-32K tokens: a speed-only analogue of [SPTS] Table 4 (TTFT
+    ratio vs the full model).  Both sides use this library's kernels; the
+    32 layers cycle through the generated layers' weights (the work does not
+    depend on the weight values)."""
+    import torch
+    from free_token_skipping_amd import pipeline
+    sch = LLAMA_SCHEDULE
+    pts = pipeline.prune_points(sch["first_skip_layer"], sch["stage_ends"], sch["budgets"], sch["final_budget"])
+    rows = []
+    for n in (8192, 16384, 24576, 32768):
+        xs = x0[:n]
+        ms = {}
+        for mode in ("dense", "spts"):
+            def run():
+                pipeline.prefill_schedule(xs, layers, cfg, sch["n_layers"], sch["first_skip_layer"], pts,
+                                          dense=(mode == "dense"))
+            run()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms[mode] = e0.elapsed_time(e1) / reps
+        rows.append({"tokens": n, "dense_ms": round(ms["dense"], 2), "spts_ms": round(ms["spts"], 2),
+                     "ttft_ratio": round(ms["dense"] / ms["spts"], 3)})
+        log(f"prefill {n}: dense {ms['dense']:.1f} ms, SPTS {ms['spts']:.1f} ms, ratio {ms['dense'] / ms['spts']:.2f}x")
+    return {"schedule": "32 layers, dense 0-9, stage ends 13/18/23/28, candidates 9216/7168/4096/2048, "
+                        "1024 after; keep 0.35 per skipping layer",
+            "weights": f"{len(layers)} generated layers cycled", "reps": reps, "rows": rows}
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -324,6 +370,9 @@ def main():
             rec.setdefault("also", {})[name] = {"tokens_per_s_per_layer": round(r["tokens_per_s_per_layer"], 1),
                                                 "ms_per_step": round(r["ms_per_step"], 4),
                                                 "roofline": r["roofline"], "breakdown": r["breakdown"]}
+    if not args.no_ttft:
+        log("timing the 32-layer prefill schedule against dense")
+        rec.setdefault("also", {})["prefill_32_layers"] = ttft_table(x0, layers, stack_cfg)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(sh, st, n_layers, points, args.cpu_sample)

@@ -243,6 +243,65 @@ def prune_points(first_skip_layer, stage_end_layers, budgets, final_budget=None)
     return pts
 
 
+def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER):
+    """The same decoder layer with every row computed: no probes, no
+    selection.  This is the dense-prefill baseline that SPTS is compared
+    against ([SPTS] Table 4 compares TTFT against the full model).  x [n, d]
+    bf16 is updated in place; every row is a query, so the attention call is
+    plain causal attention."""
+    n, d = x.shape
+    Hq, Hkv, dh = cfg.Hq, cfg.Hkv, cfg.dh
+    rope = cfg.theta is not None
+    if cfg.prenorm:
+        with tm("rmsnorm", 4.0 * n * d):
+            xt = capi.spts_rmsnorm(x, cfg.eps)
+    else:
+        xt = x
+    with tm("kv_proj", 4.0 * n * d * Hkv * dh):
+        K, V = capi.spts_linear_kv(xt, w["wk"], w["wv"], pos if rope else None, rope_table if rope else None)
+    with tm("q_proj", 2.0 * n * d * Hq * dh):
+        Q = (capi.spts_linear_rope(xt, w["wq"], pos, rope_table) if rope else capi.spts_linear(xt, w["wq"]))
+    idx = torch.arange(n, dtype=torch.int32, device=x.device)
+    with tm("attention", _attn_flops(idx, Hq, dh)):
+        O = capi.spts_reduced_attention(Q.view(n, Hq, dh), idx, K.view(n, Hkv, dh), V.view(n, Hkv, dh))
+    with tm("o_proj_add", 2.0 * n * Hq * dh * d):
+        capi.spts_linear(O.view(n, Hq * dh), w["wo"], out=x, accumulate=True)
+    if cfg.keep_ffn is not None:
+        f = w["wg"].shape[0]
+        if cfg.prenorm:
+            with tm("rmsnorm", 4.0 * n * d):
+                z = capi.spts_rmsnorm(x, cfg.eps)
+        else:
+            z = x
+        with tm("ffn_gate_up", 4.0 * n * d * f):
+            H = capi.spts_linear_swiglu(z, w["wg"], w["wu"])
+        with tm("ffn_down_add", 2.0 * n * d * f):
+            capi.spts_linear(H, w["wd"], out=x, accumulate=True)
+    return x
+
+
+def prefill_schedule(x0, layers, cfg: LayerConfig, n_layers, first_skip_layer, points, dense=False,
+                     tm=NO_TIMER):
+    """Prefill of an n_layers model: layers before first_skip_layer are dense,
+    the rest are SPTS layers pruned at `points` ([SPTS] Table B gives such a
+    schedule per model).  dense=True runs every layer dense (the full-model
+    baseline).  Layer li uses weights layers[li % len(layers)].  Returns the
+    residual over the final candidates and their original positions."""
+    N = x0.shape[0]
+    x = x0.clone()
+    pos = torch.arange(N, dtype=torch.int32, device=x0.device)
+    table = capi.spts_rope_table(N, cfg.dh, cfg.theta, x0.device) if cfg.theta is not None else None
+    for li in range(n_layers):
+        w = layers[li % len(layers)]
+        if dense or li < first_skip_layer:
+            x = dense_layer(x, pos, w, cfg, table, tm=tm)
+        else:
+            budget = points.get(li)
+            prune = budget if budget is not None and budget < x.shape[0] else None
+            x, pos = spts_layer(x, pos, w, cfg, table, prune_to=prune, tm=tm)
+    return x, pos
+
+
 def msdp_stack(x0, layers, cfg: LayerConfig, points, fused=True, traces=None, tm=NO_TIMER):
     """Run the stack on embeddings x0 [N, d] (not modified).  Returns the
     residual over the final candidates and their original positions."""

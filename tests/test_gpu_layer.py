@@ -225,3 +225,34 @@ def test_msdp_stack_small():
     err = np.abs(np64(x)[ig] - ref[io]) / np.abs(ref[io]).max(axis=1, keepdims=True)
     assert np.median(err.max(axis=1)) <= BF16_REL
 
+
+
+def test_dense_layers_and_schedule_small():
+    """Dense prefill layers (every row computed) against the oracle's layer
+    with every row kept, and the structure of a prefill schedule that runs
+    dense layers before pruned SPTS layers."""
+    sh = W.LayerShape(n=1024, d=512, Hq=8, Hkv=2, dh=128, f=1024, r=256, P=64)
+    st = W.make_stack(sh, 2, seed=3)
+    cfg = pipeline.LayerConfig(Hq=8, Hkv=2, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35, prenorm=True,
+                               eps=1e-5, theta=500000.0)
+    ws = [_gpu_w(w) for w in st["layers"]]
+    _log("dense prefill, 2 layers")
+    x, pos = pipeline.prefill_schedule(st["x"].to(DEV), ws, cfg, n_layers=2, first_skip_layer=2, points={})
+    torch.cuda.synchronize()
+    ocfg = dict(Hq=8, Hkv=2, dh=128, P=64, keep_attn=1.0, keep_ffn=1.0, prenorm=True, eps=1e-5,
+                theta=500000.0)
+    ref = W.as_f64(st["x"])
+    opos = np.arange(sh.n)
+    for w in st["layers"]:
+        ref, sa, sf = olayer.spts_layer(ref, opos, _f64_w(w), ocfg)
+        assert len(sa["idx"]) == sh.n and len(sf["idx_f"]) == sh.n     # keep-all: the dense layer
+    assert np.array_equal(pos.cpu().numpy(), opos)
+    assert_close(np64(x), ref, BF16_REL, "dense prefill (2 layers)")
+    _log("schedule: 2 dense + 4 SPTS layers, pruned at layers 2 and 4")
+    pts = {2: 700, 4: 400}
+    x2, pos2 = pipeline.prefill_schedule(st["x"].to(DEV), ws, cfg, n_layers=6, first_skip_layer=2, points=pts)
+    torch.cuda.synchronize()
+    p2 = pos2.cpu().numpy()
+    assert x2.shape == (400, sh.d) and len(p2) == 400 and np.all(np.diff(p2) > 0)
+    assert set(range(sh.n - 64, sh.n)) <= set(p2.tolist())
+    assert torch.isfinite(x2.float()).all()
