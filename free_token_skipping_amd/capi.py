@@ -24,7 +24,7 @@ EXPORTS = [
     "spts_status_name", "spts_check",
     "spts_probe_attention_workspace", "spts_score_topk_workspace", "spts_ltp_probe_workspace",
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
-    "spts_probe_attention", "spts_score_topk", "spts_gather", "spts_scatter",
+    "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_gather", "spts_scatter",
     "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
     "spts_linear", "spts_linear_rope", "spts_linear_kv", "spts_linear_swiglu", "spts_rope_table",
     "spts_rmsnorm",
@@ -48,6 +48,7 @@ _SIGS = {
     "spts_linear_workspace": (_SZ, [_I, _I, _I]),
     "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
+    "spts_score_topk_multiply": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "spts_gather": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "spts_scatter": (_I, [_P, _I, _P, _P, _I, _I, _P, _I]),
     "spts_reduced_attention": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
@@ -187,6 +188,20 @@ def spts_score_topk(s_a, k, n_forced, s_b=None, w_a=0.5, w_b=0.5, idx=None, fuse
                                       float(w_a), float(w_b), n, int(k), int(n_forced),
                                       _ptr(idx, torch.int32, "idx"), _ptr(fused_out, torch.float32, "fused_out")),
            "spts_score_topk")
+    return idx
+
+
+def spts_score_topk_multiply(s_a, s_b, k, n_forced, idx=None, fused_out=None):
+    """Top-k of the Multiply fusion fl(s_a * s_b), probes forced, ascending int32 indices."""
+    n = s_a.shape[0]
+    if idx is None:
+        idx = torch.empty(min(k, n), dtype=torch.int32, device=s_a.device)
+    ctx = context()
+    h = ctx.bind(lib().spts_score_topk_workspace(n), s_a.device)
+    _check(ctx, lib().spts_score_topk_multiply(h, _ptr(s_a, torch.float32, "s_a"), _ptr(s_b, torch.float32, "s_b"),
+                                               n, int(k), int(n_forced), _ptr(idx, torch.int32, "idx"),
+                                               _ptr(fused_out, torch.float32, "fused_out")),
+           "spts_score_topk_multiply")
     return idx
 
 

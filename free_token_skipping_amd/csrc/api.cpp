@@ -185,8 +185,25 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
           "need 0 <= n_forced <= k and n_forced <= n (n=%d k=%d n_forced=%d)", n, k, n_forced);
   const size_t need = topk_workspace(n);
   REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
-  return hip_status(ctx, launch_topk(s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, ctx->ws, ctx->stream),
+  return hip_status(ctx, launch_topk(s_a, s_b, w_a, w_b, false, n, k, n_forced, idx, fused_out, ctx->ws,
+                                     ctx->stream),
                     "score_topk");
+}
+
+spts_status spts_score_topk_multiply(spts_ctx* ctx, const float* s_a, const float* s_b, int n, int k,
+                                     int n_forced, int32_t* idx, float* fused_out) {
+  CHECK_CTX();
+  REQUIRE_PTR(s_a); REQUIRE_PTR(s_b); REQUIRE_PTR(idx);
+  REQUIRE_ALIGN(s_a); REQUIRE_ALIGN(s_b); REQUIRE_ALIGN(idx);
+  if (fused_out) REQUIRE_ALIGN(fused_out);
+  REQUIRE(n >= 1, SPTS_ERR_SHAPE, "n must be >= 1");
+  REQUIRE(n_forced >= 0 && n_forced <= k && n_forced <= n, SPTS_ERR_SHAPE,
+          "need 0 <= n_forced <= k and n_forced <= n (n=%d k=%d n_forced=%d)", n, k, n_forced);
+  const size_t need = topk_workspace(n);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  return hip_status(ctx, launch_topk(s_a, s_b, 0.f, 0.f, true, n, k, n_forced, idx, fused_out, ctx->ws,
+                                     ctx->stream),
+                    "score_topk_multiply");
 }
 
 // ------------------------------------------------------------- gather/scatter
@@ -450,7 +467,7 @@ spts_status spts_msdp_stage(spts_ctx* ctx, const float* scores, int n_prev, int 
   }
   const size_t need = topk_workspace(n_prev);
   REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
-  hipError_t e = launch_topk(scores, nullptr, 0.f, 0.f, n_prev, budget, n_forced, keep, nullptr, ctx->ws,
+  hipError_t e = launch_topk(scores, nullptr, 0.f, 0.f, false, n_prev, budget, n_forced, keep, nullptr, ctx->ws,
                              ctx->stream);
   if (e != hipSuccess) return hip_status(ctx, e, "msdp_stage (select)");
   e = launch_gather(pos_prev, keep, budget, 4, pos_new, ctx->stream);

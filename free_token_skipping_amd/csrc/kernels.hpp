@@ -66,8 +66,10 @@ hipError_t launch_attn_f32(const float* q, const int32_t* idx, const float* k, c
 
 // --------------------------------------------------------------- select
 size_t topk_workspace(int n);
-hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, int n, int k,
-                       int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s);
+// s_b == nullptr: rank s_a; else fuse s_a and s_b by MaxNorm-Add (multiply == false)
+// or by their product (multiply == true)
+hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
+                       int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s);
 
 // ------------------------------------------------------------- row ops
 hipError_t launch_gather(const void* src, const int32_t* idx, int k, long row_bytes, void* dst,

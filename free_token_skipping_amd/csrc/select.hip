@@ -1,6 +1,6 @@
 // Top-k token selection with forced probe rows, gfx950.
 //
-// Scores (or the MaxNorm-Add fusion of two scores) are mapped to unsigned
+// Scores (or the MaxNorm-Add or Multiply fusion of two scores) are mapped to unsigned
 // keys whose integer order is the float order (NaN lowest, -0 == +0).  An
 // MSB-first radix select over the non-forced rows finds the threshold key T
 // of the (k - n_forced)-th largest and how many rows equal to T to take; a
@@ -30,7 +30,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// MaxNorm-Add in fp32 with a fixed operation order (no contraction).
+// MaxNorm-Add in fp32 with a fixed operation order (no contraction); Multiply
+// is one fp32 product.
 __device__ __forceinline__ float fuse(float a, float b, float ma, float mb, float wa, float wb) {
   const float ta = ma > 0.f ? __fmul_rn(wa, __fdiv_rn(a, ma)) : 0.f;
   const float tb = mb > 0.f ? __fmul_rn(wb, __fdiv_rn(b, mb)) : 0.f;
@@ -57,7 +58,7 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 template <int IPT>
 __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a,
                                                    const float* __restrict__ s_b, float wa, float wb,
-                                                   int n, int k, int nf, int32_t* __restrict__ idx,
+                                                   int mult, int n, int k, int nf, int32_t* __restrict__ idx,
                                                    float* __restrict__ fused_out,
                                                    uint32_t* __restrict__ keys) {
   __shared__ int hist[NW][256];          // one histogram per wave (less atomic contention)
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   }
 
   float ma = 0.f, mb = 0.f;
-  if (s_b) {
+  if (s_b && !mult) {
     float la = -INFINITY, lb = -INFINITY;
     for (int i = tid; i < n; i += TPB) { la = fmaxf(la, s_a[i]); lb = fmaxf(lb, s_b[i]); }
     ma = block_max(la, red);
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     const int i = base + 64 * j;
     uint32_t key = 0u;
     if (i < n) {
-      const float x = s_b ? fuse(s_a[i], s_b[i], ma, mb, wa, wb) : s_a[i];
+      const float x = !s_b ? s_a[i] : mult ? __fmul_rn(s_a[i], s_b[i]) : fuse(s_a[i], s_b[i], ma, mb, wa, wb);
       if (fused_out) fused_out[i] = x;
       key = order_key(x);
       if (i < nfree) { k_or |= key; k_and &= key; }
@@ -223,15 +224,16 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 
 size_t topk_workspace(int n) { return (((size_t)n * 4) + 255) & ~(size_t)255; }
 
-hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, int n, int k,
-                       int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s) {
+hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
+                       int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s) {
   uint32_t* keys = reinterpret_cast<uint32_t*>(ws);
+  const int mult = multiply ? 1 : 0;
   if (n <= TPB * 8)
-    hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, keys);
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys);
   else if (n <= TPB * 32)
-    hipLaunchKernelGGL(topk_kernel<32>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, keys);
+    hipLaunchKernelGGL(topk_kernel<32>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys);
   else
-    hipLaunchKernelGGL(topk_kernel<0>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, n, k, n_forced, idx, fused_out, keys);
+    hipLaunchKernelGGL(topk_kernel<0>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys);
   return hipGetLastError();
 }
 

@@ -93,6 +93,7 @@ class LayerConfig:
     keep_attn: float = 0.35
     keep_ffn: Optional[float] = 0.35      # None: attention-only layer
     w_fuse: Tuple[float, float] = (0.5, 0.5)
+    fusion: str = "maxnorm_add"           # FFN score fusion: "maxnorm_add" or "multiply"
     prenorm: bool = False
     eps: float = 1e-5
     theta: Optional[float] = None         # None: no rotary embedding
@@ -204,8 +205,11 @@ def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None, tm=NO_TIMER):
     k_f = keep_count(cfg.keep_ffn, n)
     fused_score = torch.empty(n, dtype=torch.float32, device=h.device) if trace is not None else None
     with tm("select_ffn", 8.0 * n + 4.0 * k_f):
-        idx_f = capi.spts_score_topk(S, k_f, cfg.P, s_b=L, w_a=cfg.w_fuse[0], w_b=cfg.w_fuse[1],
-                                     fused_out=fused_score)
+        if cfg.fusion == "multiply":
+            idx_f = capi.spts_score_topk_multiply(S, L, k_f, cfg.P, fused_out=fused_score)
+        else:
+            idx_f = capi.spts_score_topk(S, k_f, cfg.P, s_b=L, w_a=cfg.w_fuse[0], w_b=cfg.w_fuse[1],
+                                         fused_out=fused_score)
     # a11 + a12 + a13: gather, reduced SwiGLU, residual add
     if fused:
         # the two GEMMs of spts_reduced_ffn as separate calls, so each is timed

@@ -119,6 +119,14 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
                             float w_b, int n, int k, int n_forced, int32_t* idx,
                             float* fused_out);
 
+/* As spts_score_topk with Table D's "Multiply" fusion, the pages' default
+ * (the criterion C^FFN * S^MHA of [SPTS] Table 6): ranking score
+ *     c = fl(s_a * s_b)   (one float32 product; s_b required),
+ * same forcing, tie, NaN and order rules.  fused_out [n] (optional) receives c.
+ * Workspace: spts_score_topk_workspace(n). */
+spts_status spts_score_topk_multiply(spts_ctx* ctx, const float* s_a, const float* s_b, int n,
+                                     int k, int n_forced, int32_t* idx, float* fused_out);
+
 /* --------------------------------------------------------- gather/scatter */
 
 /* dst[i, :] = src[idx[i], :] for i < k; rows of row_elems elements.

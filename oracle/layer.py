@@ -33,7 +33,7 @@ import numpy as np
 
 from .numerics import bf16, f32, keep_count
 from .pap import pap_scores
-from .select import select_topk, fuse_maxnorm
+from .select import select_topk, fuse_maxnorm, fuse_multiply
 from .attention import reduced_attention
 from .ltp import ltp_scores
 from .ffn import swiglu_rows
@@ -92,18 +92,21 @@ def attention_block(x, pos, w, cfg, k_given=None, prune_to=None):
 
 
 def ffn_block(h, S, w, cfg):
-    """SPTS FFN block: LTP score, MaxNorm-Add fusion with S, reduced SwiGLU.
+    """SPTS FFN block: LTP score, fusion with S (MaxNorm-Add or Multiply), reduced SwiGLU.
 
     h [n,d] residual, S [n] PAP score of this layer.  w: wg/wu [f,d], wd [d,f],
-    u_t [r,d], v_t [d,r].  cfg keys: P, keep_ffn or k_ffn, w_fuse (w_a, w_b),
-    prenorm, eps.
+    u_t [r,d], v_t [d,r].  cfg keys: P, keep_ffn or k_ffn, fusion ("maxnorm_add",
+    the default, with w_fuse (w_a, w_b); or "multiply", [SPTS] Table D), prenorm, eps.
     """
     P = cfg["P"]
     h = np.asarray(h, dtype=np.float64)
     z = bf16(rmsnorm(h, cfg.get("eps", 1e-5))) if cfg.get("prenorm") else h
     L = ltp_scores(z, w["u_t"], w["v_t"])
-    w_a, w_b = cfg.get("w_fuse", (0.5, 0.5))
-    fused = fuse_maxnorm(f32(S), f32(L), w_a, w_b)
+    if cfg.get("fusion", "maxnorm_add") == "multiply":
+        fused = fuse_multiply(f32(S), f32(L))
+    else:
+        w_a, w_b = cfg.get("w_fuse", (0.5, 0.5))
+        fused = fuse_maxnorm(f32(S), f32(L), w_a, w_b)
     n = h.shape[0]
     k_f = cfg["k_ffn"] if "k_ffn" in cfg else keep_count(cfg["keep_ffn"], n)
     idx_f = select_topk(fused, k_f, P)

@@ -21,6 +21,11 @@ an integer (which rows are kept), it is evaluated in float32 with a fixed
 operation order, exactly as the kernel evaluates it:
     c = fl(fl(w_a * fl(s_a / max s_a)) + fl(w_b * fl(s_b / max s_b))),
 with a term taken as 0 when its maximum is not positive.
+
+Table D's "Multiply" (the pages' default fusion, as C^FFN * S^MHA in Table 6)
+is `fuse_multiply`: the product of the two scores, one float32 rounding.  A
+positive factor on either score does not change the ranking, so no
+normalisation is applied.  This build reads C^FFN as the LTP score itself.
 """
 
 import numpy as np
@@ -64,3 +69,10 @@ def fuse_maxnorm(s_a, s_b, w_a=0.5, w_b=0.5):
         return (w * q).astype(np.float32)
 
     return (term(wa, a) + term(wb, b)).astype(np.float32)
+
+
+def fuse_multiply(s_a, s_b):
+    """Multiply fusion in float32: c = fl(s_a * s_b)."""
+    a = np.asarray(s_a, dtype=np.float32)
+    b = np.asarray(s_b, dtype=np.float32)
+    return (a * b).astype(np.float32)

@@ -82,6 +82,12 @@ def test_select_validation(L, ctx):
     assert f(ctx, FAKE, None, 0.5, 0.5, 0, 0, 0, FAKE, None) == SHAPE      # n = 0
     assert f(ctx, FAKE, None, 0.5, 0.5, 10, 4, 1, FAKE, None) == NOMEM
     assert f(ctx, FAKE, MIS, 0.5, 0.5, 10, 4, 1, FAKE, None) == ALIGN
+    m = L.spts_score_topk_multiply
+    assert m(ctx, FAKE, None, 10, 4, 1, FAKE, None) == INVALID            # s_b required
+    assert m(ctx, FAKE, FAKE, 10, 4, 5, FAKE, None) == SHAPE
+    assert m(ctx, FAKE, FAKE, 0, 0, 0, FAKE, None) == SHAPE
+    assert m(ctx, FAKE, FAKE, 10, 4, 1, FAKE, None) == NOMEM
+    assert m(ctx, FAKE, MIS, 10, 4, 1, FAKE, None) == ALIGN
     assert L.spts_msdp_stage(ctx, FAKE, 100, 120, 4, FAKE, FAKE, FAKE, None, None, 0) == SHAPE
     assert L.spts_msdp_stage(ctx, FAKE, 100, 50, 60, FAKE, FAKE, FAKE, None, None, 0) == SHAPE
 

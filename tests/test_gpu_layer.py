@@ -88,20 +88,21 @@ def _layer_case(n, seed=0):
     return sh, W.make_layer(sh, seed=seed)
 
 
-@pytest.mark.parametrize("fused", [True, False])
-def test_layer_32k_recipe_at_4k(fused):
+@pytest.mark.parametrize("fused,fusion", [(True, "maxnorm_add"), (False, "maxnorm_add"), (True, "multiply")])
+def test_layer_32k_recipe_at_4k(fused, fusion):
     """The 32K layer's recipe (attention + FFN, keep 0.35 / 0.35, MaxNorm-Add
-    0.5/0.5, rank-256 proxy) at 4096 tokens, where the oracle runs in seconds."""
+    0.5/0.5 or Multiply fusion, rank-256 proxy) at 4096 tokens, where the
+    oracle runs in seconds."""
     sh, inp = _layer_case(4096)
-    cfg = pipeline.LayerConfig(P=64, keep_attn=0.35, keep_ffn=0.35)
+    cfg = pipeline.LayerConfig(P=64, keep_attn=0.35, keep_ffn=0.35, fusion=fusion)
     x = inp["x"].to(DEV).clone()
     tr = {}
-    _log(f"gpu layer fused={fused}")
+    _log(f"gpu layer fused={fused} fusion={fusion}")
     pipeline.spts_layer(x, torch.arange(sh.n, dtype=torch.int32, device=DEV), _gpu_w(inp), cfg, fused=fused,
                         trace=tr)
     torch.cuda.synchronize()
     _log("oracle layer 4K")
-    ocfg = dict(Hq=32, Hkv=8, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35)
+    ocfg = dict(Hq=32, Hkv=8, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35, fusion=fusion)
     ref, st_a, st_f = olayer.spts_layer(W.as_f64(inp["x"]), np.arange(sh.n), _f64_w(inp), ocfg)
     k = numerics.keep_count(0.35, sh.n)
     idx = _check_selection(tr["idx"], k, 64, sh.n, st_a["S"])

@@ -116,6 +116,20 @@ def test_select_fused_bit_exact(n, k, nf):
     assert np.array_equal(idx.cpu().numpy().astype(np.int64), select.select_topk(ref_c, k, nf))
 
 
+@pytest.mark.parametrize("n,k,nf", [(1000, 350, 64), (32768, 11469, 64)])
+def test_select_multiply_bit_exact(n, k, nf):
+    _log(f"multiply select n={n}")
+    a = W.make_scores(n, seed=9)
+    b = W.make_scores(n, seed=10) * 3.0
+    b[5] = b[9]
+    a[11] = 0.0                                            # a zero factor
+    fused = torch.empty(n, dtype=torch.float32, device=DEV)
+    idx = capi.spts_score_topk_multiply(_cuda(a), _cuda(b), k, nf, fused_out=fused)
+    ref_c = select.fuse_multiply(a.numpy(), b.numpy())
+    assert np.array_equal(fused.cpu().numpy(), ref_c)
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), select.select_topk(ref_c, k, nf))
+
+
 # ------------------------------------------------------------ gather / scatter
 
 def test_gather_scatter_bit_exact():

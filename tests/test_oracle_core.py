@@ -181,6 +181,29 @@ def test_fuse_maxnorm_pins():
     assert np.array_equal(select.fuse_maxnorm(a, np.zeros_like(a)), (np.float32(0.5) * (a / a.max())).astype(np.float32))
 
 
+def test_fuse_multiply_pins():
+    rng = np.random.default_rng(6)
+    a = rng.exponential(size=1000).astype(np.float32)
+    b = rng.exponential(size=1000).astype(np.float32)
+    c = select.fuse_multiply(a, b)
+    assert c.dtype == np.float32
+    # a product of two fp32 values is exact in float64 (24 + 24 < 53 bits), so
+    # the correctly rounded fp32 product is that float64 value rounded once
+    assert np.array_equal(c, (a.astype(np.float64) * b.astype(np.float64)).astype(np.float32))
+    # powers of two scale exactly and leave the ranking unchanged
+    c2 = select.fuse_multiply(a * np.float32(4), b * np.float32(0.5))
+    assert np.array_equal(c2, c * np.float32(2))
+    assert np.array_equal(select.select_topk(c2, 100, 8), select.select_topk(c, 100, 8))
+    # a zero factor gives zero
+    assert np.all(select.fuse_multiply(a, np.zeros_like(b)) == 0)
+    # Multiply and MaxNorm-Add rank differently: a lopsided row wins the sum,
+    # a balanced row wins the product
+    sa = np.array([1.0, 0.5, 0.01], np.float32)
+    sb = np.array([0.01, 0.5, 1.0], np.float32)
+    assert select.select_topk(select.fuse_maxnorm(sa, sb), 1, 0).tolist() == [0]
+    assert select.select_topk(select.fuse_multiply(sa, sb), 1, 0).tolist() == [1]
+
+
 # ------------------------------------------------------------------- attention
 
 def _sdpa_gqa(q, k, v, scale):
