@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single-layer", action="store_true")
     ap.add_argument("--no-ttft", action="store_true", help="skip the 32-layer prefill schedule vs dense table")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the cold/warm gather and scatter-add table")
     ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
     ap.add_argument("--cpu-sample", type=float, default=1.0 / 32,
                     help="fraction of row-separable oracle work timed for the CPU baseline")
@@ -197,6 +198,53 @@ def ttft_table(x0, layers, cfg, reps=2):
     return {"schedule": "32 layers, dense 0-9, stage ends 13/18/23/28, candidates 9216/7168/4096/2048, "
                         "1024 after; keep 0.35 per skipping layer",
             "weights": f"{len(layers)} generated layers cycled", "reps": reps, "rows": rows}
+
+
+# ------------------------------------------------- HBM-bound row kernels
+
+def hbm_table(x0, reps=5):
+    """Standalone gather and scatter-add of the 32K layer's selected rows
+    (11469 of 32768 rows of 4096 bf16): algorithmic bytes / time against the
+    8 TB/s HBM peak.  Cold: a 1.5 GiB buffer is read before each rep, so the
+    256 MB last-level cache holds none of the operands and no dirty lines of
+    its own (a written flush buffer would be written back to HBM during the
+    timed kernel); warm: back to back."""
+    import numpy as np
+    import torch
+    from free_token_skipping_amd import capi
+    N, d = x0.shape
+    k = 11469
+    rng = np.random.default_rng(0)
+    idx = torch.from_numpy(np.sort(rng.choice(N, k, replace=False)).astype(np.int32)).to(x0.device)
+    src = torch.empty((k, d), dtype=torch.bfloat16, device=x0.device)
+    dst = x0.clone()
+    flush = torch.ones(3 << 28, dtype=torch.float16, device=x0.device)      # 1.5 GiB
+    row = d * 2
+    cases = {"gather": (lambda: capi.spts_gather(x0, idx, src), 2.0 * k * row),
+             "scatter_add": (lambda: capi.spts_scatter(src, idx, dst, accumulate=True), 3.0 * k * row)}
+    out = {}
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        for mode in ("cold", "warm"):
+            ts = []
+            for r in range(reps):
+                if mode == "cold":
+                    flush.amax()                          # reads every line of the flush buffer
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = sorted(ts)[len(ts) // 2]
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out[f"{name}_{mode}"] = {"us": round(ms * 1e3, 1), "bytes": int(nbytes), "gbs": round(gbs, 1),
+                                     "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+            log(f"{name} {mode}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.0%} of HBM peak)")
+    del flush
+    return out
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -370,6 +418,9 @@ def main():
             rec.setdefault("also", {})[name] = {"tokens_per_s_per_layer": round(r["tokens_per_s_per_layer"], 1),
                                                 "ms_per_step": round(r["ms_per_step"], 4),
                                                 "roofline": r["roofline"], "breakdown": r["breakdown"]}
+    if not args.no_hbm:
+        log("timing the standalone gather / scatter-add, cold and warm")
+        rec.setdefault("also", {})["hbm_row_kernels"] = hbm_table(x0)
     if not args.no_ttft:
         log("timing the 32-layer prefill schedule against dense")
         rec.setdefault("also", {})["prefill_32_layers"] = ttft_table(x0, layers, stack_cfg)

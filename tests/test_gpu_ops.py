@@ -132,13 +132,14 @@ def test_select_multiply_bit_exact(n, k, nf):
 
 # ------------------------------------------------------------ gather / scatter
 
-def test_gather_scatter_bit_exact():
-    _log("gather / scatter")
-    x = W.randn((777, 520), seed=9)
+@pytest.mark.parametrize("width", [520, 1536])   # 1040-byte rows; 3 KiB rows (1 KiB-segment kernels)
+def test_gather_scatter_bit_exact(width):
+    _log(f"gather / scatter width={width}")
+    x = W.randn((777, width), seed=9)
     idx = W.sorted_rows(777, 300, 16, seed=10)
     g = capi.spts_gather(_cuda(x), _cuda(idx))
     assert torch.equal(g.cpu(), x[idx.long()])
-    src = W.randn((300, 520), seed=11)
+    src = W.randn((300, width), seed=11)
     dst = _cuda(x).clone()
     capi.spts_scatter(_cuda(src), _cuda(idx), dst, accumulate=False)
     ref = x.clone()
