@@ -376,9 +376,31 @@ def main():
             x = x0.clone()
         pipeline.spts_layer(x, pos0, layers[0], layer_cfg, fused=fused, tm=tm)
 
+    # the pages' default scoring on the same layer: Multiply fusion and the
+    # structured proxy (512 hidden channels, rank 256 per projection), its
+    # factors drawn from layer 0's own feed-forward weights
+    defaults_cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=0.35, keep_ffn=0.35,
+                               fusion="multiply", proxy="structured")
+    defaults_w = None
+    if not args.no_single_layer:
+        import workloads as W
+        sp = W.structured_proxy(st["layers"][0]["wg"], st["layers"][0]["wu"], st["layers"][0]["wd"], 512, 256,
+                                seed=cfgd["seed"])
+        defaults_w = dict(layers[0])
+        defaults_w["proxy_packed"] = capi.pack_structured_proxy(
+            *[sp[k].to(dev) for k in ("a_g_t", "b_g_t", "a_u_t", "b_u_t", "c_t", "d_t")])
+
+    def defaults_step(tm):
+        with tm("layer_setup", 4.0 * x0.numel()):
+            x = x0.clone()
+        pipeline.spts_layer(x, pos0, defaults_w, defaults_cfg, fused=fused, tm=tm)
+
     results = {}
-    for name, fn, nl in (("msdp_stack_32k", stack_step, n_layers), ("layer_32k", layer_step, 1)):
+    for name, fn, nl in (("msdp_stack_32k", stack_step, n_layers), ("layer_32k", layer_step, 1),
+                         ("layer_32k_page_defaults", defaults_step, 1)):
         if name != args.workload and (args.no_single_layer or name == "msdp_stack_32k"):
+            continue
+        if name == "layer_32k_page_defaults" and defaults_w is None:
             continue
         log(f"timing {name}: warmup {args.warmup}, steps {args.steps}")
         total_ms, wall_ms, summ = timed(fn, args.steps, args.warmup)

@@ -24,6 +24,7 @@ EXPORTS = [
     "spts_status_name", "spts_check",
     "spts_probe_attention_workspace", "spts_score_topk_workspace", "spts_ltp_probe_workspace",
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
+    "spts_ltp_structured_workspace", "spts_ltp_probe_structured",
     "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_gather", "spts_scatter",
     "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
     "spts_linear", "spts_linear_rope", "spts_linear_kv", "spts_linear_swiglu", "spts_rope_table",
@@ -46,6 +47,8 @@ _SIGS = {
     "spts_reduced_ffn_workspace": (_SZ, [_I, _I]),
     "spts_msdp_stage_workspace": (_SZ, [_I]),
     "spts_linear_workspace": (_SZ, [_I, _I, _I]),
+    "spts_ltp_structured_workspace": (_SZ, [_I, _I, _I, _I]),
+    "spts_ltp_probe_structured": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
     "spts_score_topk_multiply": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
@@ -253,6 +256,36 @@ def spts_ltp_probe(z, u_t, v_t, score=None):
     bf = torch.bfloat16
     _check(ctx, lib().spts_ltp_probe(h, _ptr(z, bf, "z"), _ptr(u_t, bf, "u_t"), _ptr(v_t, bf, "v_t"), n, d, r,
                                      _ptr(score, torch.float32, "score")), "spts_ltp_probe")
+    return score
+
+
+def pack_structured_proxy(a_g_t, b_g_t, a_u_t, b_u_t, c_t, d_t):
+    """Arrange the structured proxy's factors (nn.Linear layout: a_g_t, a_u_t
+    [r, d]; b_g_t, b_u_t [d_low, r]; c_t [r, d_low]; d_t [d, r]) in the block
+    layout spts_ltp_probe_structured reads.  Layout only: concatenation and
+    zero blocks."""
+    z = torch.zeros_like(b_g_t)
+    return {"a_gu_t": torch.cat([a_g_t, a_u_t], 0).contiguous(),
+            "b_gate": torch.cat([b_g_t, z, b_g_t, z], 1).contiguous(),
+            "b_up": torch.cat([z, b_u_t, z, b_u_t], 1).contiguous(),
+            "c_t": c_t.contiguous(), "d_t": d_t.contiguous()}
+
+
+def spts_ltp_probe_structured(z, packed, score=None):
+    """Structured LTP score ||(silu((zA_g)B_g) * ((zA_u)B_u)) C D|| per row."""
+    n, d = z.shape
+    r = packed["c_t"].shape[0]
+    d_low = packed["c_t"].shape[1]
+    if score is None:
+        score = torch.empty(n, dtype=torch.float32, device=z.device)
+    ctx = context()
+    h = ctx.bind(lib().spts_ltp_structured_workspace(n, d, r, d_low), z.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_ltp_probe_structured(h, _ptr(z, bf, "z"), _ptr(packed["a_gu_t"], bf, "a_gu_t"),
+                                                _ptr(packed["b_gate"], bf, "b_gate"), _ptr(packed["b_up"], bf, "b_up"),
+                                                _ptr(packed["c_t"], bf, "c_t"), _ptr(packed["d_t"], bf, "d_t"),
+                                                n, d, r, d_low, _ptr(score, torch.float32, "score")),
+           "spts_ltp_probe_structured")
     return score
 
 

@@ -132,6 +132,22 @@ size_t spts_ltp_probe_workspace(int n, int d, int r) {
   const size_t part = round256((size_t)n * (d / 256) * 4);        // row sums of squares
   return t2 + part + gemm_split_workspace(n, d, r, EPI_SPLIT);    // split-K partials of z U
 }
+// T2 [n, 4r] | H2 [n, 2 d_low] | Td2 [n, 2r] (bf16 hi/lo pairs) | row sums [n, d/256] | split-K partials
+static void ltp_structured_layout(int n, int d, int r, int d_low, size_t off[5]) {
+  off[0] = 0;
+  off[1] = off[0] + round256((size_t)n * 4 * r * 2);
+  off[2] = off[1] + round256((size_t)n * 2 * d_low * 2);
+  off[3] = off[2] + round256((size_t)n * 2 * r * 2);
+  off[4] = off[3] + round256((size_t)n * (d / 256) * 4);
+}
+size_t spts_ltp_structured_workspace(int n, int d, int r, int d_low) {
+  if (n <= 0 || d <= 0 || r <= 0 || d_low <= 0) return 0;
+  size_t off[5];
+  ltp_structured_layout(n, d, r, d_low, off);
+  const size_t s1 = gemm_split_workspace(n, d, 2 * r, EPI_SPLIT);
+  const size_t s3 = gemm_split_workspace(n, 2 * d_low, r, EPI_SPLIT);
+  return off[4] + (s1 > s3 ? s1 : s3);
+}
 size_t spts_linear_workspace(int m, int kdim, int n) {
   if (m <= 0 || kdim <= 0 || n <= 0) return 0;
   return gemm_split_workspace(m, kdim, n, EPI_STORE);
@@ -419,6 +435,63 @@ spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const 
   e = launch_gemm(g2, EPI_SUMSQ, ctx->stream);
   if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe (T V)");
   return hip_status(ctx, launch_rowsum_sqrt(part, n, d / 256, score, ctx->stream), "ltp_probe (norm)");
+}
+
+spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* a_gu_t, const void* b_gate,
+                                      const void* b_up, const void* c_t, const void* d_t, int n, int d, int r,
+                                      int d_low, float* score) {
+  CHECK_CTX();
+  REQUIRE(n >= 0 && d > 0 && r > 0 && d_low > 0, SPTS_ERR_SHAPE, "bad structured LTP sizes");
+  REQUIRE(d % 256 == 0 && r % 256 == 0 && d_low % 256 == 0, SPTS_ERR_UNSUPPORTED,
+          "structured LTP needs d, r and d_low multiples of 256 (d=%d r=%d d_low=%d)", d, r, d_low);
+  if (n == 0) return SPTS_OK;
+  REQUIRE_PTR(z); REQUIRE_PTR(a_gu_t); REQUIRE_PTR(b_gate); REQUIRE_PTR(b_up); REQUIRE_PTR(c_t);
+  REQUIRE_PTR(d_t); REQUIRE_PTR(score);
+  REQUIRE_ALIGN(z); REQUIRE_ALIGN(a_gu_t); REQUIRE_ALIGN(b_gate); REQUIRE_ALIGN(b_up); REQUIRE_ALIGN(c_t);
+  REQUIRE_ALIGN(d_t); REQUIRE_ALIGN(score);
+  const size_t need = spts_ltp_structured_workspace(n, d, r, d_low);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  size_t off[5];
+  ltp_structured_layout(n, d, r, d_low, off);
+  char* ws = reinterpret_cast<char*>(ctx->ws);
+  uint16_t* t2 = reinterpret_cast<uint16_t*>(ws + off[0]);
+  uint16_t* h2 = reinterpret_cast<uint16_t*>(ws + off[1]);
+  uint16_t* td2 = reinterpret_cast<uint16_t*>(ws + off[2]);
+  float* part = reinterpret_cast<float*>(ws + off[3]);
+  float* split_ws = reinterpret_cast<float*>(ws + off[4]);
+  const size_t split_bytes = ctx->ws_bytes - off[4];
+  // [z A_g | z A_u] as hi/lo pairs: T2 row = [Tg_hi | Tu_hi | Tg_lo | Tu_lo]
+  GemmArgs g1{};
+  g1.a = reinterpret_cast<const uint16_t*>(z); g1.m = n; g1.k = d; g1.lda = d;
+  g1.b0 = reinterpret_cast<const uint16_t*>(a_gu_t); g1.ldb = d; g1.n = 2 * r;
+  g1.out = t2; g1.ldc = 4 * r;
+  g1.partial = split_ws; g1.partial_bytes = split_bytes;
+  hipError_t e = launch_gemm(g1, EPI_SPLIT, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (z A)");
+  // h = silu(T_g B_g) * (T_u B_u) over the hi/lo pairs (the packed B blocks pick
+  // the gate or up columns of T2), written as hi/lo pairs
+  GemmArgs g2{};
+  g2.a = t2; g2.m = n; g2.k = 4 * r; g2.lda = 4 * r;
+  g2.b0 = reinterpret_cast<const uint16_t*>(b_gate); g2.b1 = reinterpret_cast<const uint16_t*>(b_up);
+  g2.ldb = 4 * r; g2.n = 2 * d_low; g2.out = h2; g2.ldc = 2 * d_low;
+  e = launch_gemm(g2, EPI_SWIGLU_SPLIT, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (swiglu)");
+  // h C over the hi/lo pairs (C's columns read modulo d_low), as hi/lo pairs
+  GemmArgs g3{};
+  g3.a = h2; g3.m = n; g3.k = 2 * d_low; g3.lda = 2 * d_low;
+  g3.b0 = reinterpret_cast<const uint16_t*>(c_t); g3.ldb = d_low; g3.kwrap = d_low; g3.n = r;
+  g3.out = td2; g3.ldc = 2 * r;
+  g3.partial = split_ws; g3.partial_bytes = split_bytes;
+  e = launch_gemm(g3, EPI_SPLIT, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (h C)");
+  // ||(h C) D||: row sums of squares per 256 columns, then the root
+  GemmArgs g4{};
+  g4.a = td2; g4.m = n; g4.k = 2 * r; g4.lda = 2 * r;
+  g4.b0 = reinterpret_cast<const uint16_t*>(d_t); g4.ldb = r; g4.kwrap = r; g4.n = d;
+  g4.out = part; g4.ldc = d / 256;
+  e = launch_gemm(g4, EPI_SUMSQ, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (T D)");
+  return hip_status(ctx, launch_rowsum_sqrt(part, n, d / 256, score, ctx->stream), "ltp_probe_structured (norm)");
 }
 
 // ------------------------------------------------------------------------ FFN

@@ -55,7 +55,8 @@ void gemm_tn_kernel(GemmArgs g) {
   // across all column tiles, so the ~32 tiles resident on one XCD at a time
   // form a 4 x 8 block that shares A and B k-slices in that XCD's L2.
   const int tiles_m = (g.m + BM - 1) / BM;
-  const int tiles_n = (EPI == EPI_SWIGLU) ? (g.n / 2) / 128 : g.n / BN;
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
+  const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
   const int ksplit = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
   const int total = tiles_m * tiles_n * ksplit;
   const int per_xcd = (total + 7) / 8;
@@ -92,7 +93,7 @@ void gemm_tn_kernel(GemmArgs g) {
     if (ar >= g.m) ar = g.m - 1;
     if (GATHER) ar = g.a_rows[ar];
     a_off[i] = ((uint32_t)ar * (uint32_t)g.lda + ld_ch * 8) * 2u;
-    if (EPI == EPI_SWIGLU) {
+    if (kSwiglu) {
       // wave column block r / 128: rows 0..63 gate, 64..127 up, same 64 outputs
       const int within = r & 127;
       const uint32_t brow = (uint32_t)tile_n * 128 + (r >> 7) * 64 + (within & 63);
@@ -122,7 +123,7 @@ void gemm_tn_kernel(GemmArgs g) {
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(abase + a_off[i] + ka),
           (__attribute__((address_space(3))) void*)(a_s + rb * 512), 16, 0, 0);
-      const char* bb = (EPI == EPI_SWIGLU && ((b_from_up >> i) & 1u)) ? b1base : b0base;
+      const char* bb = (kSwiglu && ((b_from_up >> i) & 1u)) ? b1base : b0base;
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(bb + b_off[i] + kb),
           (__attribute__((address_space(3))) void*)(b_s + rb * 512), 16, 0, 0);
@@ -223,7 +224,7 @@ void gemm_tn_kernel(GemmArgs g) {
   for (int i = 0; i < 2; ++i) {
     const int row = tile_m * BM + wm * 64 + i * 32 + l32;
     if (row >= g.m) continue;
-    if (EPI == EPI_SWIGLU) {
+    if (kSwiglu) {
       uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)row * g.ldc;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -241,6 +242,12 @@ void gemm_tn_kernel(GemmArgs g) {
           w[0] = pack2bf(hv[0], hv[1]);
           w[1] = pack2bf(hv[2], hv[3]);
           *reinterpret_cast<u32x2*>(out + col) = w;
+          if (EPI == EPI_SWIGLU_SPLIT) {
+            u32x2 wl;
+            wl[0] = pack2bf(hv[0] - lo_bf(w[0]), hv[1] - hi_bf(w[0]));
+            wl[1] = pack2bf(hv[2] - lo_bf(w[1]), hv[3] - hi_bf(w[1]));
+            *reinterpret_cast<u32x2*>(out + g.n / 2 + col) = wl;
+          }
         }
       continue;
     }
@@ -374,7 +381,8 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
 template <int EPI, bool GATHER>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.m + BM - 1) / BM;
-  const int tiles_n = (EPI == EPI_SWIGLU) ? (g.n / 2) / 128 : g.n / BN;
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
+  const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
   const size_t lds = 2 * 2 * TILE_ELEMS * sizeof(uint16_t);
   static bool attr_set = false;
   if (!attr_set) {
@@ -440,6 +448,7 @@ hipError_t launch_gemm(const GemmArgs& g0, int epi, hipStream_t s) {
     case EPI_ROPE: return gather ? launch_one<EPI_ROPE, true>(g, s) : launch_one<EPI_ROPE, false>(g, s);
     case EPI_SWIGLU: return gather ? launch_one<EPI_SWIGLU, true>(g, s) : launch_one<EPI_SWIGLU, false>(g, s);
     case EPI_KV: return gather ? launch_one<EPI_KV, true>(g, s) : launch_one<EPI_KV, false>(g, s);
+    case EPI_SWIGLU_SPLIT: return launch_one<EPI_SWIGLU_SPLIT, false>(g, s);
     case EPI_SPLIT: return launch_one<EPI_SPLIT, false>(g, s);
     case EPI_SUMSQ: return launch_one<EPI_SUMSQ, false>(g, s);
     default: return hipErrorInvalidValue;

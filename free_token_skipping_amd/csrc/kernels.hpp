@@ -19,6 +19,8 @@ enum GemmEpilogue : int {
   EPI_PARTIAL = 5, // split-K pass: fp32 partial[ks][i][c] (internal)
   EPI_KV = 6,      // two-part B: columns < n0 from b0 into out (RoPE if rope_table),
                    // the rest from b1 into out2 (ldc2 columns), both bf16
+  EPI_SWIGLU_SPLIT = 7,  // as SWIGLU, the fp32 result h written as bf16 pair: hi = bf16(h)
+                         // at column c, lo = bf16(h - hi) at column f + c (f = n / 2)
 };
 
 struct GemmArgs {

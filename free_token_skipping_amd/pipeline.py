@@ -94,6 +94,7 @@ class LayerConfig:
     keep_ffn: Optional[float] = 0.35      # None: attention-only layer
     w_fuse: Tuple[float, float] = (0.5, 0.5)
     fusion: str = "maxnorm_add"           # FFN score fusion: "maxnorm_add" or "multiply"
+    proxy: str = "linear"                 # LTP proxy: "linear" (u_t, v_t) or "structured" (proxy_packed)
     prenorm: bool = False
     eps: float = 1e-5
     theta: Optional[float] = None         # None: no rotary embedding
@@ -192,15 +193,21 @@ def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None, tm=NO_TIMER):
     """h [n, d] residual (updated in place), S [n] PAP score of this layer."""
     n, d = h.shape
     f = w["wg"].shape[0]
-    r = w["u_t"].shape[0]
     if cfg.prenorm:
         with tm("rmsnorm", 4.0 * n * d):
             z = capi.spts_rmsnorm(h, cfg.eps)
     else:
         z = h
     # a9: LTP proxy score
-    with tm("ltp_probe", 4.0 * n * d * r):
-        L = capi.spts_ltp_probe(z, w["u_t"], w["v_t"])
+    if cfg.proxy == "structured":
+        pk = w["proxy_packed"]
+        r, d_low = pk["c_t"].shape
+        with tm("ltp_probe", 2.0 * n * 3 * r * (d + d_low)):
+            L = capi.spts_ltp_probe_structured(z, pk)
+    else:
+        r = w["u_t"].shape[0]
+        with tm("ltp_probe", 4.0 * n * d * r):
+            L = capi.spts_ltp_probe(z, w["u_t"], w["v_t"])
     # a10: fused score -> select the FFN rows
     k_f = keep_count(cfg.keep_ffn, n)
     fused_score = torch.empty(n, dtype=torch.float32, device=h.device) if trace is not None else None

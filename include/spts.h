@@ -78,6 +78,7 @@ spts_status spts_check(spts_ctx* ctx);
 size_t spts_probe_attention_workspace(int n, int P, int Hq);
 size_t spts_score_topk_workspace(int n);
 size_t spts_ltp_probe_workspace(int n, int d, int r);
+size_t spts_ltp_structured_workspace(int n, int d, int r, int d_low);
 size_t spts_reduced_ffn_workspace(int k, int f);
 size_t spts_msdp_stage_workspace(int n_prev);
 /* Workspace with which spts_linear / spts_linear_rope split the inner
@@ -164,6 +165,26 @@ spts_status spts_reduced_attention(spts_ctx* ctx, spts_dtype dtype, const void* 
  * Requires d % 256 == 0, r % 256 == 0.  Workspace: spts_ltp_probe_workspace. */
 spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const void* v_t,
                            int n, int d, int r, float* score);
+
+/* The structured proxy form of [SPTS] Table A: the feed-forward restricted to
+ * d_low of its hidden channels, each projection factored at rank r
+ * (r * (d + d_low) multiply-accumulates per projection and token):
+ *     g = (z A_g) B_g,  u = (z A_u) B_u       (d -> r -> d_low)
+ *     h = silu(g) * u
+ *     score[m] = || (h C) D ||_2               (d_low -> r -> d)
+ * The factors come packed in nn.Linear layout (blocks of r columns):
+ *     a_gu_t [2r, d]     = [A_g^T ; A_u^T]
+ *     b_gate [d_low, 4r] = [B_g^T | 0 | B_g^T | 0]
+ *     b_up   [d_low, 4r] = [0 | B_u^T | 0 | B_u^T]
+ *     c_t    [r, d_low]  = C^T,   d_t [d, r] = D^T
+ * z A, h and h C are kept near fp32 precision (each split into two bf16 terms;
+ * the zero blocks route the terms of the gate and up halves).
+ *   z [n, d] bf16, score [n] float32.
+ * Requires d, r, d_low multiples of 256.  Workspace: spts_ltp_structured_workspace. */
+spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* a_gu_t,
+                                      const void* b_gate, const void* b_up, const void* c_t,
+                                      const void* d_t, int n, int d, int r, int d_low,
+                                      float* score);
 
 /* ------------------------------------------------------------- reduced FFN */
 

@@ -35,7 +35,7 @@ from .numerics import bf16, f32, keep_count
 from .pap import pap_scores
 from .select import select_topk, fuse_maxnorm, fuse_multiply
 from .attention import reduced_attention
-from .ltp import ltp_scores
+from .ltp import ltp_scores, ltp_structured_scores
 from .ffn import swiglu_rows
 from .normrope import rmsnorm, rope
 
@@ -95,13 +95,17 @@ def ffn_block(h, S, w, cfg):
     """SPTS FFN block: LTP score, fusion with S (MaxNorm-Add or Multiply), reduced SwiGLU.
 
     h [n,d] residual, S [n] PAP score of this layer.  w: wg/wu [f,d], wd [d,f],
-    u_t [r,d], v_t [d,r].  cfg keys: P, keep_ffn or k_ffn, fusion ("maxnorm_add",
+    u_t [r,d], v_t [d,r] (or, with proxy "structured", the factors a_g_t,
+    b_g_t, a_u_t, b_u_t, c_t, d_t).  cfg keys: P, keep_ffn or k_ffn, fusion ("maxnorm_add",
     the default, with w_fuse (w_a, w_b); or "multiply", [SPTS] Table D), prenorm, eps.
     """
     P = cfg["P"]
     h = np.asarray(h, dtype=np.float64)
     z = bf16(rmsnorm(h, cfg.get("eps", 1e-5))) if cfg.get("prenorm") else h
-    L = ltp_scores(z, w["u_t"], w["v_t"])
+    if cfg.get("proxy", "linear") == "structured":
+        L = ltp_structured_scores(z, w["a_g_t"], w["b_g_t"], w["a_u_t"], w["b_u_t"], w["c_t"], w["d_t"])
+    else:
+        L = ltp_scores(z, w["u_t"], w["v_t"])
     if cfg.get("fusion", "maxnorm_add") == "multiply":
         fused = fuse_multiply(f32(S), f32(L))
     else:

@@ -50,3 +50,13 @@ def structured_proxy_delta(z, gate_f, up_f, down_f, channels):
     u = apply(z, up_f)
     h = (g / (1.0 + np.exp(-g))) * u
     return apply(h, down_f)
+
+
+def ltp_structured_scores(z, a_g_t, b_g_t, a_u_t, b_u_t, c_t, d_t):
+    """Score of the structured proxy: L_n = ||dX_hat_n||_2 with dX_hat from
+    `structured_proxy_delta`, every projection given as two nn.Linear-layout
+    factors (gate: a_g_t [r, d] then b_g_t [D_low, r]; up likewise; down:
+    c_t [r, D_low] then d_t [d, r])."""
+    t = lambda w: np.asarray(w, dtype=np.float64).T
+    dx = structured_proxy_delta(z, [t(a_g_t), t(b_g_t)], [t(a_u_t), t(b_u_t)], [t(c_t), t(d_t)], None)
+    return np.sqrt(np.einsum("nd,nd->n", dx, dx))

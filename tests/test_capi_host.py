@@ -104,6 +104,13 @@ def test_gemm_family_validation(L, ctx):
     assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 10, 4096, 14336, FAKE, None, 0) == NOMEM
     assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 0, 4096, 14336, FAKE, None, 0) == OK
     assert L.spts_rmsnorm(ctx, FAKE, 10, 12, 1e-5, FAKE) == SHAPE
+    st = L.spts_ltp_probe_structured
+    assert st(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4096, 192, 512, FAKE) == UNSUPPORTED   # r % 256
+    assert st(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4096, 256, 300, FAKE) == UNSUPPORTED   # d_low % 256
+    assert st(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4096, 256, 512, FAKE) == NOMEM
+    assert st(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4096, 256, 512, FAKE) == OK             # empty
+    assert st(ctx, FAKE, None, FAKE, FAKE, FAKE, FAKE, 10, 4096, 256, 512, FAKE) == INVALID
+    assert L.spts_ltp_structured_workspace(100, 4096, 256, 512) > 0
     kv = L.spts_linear_kv
     assert kv(ctx, FAKE, None, 100, 128, FAKE, 1024, FAKE, 200, FAKE, FAKE, None, None) == UNSUPPORTED  # nv % 256
     assert kv(ctx, FAKE, None, 100, 96, FAKE, 1024, FAKE, 1024, FAKE, FAKE, None, None) == UNSUPPORTED   # k % 64

@@ -116,6 +116,36 @@ def test_layer_32k_recipe_at_4k(fused, fusion):
     assert_close(got[same], ref[same], BF16_REL, "layer output rows")
 
 
+def test_layer_4k_page_defaults():
+    """The pages' default scoring: Multiply fusion and the structured proxy
+    (512 channels, rank 256 per projection), on the 32K layer's recipe at
+    4096 tokens."""
+    sh, inp = _layer_case(4096)
+    sp = W.structured_proxy(inp["wg"], inp["wu"], inp["wd"], 512, 256, seed=5)
+    keys = ("a_g_t", "b_g_t", "a_u_t", "b_u_t", "c_t", "d_t")
+    gw = _gpu_w(inp)
+    gw["proxy_packed"] = capi.pack_structured_proxy(*[sp[k].to(DEV) for k in keys])
+    cfg = pipeline.LayerConfig(P=64, keep_attn=0.35, keep_ffn=0.35, fusion="multiply", proxy="structured")
+    x = inp["x"].to(DEV).clone()
+    tr = {}
+    _log("gpu layer, page defaults")
+    pipeline.spts_layer(x, torch.arange(sh.n, dtype=torch.int32, device=DEV), gw, cfg, trace=tr)
+    torch.cuda.synchronize()
+    ow = _f64_w(inp)
+    ow.update({k: W.as_f64(sp[k]) for k in keys})
+    ocfg = dict(Hq=32, Hkv=8, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35, fusion="multiply", proxy="structured")
+    _log("oracle layer 4K, page defaults")
+    ref, st_a, st_f = olayer.spts_layer(W.as_f64(inp["x"]), np.arange(sh.n), ow, ocfg)
+    k = numerics.keep_count(0.35, sh.n)
+    idx = _check_selection(tr["idx"], k, 64, sh.n, st_a["S"])
+    assert_close(np64(tr["L"]), st_f["L"], 1e-2, "structured LTP scores (chain)")
+    idx_f = _check_selection(tr["idx_f"], k, 64, sh.n, st_f["fused"].astype(np.float64))
+    got = np64(x)
+    same = (_mask(sh.n, idx) == _mask(sh.n, st_a["idx"])) & (_mask(sh.n, idx_f) == _mask(sh.n, st_f["idx_f"]))
+    assert same.mean() > 0.98
+    assert_close(got[same], ref[same], BF16_REL, "layer output rows")
+
+
 def test_layer_32k_full_size_structure_and_scores():
     """Full 32K layer on the GPU: exact structure, and the probe score and
     first selection against the oracle's own projections of the inputs."""

@@ -284,6 +284,32 @@ def test_structured_proxy_full_rank_is_swiglu():
     assert np.allclose(delta, ref, rtol=1e-12, atol=1e-13)
 
 
+def test_structured_scores_exact_factors_are_swiglu_norm():
+    # each projection given as (weight, identity): the score is ||SwiGLU(z)||
+    rng = np.random.default_rng(13)
+    d, f = 16, 24
+    wg, wu, wd = (rng.standard_normal(s) * 0.3 for s in ((f, d), (f, d), (d, f)))
+    z = rng.standard_normal((7, d))
+    L = ltp.ltp_structured_scores(z, wg, np.eye(f), wu, np.eye(f), np.eye(f), wd)
+    ref = (F.silu(torch.from_numpy(z @ wg.T)) * torch.from_numpy(z @ wu.T)).numpy() @ wd.T
+    assert np.allclose(L, np.linalg.norm(ref, axis=1), rtol=1e-12)
+
+
+def test_structured_proxy_generator_full_rank():
+    rng = np.random.default_rng(14)
+    d, f, d_low = 64, 96, 32
+    wg, wu, wd = (workloads.to_bf16(rng.standard_normal(s) * 0.05) for s in ((f, d), (f, d), (d, f)))
+    sp = workloads.structured_proxy(wg, wu, wd, d_low, d_low, seed=3)
+    ch = sp["channels"]
+    assert len(ch) == d_low and np.all(np.diff(ch) > 0)
+    f64 = workloads.as_f64
+    # at rank d_low each factor pair reproduces the restricted map up to the bf16 storage of the factors
+    for a, b, ref in ((sp["a_g_t"], sp["b_g_t"], f64(wg)[ch].T), (sp["a_u_t"], sp["b_u_t"], f64(wu)[ch].T),
+                      (sp["c_t"], sp["d_t"], f64(wd)[:, ch].T)):
+        rec = f64(a).T @ f64(b).T
+        assert np.abs(rec - ref).max() <= 1e-2 * np.abs(ref).max()
+
+
 # ------------------------------------------------------------------------- FFN
 
 def test_swiglu_against_torch():

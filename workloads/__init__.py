@@ -107,6 +107,36 @@ def proxy_factors(m: np.ndarray, r: int):
     return u_t, v_t
 
 
+def structured_proxy(wg, wu, wd, d_low: int, r: int, seed: int = 0):
+    """Factors of a structured proxy ([SPTS] Table A's form) built from one
+    layer's own feed-forward weights -- a synthetic stand-in for the pages'
+    channels chosen by saliency on calibration data.
+
+    Draws d_low of the f hidden channels (sorted, without replacement, from
+    default_rng(seed)); restricts gate, up and down to them; truncates each
+    restricted map to rank r by SVD (largest-magnitude entry of each left
+    singular vector made positive).  Returns bf16 tensors in nn.Linear
+    layout: a_g_t, a_u_t [r, d]; b_g_t, b_u_t [d_low, r]; c_t [r, d_low];
+    d_t [d, r]; plus the channel indices.
+    """
+    rng = np.random.default_rng(seed)
+    wg64, wu64, wd64 = as_f64(wg), as_f64(wu), as_f64(wd)
+    ch = np.sort(rng.choice(wg64.shape[0], d_low, replace=False))
+
+    def factor(mp):
+        # mp: the [in, out] map x -> x @ mp; returns W1 [r, in], W2 [out, r]
+        p, s, qt = np.linalg.svd(mp, full_matrices=False)
+        p, s, q = p[:, :r], s[:r], qt[:r].T
+        flip = np.sign(p[np.argmax(np.abs(p), axis=0), np.arange(r)])
+        return (p * (s * flip)[None, :]).T, q * flip[None, :]
+
+    a_g_t, b_g_t = factor(wg64[ch].T)
+    a_u_t, b_u_t = factor(wu64[ch].T)
+    c_t, d_t = factor(wd64[:, ch].T)
+    return dict(a_g_t=to_bf16(a_g_t), b_g_t=to_bf16(b_g_t), a_u_t=to_bf16(a_u_t), b_u_t=to_bf16(b_u_t),
+                c_t=to_bf16(c_t), d_t=to_bf16(d_t), channels=ch)
+
+
 # ------------------------------------------------------------ layer weights
 
 def _draw_layer_weights(rng, sh: LayerShape, with_ffn: bool, with_wk: bool = True,
