@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-single-layer", action="store_true")
     ap.add_argument("--no-ttft", action="store_true", help="skip the 32-layer prefill schedule vs dense table")
     ap.add_argument("--no-hbm", action="store_true", help="skip the cold/warm gather and scatter-add table")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode / end-to-end table")
     ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
     ap.add_argument("--cpu-sample", type=float, default=1.0 / 32,
                     help="fraction of row-separable oracle work timed for the CPU baseline")
@@ -198,6 +199,67 @@ def ttft_table(x0, layers, cfg, reps=2):
     return {"schedule": "32 layers, dense 0-9, stage ends 13/18/23/28, candidates 9216/7168/4096/2048, "
                         "1024 after; keep 0.35 per skipping layer",
             "weights": f"{len(layers)} generated layers cycled", "reps": reps, "rows": rows}
+
+
+def decode_table(x0, layers, cfg, tokens=16, gen=(32, 128, 512)):
+    """Decode after the 32-layer prefill at 32K tokens: per-token latency with
+    each layer's cache holding its candidates (SPTS, [SPTS] Table 5) against
+    full caches (dense prefill), and end-to-end time for G generated tokens
+    = prefill + G * per-token time (a speed-only analogue of the pages'
+    end-to-end comparison).  Per-call HBM rates use algorithmic bytes: every
+    weight byte once per token, the cache's K and V rows once per token."""
+    import torch
+    from free_token_skipping_amd import capi, pipeline
+    sch = LLAMA_SCHEDULE
+    pts = pipeline.prune_points(sch["first_skip_layer"], sch["stage_ends"], sch["budgets"], sch["final_budget"])
+    n = x0.shape[0]
+    table = capi.spts_rope_table(n + 2 * tokens + 2, cfg.dh, cfg.theta, x0.device)
+    out = {}
+    for mode in ("dense", "spts"):
+        kvs = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        pipeline.prefill_schedule(x0, layers, cfg, sch["n_layers"], sch["first_skip_layer"], pts,
+                                  dense=(mode == "dense"), kv_out=kvs)
+        e1.record()
+        torch.cuda.synchronize()
+        prefill_ms = e0.elapsed_time(e1)
+        caches = pipeline.DecodeCaches(kvs, 2 * tokens + 2)
+        del kvs
+        x = x0[n - 1].clone()
+        pipeline.decode_step(x, n, layers, caches, cfg, table)                      # warm-up token
+        torch.cuda.synchronize()
+        e0.record()
+        w0 = time.perf_counter()
+        for t in range(tokens):
+            pipeline.decode_step(x, n + 1 + t, layers, caches, cfg, table)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w0) * 1e3 / tokens
+        tok_ms = e0.elapsed_time(e1) / tokens
+        tm = pipeline.CallTimer()
+        for t in range(tokens):
+            pipeline.decode_step(x, n + 1 + tokens + t, layers, caches, cfg, table, tm)
+        torch.cuda.synchronize()
+        calls = {}
+        for name, (c, ms, work) in tm.summary().items():
+            calls[name] = {"ms_per_token": round(ms / tokens, 4), "gb_per_s": round(work / (ms * 1e-3) / 1e9, 1)}
+        out[mode] = {"prefill_ms": round(prefill_ms, 2), "ms_per_token": round(tok_ms, 4),
+                     "wall_ms_per_token": round(wall, 4), "cache_rows_per_layer": caches.lengths[:1] + caches.lengths[-1:],
+                     "cache_gib": round(caches.nbytes() / 2 ** 30, 3), "calls": calls}
+        log(f"decode {mode}: prefill {prefill_ms:.1f} ms, {tok_ms:.3f} ms/token (wall {wall:.3f}), "
+            f"cache {caches.nbytes() / 2 ** 30:.2f} GiB")
+        del caches
+    e2e = []
+    for g in gen:
+        dm = out["dense"]["prefill_ms"] + g * out["dense"]["ms_per_token"]
+        sm = out["spts"]["prefill_ms"] + g * out["spts"]["ms_per_token"]
+        e2e.append({"generated": g, "dense_ms": round(dm, 1), "spts_ms": round(sm, 1), "ratio": round(dm / sm, 3)})
+    out["tokens_timed"] = tokens
+    out["prompt_tokens"] = n
+    out["end_to_end"] = e2e
+    return out
 
 
 # ------------------------------------------------- HBM-bound row kernels
@@ -446,6 +508,9 @@ def main():
     if not args.no_ttft:
         log("timing the 32-layer prefill schedule against dense")
         rec.setdefault("also", {})["prefill_32_layers"] = ttft_table(x0, layers, stack_cfg)
+    if not args.no_decode:
+        log("timing decode after the 32-layer prefill, SPTS against full caches")
+        rec.setdefault("also", {})["decode_32_layers"] = decode_table(x0, layers, stack_cfg)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(sh, st, n_layers, points, args.cpu_sample)

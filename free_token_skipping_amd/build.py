@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libspts.so")
-SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "select.hip", "rowops.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "select.hip", "rowops.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -25,6 +25,8 @@ EXPORTS = [
     "spts_probe_attention_workspace", "spts_score_topk_workspace", "spts_ltp_probe_workspace",
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
     "spts_ltp_structured_workspace", "spts_ltp_probe_structured",
+    "spts_decode_attention_workspace", "spts_decode_linear", "spts_decode_linear_rope", "spts_decode_swiglu",
+    "spts_decode_attention",
     "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_gather", "spts_scatter",
     "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
     "spts_linear", "spts_linear_rope", "spts_linear_kv", "spts_linear_swiglu", "spts_rope_table",
@@ -48,6 +50,11 @@ _SIGS = {
     "spts_msdp_stage_workspace": (_SZ, [_I]),
     "spts_linear_workspace": (_SZ, [_I, _I, _I]),
     "spts_ltp_structured_workspace": (_SZ, [_I, _I, _I, _I]),
+    "spts_decode_attention_workspace": (_SZ, [_I, _I]),
+    "spts_decode_linear": (_I, [_P, _P, _P, _I, _I, _P, _I]),
+    "spts_decode_linear_rope": (_I, [_P, _P, _P, _I, _I, _P, _I, _P]),
+    "spts_decode_swiglu": (_I, [_P, _P, _P, _P, _I, _I, _P]),
+    "spts_decode_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
     "spts_ltp_probe_structured": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
@@ -287,6 +294,59 @@ def spts_ltp_probe_structured(z, packed, score=None):
                                                 n, d, r, d_low, _ptr(score, torch.float32, "score")),
            "spts_ltp_probe_structured")
     return score
+
+
+def spts_decode_linear(x, w, out=None, accumulate=False):
+    """One token row x [kdim] through w [n, kdim]; accumulate adds into out (residual)."""
+    n, kdim = w.shape
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=x.device)
+    ctx = context()
+    h = ctx.bind(0, x.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_decode_linear(h, _ptr(x, bf, "x"), _ptr(w, bf, "w"), kdim, n, _ptr(out, bf, "out"),
+                                         int(bool(accumulate))), "spts_decode_linear")
+    return out
+
+
+def spts_decode_linear_rope(x, w, pos, table, out=None):
+    n, kdim = w.shape
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=x.device)
+    ctx = context()
+    h = ctx.bind(0, x.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_decode_linear_rope(h, _ptr(x, bf, "x"), _ptr(w, bf, "w"), kdim, n, _ptr(out, bf, "out"),
+                                              int(pos), _ptr(table, torch.float32, "table")), "spts_decode_linear_rope")
+    return out
+
+
+def spts_decode_swiglu(x, w_gate, w_up, out=None):
+    f, kdim = w_gate.shape
+    if out is None:
+        out = torch.empty(f, dtype=torch.bfloat16, device=x.device)
+    ctx = context()
+    h = ctx.bind(0, x.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_decode_swiglu(h, _ptr(x, bf, "x"), _ptr(w_gate, bf, "w_gate"), _ptr(w_up, bf, "w_up"),
+                                         kdim, f, _ptr(out, bf, "out")), "spts_decode_swiglu")
+    return out
+
+
+def spts_decode_attention(q, k_cache, v_cache, L, scale=None, o=None):
+    """q [Hq, dh] against the first L rows of k_cache, v_cache [cap, Hkv, dh]."""
+    Hq, dh = q.shape
+    Hkv = k_cache.shape[1]
+    scale = float(dh ** -0.5) if scale is None else float(scale)
+    if o is None:
+        o = torch.empty_like(q)
+    ctx = context()
+    h = ctx.bind(lib().spts_decode_attention_workspace(int(L), Hq), q.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_decode_attention(h, _ptr(q, bf, "q"), _ptr(k_cache, bf, "k_cache"),
+                                            _ptr(v_cache, bf, "v_cache"), int(L), Hq, Hkv, dh, scale,
+                                            _ptr(o, bf, "o")), "spts_decode_attention")
+    return o
 
 
 def spts_reduced_ffn(z, w_gate, w_up, w_down, rows=None, y=None, y_rows=None, accumulate=False):

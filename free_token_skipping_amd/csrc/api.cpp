@@ -494,6 +494,77 @@ spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* 
   return hip_status(ctx, launch_rowsum_sqrt(part, n, d / 256, score, ctx->stream), "ltp_probe_structured (norm)");
 }
 
+// --------------------------------------------------------------------- decode
+
+size_t spts_decode_attention_workspace(int L, int Hq) {
+  return (L > 0 && Hq > 0) ? round256(decode_attn_workspace(L, Hq)) : 0;
+}
+
+static spts_status gemv_shape_ok(spts_ctx* ctx, int kdim, int n) {
+  REQUIRE(kdim > 0 && n > 0, SPTS_ERR_SHAPE, "bad decode projection sizes kdim=%d n=%d", kdim, n);
+  REQUIRE(gemv_supported_k(kdim), SPTS_ERR_UNSUPPORTED, "decode projections need kdim %% 512 == 0, <= 16384 (got %d)",
+          kdim);
+  return SPTS_OK;
+}
+
+spts_status spts_decode_linear(spts_ctx* ctx, const void* x, const void* w, int kdim, int n, void* out,
+                               int accumulate) {
+  CHECK_CTX();
+  spts_status st = gemv_shape_ok(ctx, kdim, n);
+  if (st != SPTS_OK) return st;
+  REQUIRE(accumulate == 0 || accumulate == 1, SPTS_ERR_INVALID, "accumulate must be 0 or 1");
+  REQUIRE_PTR(x); REQUIRE_PTR(w); REQUIRE_PTR(out);
+  REQUIRE_ALIGN(x); REQUIRE_ALIGN(w);
+  return hip_status(ctx, launch_gemv(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
+                                     nullptr, kdim, n, reinterpret_cast<uint16_t*>(out), accumulate ? 3 : 0, 0,
+                                     nullptr, ctx->stream),
+                    "decode_linear");
+}
+
+spts_status spts_decode_linear_rope(spts_ctx* ctx, const void* x, const void* w, int kdim, int n, void* out,
+                                    int pos, const float* table) {
+  CHECK_CTX();
+  spts_status st = gemv_shape_ok(ctx, kdim, n);
+  if (st != SPTS_OK) return st;
+  REQUIRE(n % 128 == 0, SPTS_ERR_UNSUPPORTED, "decode RoPE needs 128-wide heads (n=%d)", n);
+  REQUIRE(pos >= 0, SPTS_ERR_SHAPE, "pos must be >= 0");
+  REQUIRE_PTR(x); REQUIRE_PTR(w); REQUIRE_PTR(out); REQUIRE_PTR(table);
+  REQUIRE_ALIGN(x); REQUIRE_ALIGN(w); REQUIRE_ALIGN(table);
+  return hip_status(ctx, launch_gemv(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
+                                     nullptr, kdim, n, reinterpret_cast<uint16_t*>(out), 1, pos, table, ctx->stream),
+                    "decode_linear_rope");
+}
+
+spts_status spts_decode_swiglu(spts_ctx* ctx, const void* x, const void* w_gate, const void* w_up, int kdim, int f,
+                               void* h_out) {
+  CHECK_CTX();
+  spts_status st = gemv_shape_ok(ctx, kdim, f);
+  if (st != SPTS_OK) return st;
+  REQUIRE_PTR(x); REQUIRE_PTR(w_gate); REQUIRE_PTR(w_up); REQUIRE_PTR(h_out);
+  REQUIRE_ALIGN(x); REQUIRE_ALIGN(w_gate); REQUIRE_ALIGN(w_up);
+  return hip_status(ctx, launch_gemv(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w_gate),
+                                     reinterpret_cast<const uint16_t*>(w_up), kdim, f,
+                                     reinterpret_cast<uint16_t*>(h_out), 2, 0, nullptr, ctx->stream),
+                    "decode_swiglu");
+}
+
+spts_status spts_decode_attention(spts_ctx* ctx, const void* q, const void* k_cache, const void* v_cache, int L,
+                                  int Hq, int Hkv, int dh, float scale, void* o) {
+  CHECK_CTX();
+  REQUIRE(L > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, SPTS_ERR_SHAPE, "bad decode attention sizes");
+  REQUIRE(dh == 128 && Hq / Hkv == 4, SPTS_ERR_UNSUPPORTED, "decode attention needs dh == 128 and Hq/Hkv == 4");
+  REQUIRE((long)L * Hkv * dh < (1L << 40), SPTS_ERR_UNSUPPORTED, "cache too large");
+  REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(o);
+  REQUIRE_ALIGN(q); REQUIRE_ALIGN(k_cache); REQUIRE_ALIGN(v_cache);
+  const size_t need = spts_decode_attention_workspace(L, Hq);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  return hip_status(ctx, launch_decode_attn(reinterpret_cast<const uint16_t*>(q),
+                                            reinterpret_cast<const uint16_t*>(k_cache),
+                                            reinterpret_cast<const uint16_t*>(v_cache), L, Hq, Hkv, scale,
+                                            reinterpret_cast<uint16_t*>(o), ctx->ws, ctx->stream),
+                    "decode_attention");
+}
+
 // ------------------------------------------------------------------------ FFN
 
 spts_status spts_reduced_ffn(spts_ctx* ctx, const void* z, const int32_t* rows, const void* w_gate,

@@ -73,6 +73,16 @@ size_t topk_workspace(int n);
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
                        int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s);
 
+// -------------------------------------------------------------- decode
+// y = x W^T for one row x [K]; epi 0 store, 1 RoPE at pos (pairs c, c+64 of
+// 128-wide heads), 2 SwiGLU (w = gate, w2 = up), 3 residual add into out.
+bool gemv_supported_k(int K);
+hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint16_t* w2, int K, int N, uint16_t* out,
+                       int epi, int pos, const float* table, hipStream_t s);
+size_t decode_attn_workspace(int L, int Hq);
+hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int L, int Hq, int Hkv,
+                              float scale, uint16_t* o, void* ws, hipStream_t s);
+
 // ------------------------------------------------------------- row ops
 hipError_t launch_gather(const void* src, const int32_t* idx, int k, long row_bytes, void* dst,
                          hipStream_t s);

@@ -106,7 +106,7 @@ def _attn_flops(idx, Hq, dh):
 
 
 def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_table=None,
-                    k_given=None, prune_to=None, fused=True, trace=None, tm=NO_TIMER):
+                    k_given=None, prune_to=None, fused=True, trace=None, tm=NO_TIMER, kv_out=None):
     """x [n, d] bf16 residual (updated in place unless pruned), pos [n] int32.
 
     Returns (x_out, pos_out, S) where x_out/pos_out are the (possibly pruned)
@@ -157,6 +157,8 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
         n = prune_to
         if trace is not None:
             trace.update(keep=keep)
+    if kv_out is not None:
+        kv_out.append((K, V))             # this layer's cache: its candidates' keys and values
     # a4: select the attention rows
     k_a = keep_count(cfg.keep_attn, n)
     with tm("select_attn", 4.0 * n + 4.0 * k_a):
@@ -237,9 +239,9 @@ def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None, tm=NO_TIMER):
 
 
 def spts_layer(x, pos, w, cfg: LayerConfig, rope_table=None, k_given=None, prune_to=None, fused=True,
-               trace=None, tm=NO_TIMER):
+               trace=None, tm=NO_TIMER, kv_out=None):
     """Attention block then (if cfg.keep_ffn is set) FFN block."""
-    x, pos, S = attention_block(x, pos, w, cfg, rope_table, k_given, prune_to, fused, trace, tm)
+    x, pos, S = attention_block(x, pos, w, cfg, rope_table, k_given, prune_to, fused, trace, tm, kv_out)
     if cfg.keep_ffn is not None:
         x = ffn_block(x, S, w, cfg, fused, trace, tm)
     return x, pos
@@ -254,7 +256,7 @@ def prune_points(first_skip_layer, stage_end_layers, budgets, final_budget=None)
     return pts
 
 
-def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER):
+def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER, kv_out=None):
     """The same decoder layer with every row computed: no probes, no
     selection.  This is the dense-prefill baseline that SPTS is compared
     against ([SPTS] Table 4 compares TTFT against the full model).  x [n, d]
@@ -272,6 +274,8 @@ def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER):
         K, V = capi.spts_linear_kv(xt, w["wk"], w["wv"], pos if rope else None, rope_table if rope else None)
     with tm("q_proj", 2.0 * n * d * Hq * dh):
         Q = (capi.spts_linear_rope(xt, w["wq"], pos, rope_table) if rope else capi.spts_linear(xt, w["wq"]))
+    if kv_out is not None:
+        kv_out.append((K.view(n, Hkv, dh), V.view(n, Hkv, dh)))
     idx = torch.arange(n, dtype=torch.int32, device=x.device)
     with tm("attention", _attn_flops(idx, Hq, dh)):
         O = capi.spts_reduced_attention(Q.view(n, Hq, dh), idx, K.view(n, Hkv, dh), V.view(n, Hkv, dh))
@@ -292,7 +296,7 @@ def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER):
 
 
 def prefill_schedule(x0, layers, cfg: LayerConfig, n_layers, first_skip_layer, points, dense=False,
-                     tm=NO_TIMER):
+                     tm=NO_TIMER, kv_out=None):
     """Prefill of an n_layers model: layers before first_skip_layer are dense,
     the rest are SPTS layers pruned at `points` ([SPTS] Table B gives such a
     schedule per model).  dense=True runs every layer dense (the full-model
@@ -305,12 +309,69 @@ def prefill_schedule(x0, layers, cfg: LayerConfig, n_layers, first_skip_layer, p
     for li in range(n_layers):
         w = layers[li % len(layers)]
         if dense or li < first_skip_layer:
-            x = dense_layer(x, pos, w, cfg, table, tm=tm)
+            x = dense_layer(x, pos, w, cfg, table, tm=tm, kv_out=kv_out)
         else:
             budget = points.get(li)
             prune = budget if budget is not None and budget < x.shape[0] else None
-            x, pos = spts_layer(x, pos, w, cfg, table, prune_to=prune, tm=tm)
+            x, pos = spts_layer(x, pos, w, cfg, table, prune_to=prune, tm=tm, kv_out=kv_out)
     return x, pos
+
+
+# ------------------------------------------------------------------- decode
+
+class DecodeCaches:
+    """Per-layer K/V caches for the decode phase: [capacity, Hkv, dh] bf16
+    each, the first `lengths[l]` rows filled.  A prefill's (K, V) per layer
+    (its candidates; [SPTS] Table 5) is copied in once, with room for
+    `extra` generated tokens."""
+
+    def __init__(self, kvs, extra):
+        self.k, self.v, self.lengths = [], [], []
+        for K, V in kvs:
+            n = K.shape[0]
+            kc = torch.empty((n + extra,) + tuple(K.shape[1:]), dtype=K.dtype, device=K.device)
+            vc = torch.empty_like(kc)
+            kc[:n].copy_(K)
+            vc[:n].copy_(V)
+            self.k.append(kc)
+            self.v.append(vc)
+            self.lengths.append(n)
+
+    def nbytes(self):
+        return sum(2 * l * k[0].numel() * k.element_size() for l, k in zip(self.lengths, self.k))
+
+
+def decode_step(x, pos, layers, caches: DecodeCaches, cfg: LayerConfig, rope_table, tm=NO_TIMER):
+    """One new token (residual row x [d] bf16, updated in place) at original
+    position pos through every layer; layer l's K/V row is written into its
+    cache and its query attends to every cached row.  Layer l uses weights
+    layers[l % len(layers)]."""
+    Hq, Hkv, dh = cfg.Hq, cfg.Hkv, cfg.dh
+    d = x.shape[0]
+    rope = cfg.theta is not None
+    for li in range(len(caches.k)):
+        w = layers[li % len(layers)]
+        L = caches.lengths[li]
+        xt = capi.spts_rmsnorm(x.view(1, d), cfg.eps).view(d) if cfg.prenorm else x
+        with tm("dec_qkv", 2.0 * d * (Hq + 2 * Hkv) * dh):        # weight bytes read
+            if rope:
+                q = capi.spts_decode_linear_rope(xt, w["wq"], pos, rope_table)
+                capi.spts_decode_linear_rope(xt, w["wk"], pos, rope_table, out=caches.k[li][L].view(-1))
+            else:
+                q = capi.spts_decode_linear(xt, w["wq"])
+                capi.spts_decode_linear(xt, w["wk"], out=caches.k[li][L].view(-1))
+            capi.spts_decode_linear(xt, w["wv"], out=caches.v[li][L].view(-1))
+        caches.lengths[li] = L + 1
+        with tm("dec_attention", 2.0 * 2 * (L + 1) * Hkv * dh):   # cache bytes read (K and V)
+            o = capi.spts_decode_attention(q.view(Hq, dh), caches.k[li], caches.v[li], L + 1)
+        with tm("dec_o_proj", 2.0 * Hq * dh * d):
+            capi.spts_decode_linear(o.view(-1), w["wo"], out=x, accumulate=True)
+        z = capi.spts_rmsnorm(x.view(1, d), cfg.eps).view(d) if cfg.prenorm else x
+        f = w["wg"].shape[0]
+        with tm("dec_ffn", 2.0 * 3 * d * f):
+            h = capi.spts_decode_swiglu(z, w["wg"], w["wu"])
+            capi.spts_decode_linear(h, w["wd"], out=x, accumulate=True)
+    return x
 
 
 def msdp_stack(x0, layers, cfg: LayerConfig, points, fused=True, traces=None, tm=NO_TIMER):

@@ -79,6 +79,7 @@ size_t spts_probe_attention_workspace(int n, int P, int Hq);
 size_t spts_score_topk_workspace(int n);
 size_t spts_ltp_probe_workspace(int n, int d, int r);
 size_t spts_ltp_structured_workspace(int n, int d, int r, int d_low);
+size_t spts_decode_attention_workspace(int L, int Hq);
 size_t spts_reduced_ffn_workspace(int k, int f);
 size_t spts_msdp_stage_workspace(int n_prev);
 /* Workspace with which spts_linear / spts_linear_rope split the inner
@@ -254,6 +255,37 @@ spts_status spts_linear_kv(spts_ctx* ctx, const void* a, const int32_t* a_rows, 
  * Requires kdim % 64 == 0, f % 128 == 0.  ([SPTS] Fig. 2(b), reduced feed-forward.) */
 spts_status spts_linear_swiglu(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
                                const void* w_gate, const void* w_up, int f, void* h_out);
+
+/* ------------------------------------------------------------------ decode */
+
+/* Decode phase: one new token per step through every layer.  With MSDP each
+ * layer keeps the K/V of its candidates only ([SPTS] Table 5, Fig. A(c)), so
+ * the new token attends to that layer's cache.  One token row x [kdim] bf16.
+ * Projections (HBM-bound matrix-vector products, fp32 accumulate):
+ *   spts_decode_linear:      out[c] = bf16(x . w[c,:]); accumulate == 1:
+ *                            out[c] = bf16(out[c] + bf16(x . w[c,:]))  (residual add)
+ *   spts_decode_linear_rope: as store, then RoPE at position pos on 128-wide
+ *                            heads (pairs c, c+64); table from spts_rope_table
+ *                            must hold row pos (the caller sizes it to the
+ *                            prompt plus every generated token)
+ *   spts_decode_swiglu:      h[c] = bf16(silu(x . w_gate[c,:]) * (x . w_up[c,:]))
+ *   w [n, kdim] bf16; out [n] bf16.  Requires kdim % 512 == 0, kdim <= 16384;
+ *   x and w 16-byte aligned.  Errors: SPTS_ERR_INVALID (null pointer, bad
+ *   flag), SPTS_ERR_SHAPE, SPTS_ERR_UNSUPPORTED, SPTS_ERR_ALIGN. */
+spts_status spts_decode_linear(spts_ctx* ctx, const void* x, const void* w, int kdim, int n, void* out,
+                               int accumulate);
+spts_status spts_decode_linear_rope(spts_ctx* ctx, const void* x, const void* w, int kdim, int n,
+                                    void* out, int pos, const float* table);
+spts_status spts_decode_swiglu(spts_ctx* ctx, const void* x, const void* w_gate, const void* w_up,
+                               int kdim, int f, void* h_out);
+/* One query row against a layer's cache, every cached row visible:
+ *   o[h] = sum_j softmax_j(scale * q[h] . k_cache[j, g]) v_cache[j, g],  g = h / (Hq/Hkv),
+ *   j < L.  q [Hq, 128], k_cache, v_cache [>= L, Hkv, 128], o [Hq, 128], bf16.
+ * Split over 256-key chunks, merged in chunk order.  Requires dh == 128,
+ * Hq/Hkv == 4.  Workspace: spts_decode_attention_workspace(L, Hq). */
+spts_status spts_decode_attention(spts_ctx* ctx, const void* q, const void* k_cache,
+                                  const void* v_cache, int L, int Hq, int Hkv, int dh, float scale,
+                                  void* o);
 
 /* table[p, c, 0..1] = (cos, sin)(p * theta^(-2c/dh)) for p < max_pos, c < dh/2,
  * angle formed in fp64 and rounded to fp32. */

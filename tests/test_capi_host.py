@@ -132,6 +132,29 @@ def test_attention_and_rows_validation(L, ctx):
     assert L.spts_scatter(ctx, capi.BF16, FAKE, MIS, 4, 8, FAKE, 1) == ALIGN
 
 
+def test_decode_validation(L, ctx):
+    assert L.spts_decode_linear(ctx, FAKE, FAKE, 4000, 64, FAKE, 0) == UNSUPPORTED        # kdim % 512
+    assert L.spts_decode_linear(ctx, FAKE, FAKE, 32768, 64, FAKE, 0) == UNSUPPORTED       # kdim > 16384
+    assert L.spts_decode_linear(ctx, FAKE, FAKE, 4096, 0, FAKE, 0) == SHAPE
+    assert L.spts_decode_linear(ctx, FAKE, FAKE, 4096, 64, FAKE, 2) == INVALID
+    assert L.spts_decode_linear(ctx, None, FAKE, 4096, 64, FAKE, 0) == INVALID
+    assert L.spts_decode_linear(ctx, MIS, FAKE, 4096, 64, FAKE, 0) == ALIGN
+    r = L.spts_decode_linear_rope
+    assert r(ctx, FAKE, FAKE, 4096, 192, FAKE, 3, FAKE) == UNSUPPORTED                    # 128-wide heads
+    assert r(ctx, FAKE, FAKE, 4096, 256, FAKE, -1, FAKE) == SHAPE
+    assert r(ctx, FAKE, FAKE, 4096, 256, FAKE, 3, None) == INVALID
+    assert L.spts_decode_swiglu(ctx, FAKE, None, FAKE, 4096, 256, FAKE) == INVALID
+    assert L.spts_decode_swiglu(ctx, FAKE, FAKE, MIS, 4096, 256, FAKE) == ALIGN
+    a = L.spts_decode_attention
+    assert a(ctx, FAKE, FAKE, FAKE, 0, 32, 8, 128, 0.1, FAKE) == SHAPE                    # empty cache
+    assert a(ctx, FAKE, FAKE, FAKE, 10, 32, 16, 128, 0.1, FAKE) == UNSUPPORTED            # group of 2
+    assert a(ctx, FAKE, FAKE, FAKE, 10, 32, 8, 64, 0.1, FAKE) == UNSUPPORTED
+    assert a(ctx, FAKE, FAKE, FAKE, 10, 32, 8, 128, 0.1, FAKE) == NOMEM                   # no workspace
+    assert L.spts_decode_attention_workspace(32768, 32) >= 128 * 32 * 130 * 4
+    L.spts_set_workspace(ctx, FAKE, 1 << 20)
+    assert a(ctx, FAKE, MIS, FAKE, 10, 32, 8, 128, 0.1, FAKE) == ALIGN
+
+
 def test_product_path_has_no_cpu_fallback():
     """The binding refuses CPU tensors instead of computing on the host."""
     import torch

@@ -310,6 +310,27 @@ def test_structured_proxy_generator_full_rank():
         assert np.abs(rec - ref).max() <= 1e-2 * np.abs(ref).max()
 
 
+def test_decode_of_token_n_is_row_n_of_dense_prefill():
+    # two pre-norm RoPE layers, every token cached: decoding token N from the
+    # N-token caches reproduces row N of a dense prefill over N + 1 tokens
+    from oracle import decode
+    sh = workloads.LayerShape(n=97, d=256, Hq=8, Hkv=2, dh=32, f=384, r=32, P=4)
+    st = workloads.make_stack(sh, 2, seed=21)
+    cfg = dict(Hq=8, Hkv=2, dh=32, P=4, keep_attn=1.0, keep_ffn=1.0, prenorm=True, eps=1e-5, theta=10000.0)
+    ws = [{k: workloads.as_f64(v) for k, v in w.items() if hasattr(v, "numpy")} for w in st["layers"]]
+    X = workloads.as_f64(st["x"])
+    N = sh.n - 1
+    full, pre = X, X[:N]
+    caches = []
+    for w in ws:
+        full, _, _ = layer.spts_layer(full, np.arange(N + 1), w, cfg)
+        pre, sa, _ = layer.spts_layer(pre, np.arange(N), w, cfg)
+        caches.append([sa["K"], sa["V"]])
+    out = decode.decode_step(X[N], N, caches, ws, cfg)
+    assert np.allclose(out, full[N], rtol=0, atol=1e-9 * np.abs(full[N]).max())
+    assert caches[0][0].shape == (N + 1, 2, 32) and caches[1][1].shape == (N + 1, 2, 32)
+
+
 # ------------------------------------------------------------------------- FFN
 
 def test_swiglu_against_torch():
