@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-ttft", action="store_true", help="skip the 32-layer prefill schedule vs dense table")
     ap.add_argument("--no-hbm", action="store_true", help="skip the cold/warm gather and scatter-add table")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode / end-to-end table")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode table (prefill + decode at 32K), printed as one JSON line")
     ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
     ap.add_argument("--cpu-sample", type=float, default=1.0 / 32,
                     help="fraction of row-separable oracle work timed for the CPU baseline")
@@ -206,50 +208,54 @@ def decode_table(x0, layers, cfg, tokens=16, gen=(32, 128, 512)):
     each layer's cache holding its candidates (SPTS, [SPTS] Table 5) against
     full caches (dense prefill), and end-to-end time for G generated tokens
     = prefill + G * per-token time (a speed-only analogue of the pages'
-    end-to-end comparison).  Per-call HBM rates use algorithmic bytes: every
-    weight byte once per token, the cache's K and V rows once per token."""
+    end-to-end comparison).  A step is one spts_decode_step call (all 32
+    layers); the per-call composition is timed beside it.  HBM rate: the
+    algorithmic bytes of a token (every weight byte once, every cached K and
+    V row once) over its time."""
     import torch
     from free_token_skipping_amd import capi, pipeline
     sch = LLAMA_SCHEDULE
     pts = pipeline.prune_points(sch["first_skip_layer"], sch["stage_ends"], sch["budgets"], sch["final_budget"])
     n = x0.shape[0]
-    table = capi.spts_rope_table(n + 2 * tokens + 2, cfg.dh, cfg.theta, x0.device)
+    nl = sch["n_layers"]
+    table = capi.spts_rope_table(n + 3 * tokens + 2, cfg.dh, cfg.theta, x0.device)
+    wbytes = sum(layers[l % len(layers)][k].numel() * 2 for l in range(nl)
+                 for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"))
     out = {}
-    for mode in ("dense", "spts"):
-        kvs = []
+
+    def clock(fn, count):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        w0 = time.perf_counter()
         e0.record()
-        pipeline.prefill_schedule(x0, layers, cfg, sch["n_layers"], sch["first_skip_layer"], pts,
-                                  dense=(mode == "dense"), kv_out=kvs)
+        for t in range(count):
+            fn(t)
         e1.record()
         torch.cuda.synchronize()
-        prefill_ms = e0.elapsed_time(e1)
-        caches = pipeline.DecodeCaches(kvs, 2 * tokens + 2)
+        return e0.elapsed_time(e1) / count, (time.perf_counter() - w0) * 1e3 / count
+
+    for mode in ("dense", "spts"):
+        kvs = []
+        prefill_ms, _ = clock(lambda t: pipeline.prefill_schedule(
+            x0, layers, cfg, nl, sch["first_skip_layer"], pts, dense=(mode == "dense"), kv_out=kvs), 1)
+        caches = pipeline.DecodeCaches(kvs, 3 * tokens + 2)
         del kvs
         x = x0[n - 1].clone()
-        pipeline.decode_step(x, n, layers, caches, cfg, table)                      # warm-up token
-        torch.cuda.synchronize()
-        e0.record()
-        w0 = time.perf_counter()
-        for t in range(tokens):
-            pipeline.decode_step(x, n + 1 + t, layers, caches, cfg, table)
-        e1.record()
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - w0) * 1e3 / tokens
-        tok_ms = e0.elapsed_time(e1) / tokens
-        tm = pipeline.CallTimer()
-        for t in range(tokens):
-            pipeline.decode_step(x, n + 1 + tokens + t, layers, caches, cfg, table, tm)
-        torch.cuda.synchronize()
-        calls = {}
-        for name, (c, ms, work) in tm.summary().items():
-            calls[name] = {"ms_per_token": round(ms / tokens, 4), "gb_per_s": round(work / (ms * 1e-3) / 1e9, 1)}
+        pipeline.decode_step_native(x, n, layers, caches, cfg, table)                # warm-up token
+        len0 = list(caches.lengths)
+        tok_ms, wall = clock(lambda t: pipeline.decode_step_native(x, n + 1 + t, layers, caches, cfg, table), tokens)
+        cache_read = sum(2 * (l0 + t + 1) * cfg.Hkv * cfg.dh * 2 for l0 in len0 for t in range(tokens)) / tokens
+        per_call_ms, _ = clock(lambda t: pipeline.decode_step(x, n + 1 + tokens + t, layers, caches, cfg, table),
+                               tokens)
+        gbs = (wbytes + cache_read) / (tok_ms * 1e-3) / 1e9
         out[mode] = {"prefill_ms": round(prefill_ms, 2), "ms_per_token": round(tok_ms, 4),
-                     "wall_ms_per_token": round(wall, 4), "cache_rows_per_layer": caches.lengths[:1] + caches.lengths[-1:],
-                     "cache_gib": round(caches.nbytes() / 2 ** 30, 3), "calls": calls}
-        log(f"decode {mode}: prefill {prefill_ms:.1f} ms, {tok_ms:.3f} ms/token (wall {wall:.3f}), "
-            f"cache {caches.nbytes() / 2 ** 30:.2f} GiB")
+                     "wall_ms_per_token": round(wall, 4), "per_call_ms_per_token": round(per_call_ms, 4),
+                     "bytes_per_token": int(wbytes + cache_read), "hbm_gb_per_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / 8000.0, 4),
+                     "cache_rows_first_last_layer": [len0[0], len0[-1]],
+                     "cache_gib": round(caches.nbytes() / 2 ** 30, 3)}
+        log(f"decode {mode}: prefill {prefill_ms:.1f} ms, {tok_ms:.3f} ms/token (wall {wall:.3f}, per-call "
+            f"composition {per_call_ms:.3f}), {gbs:,.0f} GB/s, cache {caches.nbytes() / 2 ** 30:.2f} GiB")
         del caches
     e2e = []
     for g in gen:
@@ -258,6 +264,7 @@ def decode_table(x0, layers, cfg, tokens=16, gen=(32, 128, 512)):
         e2e.append({"generated": g, "dense_ms": round(dm, 1), "spts_ms": round(sm, 1), "ratio": round(dm / sm, 3)})
     out["tokens_timed"] = tokens
     out["prompt_tokens"] = n
+    out["weights"] = f"{len(layers)} generated layers cycled over {nl}; {wbytes / 1e9:.2f} GB read per token"
     out["end_to_end"] = e2e
     return out
 
@@ -419,6 +426,12 @@ def main():
 
     cfgd, sh, st, x0, layers = stack_inputs(dev)
     N = sh.n
+    if args.decode_only:
+        cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=cfgd["keep_attn"],
+                          keep_ffn=cfgd["keep_ffn"], w_fuse=cfgd["w_fuse"], prenorm=True, eps=cfgd["eps"],
+                          theta=cfgd["theta"])
+        print(json.dumps({"decode_32_layers": decode_table(x0, layers, cfg)}), flush=True)
+        return
     budgets = [keep_count(r, N) for r in cfgd["budget_ratios"]]
     points = pipeline.prune_points(0, cfgd["stage_ends"], budgets)
     stack_cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=cfgd["keep_attn"],

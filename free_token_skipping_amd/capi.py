@@ -26,7 +26,7 @@ EXPORTS = [
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
     "spts_ltp_structured_workspace", "spts_ltp_probe_structured",
     "spts_decode_attention_workspace", "spts_decode_linear", "spts_decode_linear_rope", "spts_decode_swiglu",
-    "spts_decode_attention",
+    "spts_decode_attention", "spts_decode_step_workspace", "spts_decode_step",
     "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_gather", "spts_scatter",
     "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
     "spts_linear", "spts_linear_rope", "spts_linear_kv", "spts_linear_swiglu", "spts_rope_table",
@@ -55,6 +55,8 @@ _SIGS = {
     "spts_decode_linear_rope": (_I, [_P, _P, _P, _I, _I, _P, _I, _P]),
     "spts_decode_swiglu": (_I, [_P, _P, _P, _P, _I, _I, _P]),
     "spts_decode_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "spts_decode_step_workspace": (_SZ, [_I, _I, _I]),
+    "spts_decode_step": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _I, _F]),
     "spts_ltp_probe_structured": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
@@ -331,6 +333,50 @@ def spts_decode_swiglu(x, w_gate, w_up, out=None):
     _check(ctx, lib().spts_decode_swiglu(h, _ptr(x, bf, "x"), _ptr(w_gate, bf, "w_gate"), _ptr(w_up, bf, "w_up"),
                                          kdim, f, _ptr(out, bf, "out")), "spts_decode_swiglu")
     return out
+
+
+class DecodeLayer(ctypes.Structure):
+    """struct spts_decode_layer: one layer's weight and cache pointers."""
+    _fields_ = [("wq", _P), ("wk", _P), ("wv", _P), ("wo", _P), ("w_gate", _P), ("w_up", _P), ("w_down", _P),
+                ("k_cache", _P), ("v_cache", _P), ("cap", _I)]
+
+
+def decode_layer_table(weights, k_caches, v_caches):
+    """ctypes array of spts_decode_layer for layer l = 0 .. len(k_caches)-1,
+    layer l taking weights[l % len(weights)] (dicts of bf16 GPU tensors
+    wq, wk, wv, wo, wg, wu, wd) and caches [cap, Hkv, dh] bf16."""
+    bf = torch.bfloat16
+    arr = (DecodeLayer * len(k_caches))()
+    for l, (kc, vc) in enumerate(zip(k_caches, v_caches)):
+        w = weights[l % len(weights)]
+        if kc.shape != vc.shape:
+            raise ValueError("k and v caches differ in shape")
+        arr[l] = DecodeLayer(_ptr(w["wq"], bf, "wq"), _ptr(w["wk"], bf, "wk"), _ptr(w["wv"], bf, "wv"),
+                             _ptr(w["wo"], bf, "wo"), _ptr(w["wg"], bf, "wg"), _ptr(w["wu"], bf, "wu"),
+                             _ptr(w["wd"], bf, "wd"), _ptr(kc, bf, "k_cache"), _ptr(vc, bf, "v_cache"),
+                             int(kc.shape[0]))
+    return arr
+
+
+def spts_decode_step(x, pos, layer_table, lengths, Hq, Hkv, dh, f, eps, prenorm, rope_table=None, scale=None):
+    """One whole decode step in one library call: x [d] bf16 (updated in place)
+    through every layer of layer_table (decode_layer_table); lengths is a
+    Python list of per-layer cache lengths, incremented on success."""
+    d = x.shape[0]
+    n = len(layer_table)
+    if len(lengths) != n:
+        raise ValueError("one cache length per layer")
+    scale = float(dh ** -0.5) if scale is None else float(scale)
+    lens = (ctypes.c_int * n)(*lengths)
+    ctx = context()
+    h = ctx.bind(lib().spts_decode_step_workspace(max(lengths) + 1 if n else 1, Hq, f), x.device)
+    table_rows = rope_table.shape[0] if rope_table is not None else 0
+    _check(ctx, lib().spts_decode_step(h, _ptr(x, torch.bfloat16, "x"), d, int(pos), layer_table, n, lens, Hq, Hkv,
+                                       dh, f, float(eps), int(bool(prenorm)),
+                                       _ptr(rope_table, torch.float32, "rope_table"), table_rows, scale),
+           "spts_decode_step")
+    lengths[:] = list(lens)
+    return x
 
 
 def spts_decode_attention(q, k_cache, v_cache, L, scale=None, o=None):

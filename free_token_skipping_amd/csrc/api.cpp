@@ -565,6 +565,60 @@ spts_status spts_decode_attention(spts_ctx* ctx, const void* q, const void* k_ca
                     "decode_attention");
 }
 
+size_t spts_decode_step_workspace(int max_len, int Hq, int f) {
+  return (max_len > 0 && Hq > 0 && f > 0) ? round256(decode_layer_workspace(max_len, Hq, f)) : 0;
+}
+
+spts_status spts_decode_step(spts_ctx* ctx, void* x, int d, int pos, const spts_decode_layer* layers, int n_layers,
+                             int* lengths, int Hq, int Hkv, int dh, int f, float eps, int prenorm,
+                             const float* rope_table, int table_rows, float scale) {
+  CHECK_CTX();
+  REQUIRE(n_layers >= 0 && d > 0 && f > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, SPTS_ERR_SHAPE,
+          "bad decode step sizes");
+  REQUIRE(dh == 128 && Hq / Hkv == 4, SPTS_ERR_UNSUPPORTED, "decode step needs dh == 128 and Hq/Hkv == 4");
+  REQUIRE(gemv_supported_k(d) && gemv_supported_k(f) && gemv_supported_k(Hq * dh), SPTS_ERR_UNSUPPORTED,
+          "decode step needs d, f and Hq*dh multiples of 512, at most 16384 (d=%d f=%d)", d, f);
+  REQUIRE(prenorm == 0 || prenorm == 1, SPTS_ERR_INVALID, "prenorm must be 0 or 1");
+  REQUIRE(pos >= 0, SPTS_ERR_SHAPE, "pos must be >= 0");
+  REQUIRE(rope_table == nullptr || pos < table_rows, SPTS_ERR_SHAPE, "RoPE table has %d rows, pos %d", table_rows,
+          pos);
+  REQUIRE_PTR(x);
+  REQUIRE_ALIGN(x);
+  if (n_layers == 0) return SPTS_OK;
+  REQUIRE_PTR(layers);
+  REQUIRE_PTR(lengths);
+  int max_len = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const spts_decode_layer& Ly = layers[l];
+    REQUIRE(Ly.wq && Ly.wk && Ly.wv && Ly.wo && Ly.w_gate && Ly.w_up && Ly.w_down && Ly.k_cache && Ly.v_cache,
+            SPTS_ERR_INVALID, "layer %d: NULL weight or cache pointer", l);
+    REQUIRE(aligned16(Ly.wq) && aligned16(Ly.wk) && aligned16(Ly.wv) && aligned16(Ly.wo) && aligned16(Ly.w_gate) &&
+                aligned16(Ly.w_up) && aligned16(Ly.w_down) && aligned16(Ly.k_cache) && aligned16(Ly.v_cache),
+            SPTS_ERR_ALIGN, "layer %d: weight or cache pointer not 16-byte aligned", l);
+    REQUIRE(lengths[l] >= 0 && lengths[l] < Ly.cap, SPTS_ERR_SHAPE, "layer %d: cache holds %d of %d rows", l,
+            lengths[l], Ly.cap);
+    REQUIRE((long)Ly.cap * Hkv * dh < (1L << 40), SPTS_ERR_UNSUPPORTED, "layer %d: cache too large", l);
+    max_len = lengths[l] + 1 > max_len ? lengths[l] + 1 : max_len;
+  }
+  const size_t need = spts_decode_step_workspace(max_len, Hq, f);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  for (int l = 0; l < n_layers; ++l) {
+    const spts_decode_layer& Ly = layers[l];
+    DecodeLayerPtrs w{reinterpret_cast<const uint16_t*>(Ly.wq), reinterpret_cast<const uint16_t*>(Ly.wk),
+                      reinterpret_cast<const uint16_t*>(Ly.wv), reinterpret_cast<const uint16_t*>(Ly.wo),
+                      reinterpret_cast<const uint16_t*>(Ly.w_gate), reinterpret_cast<const uint16_t*>(Ly.w_up),
+                      reinterpret_cast<const uint16_t*>(Ly.w_down), reinterpret_cast<uint16_t*>(Ly.k_cache),
+                      reinterpret_cast<uint16_t*>(Ly.v_cache)};
+    const spts_status st = hip_status(ctx, launch_decode_layer(reinterpret_cast<uint16_t*>(x), d, pos, w, lengths[l],
+                                                               Hq, Hkv, f, eps, prenorm == 1, rope_table, scale,
+                                                               ctx->ws, ctx->stream),
+                                      "decode_step");
+    if (st != SPTS_OK) return st;
+  }
+  for (int l = 0; l < n_layers; ++l) lengths[l] += 1;
+  return SPTS_OK;
+}
+
 // ------------------------------------------------------------------------ FFN
 
 spts_status spts_reduced_ffn(spts_ctx* ctx, const void* z, const int32_t* rows, const void* w_gate,

@@ -31,6 +31,22 @@ __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// RMSNorm pieces shared by every kernel that normalises a row, so that they all
+// produce the same bf16 values: sum of squares of 8 bf16 values added to ss in
+// a fixed order, and 1/sqrt(mean + eps) from a 256-thread block's four wave sums.
+__device__ __forceinline__ float sumsq8(const u32x4& v, float ss) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a = lo_bf(v[w]), b = hi_bf(v[w]);
+    ss += a * a + b * b;
+  }
+  return ss;
+}
+__device__ __forceinline__ float rms_inv(const float* red, int d, float eps) {
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  return 1.0f / sqrtf(tot / (float)d + eps);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

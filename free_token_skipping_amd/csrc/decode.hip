@@ -6,34 +6,65 @@
 // query against the layer's cached keys and values (HBM-bound on the cache).
 //
 // gemv_kernel: y[c] = sum_k x[k] W[c, k], bf16 in, fp32 accumulate.  One wave
-// per output (a pair of outputs for RoPE, a gate/up pair for SwiGLU); its 64
-// lanes stream the weight row 16 bytes at a time, 8 loads in flight per lane,
-// against x staged once per workgroup in LDS.
+// per work item (one output; a pair of outputs c, c + 64 of a 128-wide head
+// for RoPE; a gate/up pair for SwiGLU); its 64 lanes stream the weight rows
+// 16 bytes at a time, 8 loads in flight per lane, against x staged once per
+// workgroup in LDS.  With NORM the staged row is RMS-normalised first, with
+// the same per-thread order as the RMSNorm kernel (identical bf16 values), so
+// a layer needs no separate normalisation launch.  The QKV epilogue takes the
+// three projections of a layer in one launch and writes K and V straight
+// into the cache row of the new token.
 //
 // decode_attention: split over the cached keys.  Workgroup (chunk, KV head)
-// scores its 256 keys against the G query heads of the group, keeps the
-// chunk's softmax max, sum and unnormalised output per head; a combine kernel
-// merges the chunks in chunk order (log-sum-exp), so the result does not
-// depend on scheduling.
+// scores its chunk of keys against the 4 query heads of the group and keeps
+// the chunk's softmax max, sum and unnormalised output per head; a combine
+// kernel merges the chunks (log-sum-exp) in a fixed order, so the result
+// does not depend on scheduling.  A workgroup streams its chunk in 64-key
+// tiles with the next tile's loads in flight and no barrier in the loop; the
+// chunk is sized so that the grid has about two workgroups per compute unit.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace spts {
 namespace {
 
-constexpr int GV_WAVES = 4;        // waves per workgroup
+constexpr int GV_WAVES = 4;        // waves per workgroup (256 threads, as the RMSNorm kernel)
 constexpr int GV_MAXK = 16384;     // largest inner dimension (x staged in LDS, 32 KiB)
 constexpr int GV_BATCH = 8;        // 16-byte weight loads in flight per lane and row
 
-// one weight row against x (in LDS): lane l takes bytes [16 l, 16 l + 16) of
-// every 1 KiB step of the row
-__device__ __forceinline__ float row_dot(const uint16_t* __restrict__ w, const uint16_t* xs, int K, int lane) {
+enum GemvEpi { GV_STORE = 0, GV_ROPE = 1, GV_SWIGLU = 2, GV_ADD = 3, GV_QKV = 4 };
+
+struct GemvArgs {
+  const uint16_t* x;
+  const uint16_t* w[3];   // STORE/ROPE/ADD: w[0]; SWIGLU: gate, up; QKV: wq, wk, wv
+  uint16_t* out[3];       // QKV: q, k row, v row
+  int K;                  // inner dimension
+  int N;                  // rows of w[0]
+  int nkv;                // QKV: rows of wk and of wv
+  int pos;                // RoPE position
+  const float* table;     // RoPE table (QKV without RoPE: nullptr)
+  float eps;              // NORM
+};
+
+// A weight row is read in batches of GV_BATCH 16-byte loads per lane (lane l
+// takes bytes [16 l, 16 l + 16) of every 1 KiB step).  The first batch of a
+// wave's rows is issued before x is staged; later batches are loaded while
+// the previous one is consumed.
+__device__ __forceinline__ void load_batch(const uint16_t* __restrict__ w, int s0, int K, int lane,
+                                           u32x4 (&wr)[GV_BATCH]) {
+#pragma unroll
+  for (int b = 0; b < GV_BATCH; ++b)
+    if (s0 + b * 512 < K) wr[b] = ld16(w + s0 + b * 512 + lane * 8);
+}
+
+// one weight row against x (in LDS), its first batch already in wr
+__device__ __forceinline__ float row_dot(const uint16_t* __restrict__ w, const uint16_t* xs, int K, int lane,
+                                         u32x4 (&wr)[GV_BATCH]) {
   float acc = 0.f;
   for (int s0 = 0; s0 < K; s0 += GV_BATCH * 512) {
-    u32x4 wr[GV_BATCH];
-#pragma unroll
-    for (int b = 0; b < GV_BATCH; ++b)
-      if (s0 + b * 512 < K) wr[b] = ld16(w + s0 + b * 512 + lane * 8);
+    const bool more = s0 + GV_BATCH * 512 < K;
+    u32x4 nx[GV_BATCH];
+    if (more) load_batch(w, s0 + GV_BATCH * 512, K, lane, nx);
 #pragma unroll
     for (int b = 0; b < GV_BATCH; ++b) {
       if (s0 + b * 512 >= K) break;
@@ -44,205 +75,463 @@ __device__ __forceinline__ float row_dot(const uint16_t* __restrict__ w, const u
         acc = __builtin_fmaf(hi_bf(xv[q]), hi_bf(wr[b][q]), acc);
       }
     }
+    if (more) {
+#pragma unroll
+      for (int b = 0; b < GV_BATCH; ++b) wr[b] = nx[b];
+    }
   }
   return wave_sum(acc);
 }
 
-// EPI: 0 store, 1 RoPE (outputs c and c+64 of a 128-wide head), 2 SwiGLU
-// (W = gate, W2 = up), 3 residual add (out = bf16(out + bf16(y))).
-template <int EPI>
-__global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(const uint16_t* __restrict__ x,
-                                                             const uint16_t* __restrict__ w,
-                                                             const uint16_t* __restrict__ w2, int K, int N,
-                                                             uint16_t* __restrict__ out, int pos,
-                                                             const float* __restrict__ table) {
+__device__ __forceinline__ void rope_pair(float y1, float y2, int pos, int c, const float* table, uint16_t* o1,
+                                          uint16_t* o2) {
+  const float cs = table[((long)pos * 64 + c) * 2], sn = table[((long)pos * 64 + c) * 2 + 1];
+  *o1 = f2bf(y1 * cs - y2 * sn);
+  *o2 = f2bf(y2 * cs + y1 * sn);
+}
+
+template <int EPI, bool NORM>
+__global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // K elements
-  const int lane = threadIdx.x & 63;
-  for (int i = threadIdx.x * 8; i < K; i += GV_WAVES * 64 * 8) st16(xs + i, ld16(x + i));
-  __syncthreads();
-  const int wv = (int)blockIdx.x * GV_WAVES + (int)(threadIdx.x >> 6);   // this wave's work item
-  if (EPI == 1) {
-    // work item = (head, c < 64): outputs head*128 + c and head*128 + c + 64
-    if (wv >= N / 2) return;
-    const int head = wv / 64, c = wv % 64;
-    const int o1 = head * 128 + c, o2 = o1 + 64;
-    const float y1 = row_dot(w + (long)o1 * K, xs, K, lane);
-    const float y2 = row_dot(w + (long)o2 * K, xs, K, lane);
-    if (lane == 0) {
-      const float cs = table[((long)pos * 64 + c) * 2], sn = table[((long)pos * 64 + c) * 2 + 1];
-      out[o1] = f2bf(y1 * cs - y2 * sn);
-      out[o2] = f2bf(y2 * cs + y1 * sn);
+  __shared__ float red[GV_WAVES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int K = a.K;
+  const int wv = (int)blockIdx.x * GV_WAVES + (tid >> 6);   // this wave's work item
+  constexpr bool kPair = (EPI == GV_ROPE || EPI == GV_QKV || EPI == GV_SWIGLU);
+  // the work item's rows: ROPE/QKV item = (head, c < 64), outputs head*128 + c
+  // and head*128 + c + 64; SWIGLU item c = gate row c and up row c
+  const int items = (EPI == GV_QKV) ? (a.N + 2 * a.nkv) / 2 : (EPI == GV_ROPE) ? a.N / 2 : a.N;
+  const bool valid = wv < items;
+  int which = 0, o1 = wv, o2 = wv, c = 0;
+  const uint16_t* r1 = nullptr;
+  const uint16_t* r2 = nullptr;
+  if (EPI == GV_ROPE || EPI == GV_QKV) {
+    int head = wv / 64;
+    c = wv % 64;
+    if (EPI == GV_QKV) {
+      const int hq = a.N / 128, hk = a.nkv / 128;
+      if (head >= hq + hk) {
+        which = 2;
+        head -= hq + hk;
+      } else if (head >= hq) {
+        which = 1;
+        head -= hq;
+      }
     }
-    return;
-  }
-  if (wv >= N) return;
-  const float y = row_dot(w + (long)wv * K, xs, K, lane);
-  if (EPI == 2) {
-    const float u = row_dot(w2 + (long)wv * K, xs, K, lane);
-    if (lane == 0) out[wv] = f2bf((y / (1.0f + __expf(-y))) * u);
-  } else if (EPI == 3) {
-    if (lane == 0) out[wv] = f2bf(bf2f(out[wv]) + bf2f(f2bf(y)));
+    o1 = head * 128 + c;
+    o2 = o1 + 64;
+    r1 = a.w[which] + (long)o1 * K;
+    r2 = a.w[which] + (long)o2 * K;
+  } else if (EPI == GV_SWIGLU) {
+    r1 = a.w[0] + (long)wv * K;
+    r2 = a.w[1] + (long)wv * K;
   } else {
-    if (lane == 0) out[wv] = f2bf(y);
+    r1 = a.w[0] + (long)wv * K;
+  }
+  u32x4 w1[GV_BATCH], w2[GV_BATCH];
+  if (valid) {
+    load_batch(r1, 0, K, lane, w1);
+    if (kPair) load_batch(r2, 0, K, lane, w2);
+  }
+  if (NORM) {
+    float ss = 0.f;
+    for (int i = tid * 8; i < K; i += GV_WAVES * 64 * 8) {
+      const u32x4 v = ld16(a.x + i);
+      ss = sumsq8(v, ss);
+      st16(xs + i, v);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float r = rms_inv(red, K, a.eps);
+    for (int i = tid * 8; i < K; i += GV_WAVES * 64 * 8) {   // the entries this thread staged
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + i);
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = pack2bf(lo_bf(v[w]) * r, hi_bf(v[w]) * r);
+      st16(xs + i, o);
+    }
+  } else {
+    for (int i = tid * 8; i < K; i += GV_WAVES * 64 * 8) st16(xs + i, ld16(a.x + i));
+  }
+  __syncthreads();
+  if (!valid) return;
+  const float y1 = row_dot(r1, xs, K, lane, w1);
+  if (EPI == GV_ROPE || EPI == GV_QKV) {
+    const float y2 = row_dot(r2, xs, K, lane, w2);
+    uint16_t* out = a.out[which];
+    if (lane == 0) {
+      if (which < 2 && a.table != nullptr) {
+        rope_pair(y1, y2, a.pos, c, a.table, out + o1, out + o2);
+      } else {
+        out[o1] = f2bf(y1);
+        out[o2] = f2bf(y2);
+      }
+    }
+  } else if (EPI == GV_SWIGLU) {
+    const float u = row_dot(r2, xs, K, lane, w2);
+    if (lane == 0) a.out[0][wv] = f2bf((y1 / (1.0f + __expf(-y1))) * u);
+  } else if (EPI == GV_ADD) {
+    if (lane == 0) a.out[0][wv] = f2bf(bf2f(a.out[0][wv]) + bf2f(f2bf(y1)));
+  } else {
+    if (lane == 0) a.out[0][wv] = f2bf(y1);
   }
 }
 
-template <int EPI>
-hipError_t launch_gemv_k(const uint16_t* x, const uint16_t* w, const uint16_t* w2, int K, int N, uint16_t* out,
-                         int pos, const float* table, hipStream_t s) {
-  const int items = (EPI == 1) ? N / 2 : N;
-  hipLaunchKernelGGL((gemv_kernel<EPI>), dim3((items + GV_WAVES - 1) / GV_WAVES), dim3(GV_WAVES * 64),
-                     (size_t)K * sizeof(uint16_t), s, x, w, w2, K, N, out, pos, table);
+template <int EPI, bool NORM>
+hipError_t launch_gemv_k(const GemvArgs& a, hipStream_t s) {
+  const int items = (EPI == GV_QKV) ? (a.N + 2 * a.nkv) / 2 : (EPI == GV_ROPE) ? a.N / 2 : a.N;
+  hipLaunchKernelGGL((gemv_kernel<EPI, NORM>), dim3((items + GV_WAVES - 1) / GV_WAVES), dim3(GV_WAVES * 64),
+                     (size_t)a.K * sizeof(uint16_t), s, a);
   return hipGetLastError();
+}
+
+template <bool NORM>
+hipError_t launch_gemv_n(int epi, const GemvArgs& a, hipStream_t s) {
+  switch (epi) {
+    case GV_STORE: return launch_gemv_k<GV_STORE, NORM>(a, s);
+    case GV_ROPE: return launch_gemv_k<GV_ROPE, NORM>(a, s);
+    case GV_SWIGLU: return launch_gemv_k<GV_SWIGLU, NORM>(a, s);
+    case GV_ADD: return launch_gemv_k<GV_ADD, NORM>(a, s);
+    case GV_QKV: return launch_gemv_k<GV_QKV, NORM>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ------------------------------------------------------------ decode attention
-constexpr int DA_CHUNK = 256;      // cached keys per workgroup
 constexpr int DA_G = 4;            // query heads per KV head handled by one workgroup
 constexpr int DA_DH = 128;
+constexpr int DA_MINCH = 64;       // smallest chunk: bounds the number of partials
+constexpr int DA_PR = DA_DH + 4;   // floats per (chunk, head) partial: o[128], m, l, 2 pad (16-byte rows)
 
-// Partial softmax attention of the G query heads of KV head g over keys
-// [c*256, c*256 + 256) of the cache.  Writes per head m (max, exp2 units),
-// l (sum) and o[128] (unnormalised), into part[(c * Hq + h) * (DA_DH + 2)].
+// DPP lane moves inside a row of 16 lanes (quad_perm, row_half_mirror,
+// row_mirror); every lane of the row ends with the sum of the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);    // lanes [1,0,3,2] of each quad
+  x += dpp_mov<0x4E>(x);    // lanes [2,3,0,1] of each quad
+  x += dpp_mov<0x141>(x);   // lane i <- 7 - i within each half row
+  x += dpp_mov<0x140>(x);   // lane i <- 15 - i within the row
+  return x;
+}
+
+// Partial softmax attention of the G query heads of KV head g over the keys
+// [c*chunk, c*chunk + chunk) of the cache, streamed in tiles of 64 keys with
+// the next tile's K and V rows in flight (registers, two sets).
+//   lane layout, for K and for V alike: wave w takes keys 16 w .. 16 w + 15 of
+//   a tile, 4 per load; lane = (key within the 4: its row of 16 lanes) * 16 +
+//   16-byte slice of the 256-byte row (8 of the 128 dims).
+// A key's logit is summed over its row of 16 lanes (DPP), so every lane that
+// holds a slice of that key's V row also holds its logit: each lane keeps its
+// own online softmax (running max, sum and output slice per head) over the
+// keys its row sees, and the loop needs no barrier.  At the end the 16 row
+// states of the workgroup are merged in a fixed order; the chunk's o[128]
+// (unnormalised), m (max, exp2 units) and l (sum) per head go to
+// part[(c * Hq + h) * DA_PR ...].
+struct DecodeTile {
+  u32x4 k[4], v[4];
+};
+
+__device__ __forceinline__ void load_tile(DecodeTile& t, const uint16_t* __restrict__ kb,
+                                          const uint16_t* __restrict__ vb, long row, int jb, int nk, int sl) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int j = jb + s * 4;
+    if (j < nk) {
+      t.k[s] = ld16(kb + (long)j * row + sl * 8);
+      t.v[s] = ld16(vb + (long)j * row + sl * 8);
+    } else {
+      t.k[s] = u32x4{0u, 0u, 0u, 0u};
+      t.v[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void decode_attn_partial_kernel(const uint16_t* __restrict__ q,
                                                                   const uint16_t* __restrict__ kc,
                                                                   const uint16_t* __restrict__ vc, int L,
-                                                                  int Hq, int Hkv, float sl2,
+                                                                  int chunk, int Hq, int Hkv, float sl2,
                                                                   float* __restrict__ part) {
-  __shared__ float qs[DA_G][DA_DH];
-  __shared__ float lg[DA_G][DA_CHUNK];
-  __shared__ float ored[16][DA_G][DA_DH / 8][8];   // [key group][head][8-dim slice][element]
+  __shared__ float ms[16][DA_G];                 // [wave*4 + row][head]
+  __shared__ float ls[16][DA_G];
+  __shared__ float os[16][DA_G][DA_DH];          // 32 KiB
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, g = blockIdx.y;
   const int h0 = g * DA_G;
-  const int j0 = c * DA_CHUNK;
-  const int nk = min(DA_CHUNK, L - j0);
+  const int j0 = c * chunk;
+  const int nk = min(chunk, L - j0);
+  const int nt = (nk + 63) / 64;
   const long row = (long)Hkv * DA_DH;                 // elements between consecutive keys
-  for (int i = tid; i < DA_G * DA_DH; i += 256) qs[i / DA_DH][i % DA_DH] = bf2f(q[(long)(h0 + i / DA_DH) * DA_DH + i % DA_DH]);
-  __syncthreads();
-  // logits: wave w takes keys w*64 .. w*64+63 of the chunk, 4 per instruction;
-  // lane = (key within the 4) * 16 + 16-byte slice of the 256-byte row
   const int sub = lane >> 4, sl = lane & 15;
-  u32x4 kr[16];
+  const uint16_t* kb = kc + (long)j0 * row + (long)g * DA_DH;
+  const uint16_t* vb = vc + (long)j0 * row + (long)g * DA_DH;
+  const int jw = wave * 16 + sub;                     // this lane's first key of a tile; then + 4 s
+  DecodeTile ta, tb;
+  load_tile(ta, kb, vb, row, jw, nk, sl);
+  float qv[DA_G][8];                                  // this lane's 8 dims of each head, times scale*log2(e)
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int j = wave * 64 + s * 4 + sub;
-    if (j < nk) kr[s] = ld16(kc + (long)(j0 + j) * row + (long)g * DA_DH + sl * 8);
-  }
+  for (int h = 0; h < DA_G; ++h) {
+    const u32x4 qr = ld16(q + (long)(h0 + h) * DA_DH + sl * 8);
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int j = wave * 64 + s * 4 + sub;
-    float d[DA_G];
-#pragma unroll
-    for (int h = 0; h < DA_G; ++h) {
-      float a = 0.f;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        a = __builtin_fmaf(lo_bf(kr[s][q4]), qs[h][sl * 8 + 2 * q4], a);
-        a = __builtin_fmaf(hi_bf(kr[s][q4]), qs[h][sl * 8 + 2 * q4 + 1], a);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o);   // sum over the 16 slices of the key
-      d[h] = a;
-    }
-    if (sl == 0) {
-#pragma unroll
-      for (int h = 0; h < DA_G; ++h) lg[h][j] = (j < nk) ? d[h] * sl2 : -INFINITY;
+    for (int e = 0; e < 4; ++e) {
+      qv[h][2 * e] = lo_bf(qr[e]) * sl2;
+      qv[h][2 * e + 1] = hi_bf(qr[e]) * sl2;
     }
   }
-  __syncthreads();
-  // per head: max, exp2, sum (wave h reduces head h)
-  float m = -INFINITY;
-  for (int j = lane; j < DA_CHUNK; j += 64) m = fmaxf(m, lg[wave][j]);
-  m = wave_max(m);
-  float l = 0.f;
-  for (int j = lane; j < DA_CHUNK; j += 64) {
-    const float p = __builtin_amdgcn_exp2f(lg[wave][j] - m);
-    lg[wave][j] = p;
-    l += p;
-  }
-  l = wave_sum(l);
-  float* ph = part + ((long)c * Hq + h0 + wave) * (DA_DH + 2);
-  if (lane == 0) { ph[0] = m; ph[1] = l; }
-  __syncthreads();
-  // o[h][d] = sum_j p[h][j] v[j][d]: thread = (key group kg of 16, 8-dim slice ds);
-  // a wave covers 4 keys' full rows per load
-  const int kg = tid >> 4, ds = tid & 15;
-  float acc[DA_G][8];
+  float m[DA_G], l[DA_G], acc[DA_G][8];
 #pragma unroll
-  for (int h = 0; h < DA_G; ++h)
+  for (int h = 0; h < DA_G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  for (int j = kg; j < nk; j += 16) {
-    const u32x4 vr = ld16(vc + (long)(j0 + j) * row + (long)g * DA_DH + ds * 8);
+  }
+
+  auto step = [&](const DecodeTile& t, int ti) {
+    const int jb = ti * 64 + jw;
+    float lg[4][DA_G];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = lo_bf(t.k[s][e]);
+        kf[2 * e + 1] = hi_bf(t.k[s][e]);
+      }
+      const bool ok = jb + s * 4 < nk;
+#pragma unroll
+      for (int h = 0; h < DA_G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(kf[e], qv[h][e], a);
+        a = row16_sum(a);
+        lg[s][h] = ok ? a : -INFINITY;
+      }
+    }
 #pragma unroll
     for (int h = 0; h < DA_G; ++h) {
-      const float p = lg[h][j];
+      const float mt = fmaxf(fmaxf(lg[0][h], lg[1][h]), fmaxf(lg[2][h], lg[3][h]));
+      const float mn = fmaxf(m[h], mt);
+      if (mn == -INFINITY) continue;                  // no key of this row seen yet (uniform in the row)
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);   // 0 while m[h] is -inf
+      float p[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        acc[h][2 * q4] = __builtin_fmaf(p, lo_bf(vr[q4]), acc[h][2 * q4]);
-        acc[h][2 * q4 + 1] = __builtin_fmaf(p, hi_bf(vr[q4]), acc[h][2 * q4 + 1]);
+      for (int s = 0; s < 4; ++s) p[s] = __builtin_amdgcn_exp2f(lg[s][h] - mn);
+      l[h] = l[h] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      m[h] = mn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[h][2 * e] = __builtin_fmaf(p[s], lo_bf(t.v[s][e]), acc[h][2 * e]);
+          acc[h][2 * e + 1] = __builtin_fmaf(p[s], hi_bf(t.v[s][e]), acc[h][2 * e + 1]);
+        }
       }
+    }
+  };
+
+  for (int ti = 0; ti < nt; ti += 2) {
+    if (ti + 1 < nt) load_tile(tb, kb, vb, row, (ti + 1) * 64 + jw, nk, sl);
+    step(ta, ti);
+    if (ti + 1 >= nt) break;
+    if (ti + 2 < nt) load_tile(ta, kb, vb, row, (ti + 2) * 64 + jw, nk, sl);
+    step(tb, ti + 1);
+  }
+  const int rs = wave * 4 + sub;                      // this lane's row state
+  if (sl == 0) {
+#pragma unroll
+    for (int h = 0; h < DA_G; ++h) {
+      ms[rs][h] = m[h];
+      ls[rs][h] = l[h];
     }
   }
 #pragma unroll
   for (int h = 0; h < DA_G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ored[kg][h][ds][e] = acc[h][e];
+    for (int e = 0; e < 8; ++e) os[rs][h][sl * 8 + e] = acc[h][e];
   __syncthreads();
-  // fixed-order sum over the 16 key groups: thread = (head, dim)
+  // merge the 16 row states in order: thread = (head, dim)
   for (int i = tid; i < DA_G * DA_DH; i += 256) {
     const int h = i / DA_DH, dd = i % DA_DH;
-    float t = 0.f;
-    for (int k2 = 0; k2 < 16; ++k2) t += ored[k2][h][dd / 8][dd % 8];
-    part[((long)c * Hq + h0 + h) * (DA_DH + 2) + 2 + dd] = t;
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) M = fmaxf(M, ms[r][h]);
+    float o = 0.f, lt = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float a = ms[r][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[r][h] - M);
+      o = __builtin_fmaf(a, os[r][h][dd], o);
+      lt = __builtin_fmaf(a, ls[r][h], lt);
+    }
+    float* ph = part + ((long)c * Hq + h0 + h) * DA_PR;
+    ph[dd] = o;
+    if (dd == 0) {
+      ph[DA_DH] = M;
+      ph[DA_DH + 1] = lt;
+    }
   }
 }
 
-// o[h][d] = sum_c 2^(m_c - M) o_c[d] / sum_c 2^(m_c - M) l_c, chunks in order
-__global__ __launch_bounds__(DA_DH) void decode_attn_combine_kernel(const float* __restrict__ part, int nchunks,
-                                                                    int Hq, uint16_t* __restrict__ o) {
-  const int h = blockIdx.x, d = threadIdx.x;
-  float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part[((long)c * Hq + h) * (DA_DH + 2)]);
-  float num = 0.f, den = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
-    const float* ph = part + ((long)c * Hq + h) * (DA_DH + 2);
-    const float a = __builtin_amdgcn_exp2f(ph[0] - M);
-    num = __builtin_fmaf(a, ph[2 + d], num);
-    den = __builtin_fmaf(a, ph[1], den);
+// o[h][d] = sum_c 2^(m_c - M) o_c[d] / sum_c 2^(m_c - M) l_c.  Workgroup per
+// head; thread (chunk group cg of 8, 4-dim quad dq) sums chunks cg, cg + 8, ...
+// in order, then the 8 groups are added in order: a fixed summation tree.
+__global__ __launch_bounds__(256) void decode_attn_combine_kernel(const float* __restrict__ part, int nchunks,
+                                                                  int Hq, uint16_t* __restrict__ o) {
+  __shared__ float wm[4];
+  __shared__ float red[8][DA_DH + 1];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const long cs = (long)Hq * DA_PR;                 // floats between consecutive chunks of one head
+  const float* ph = part + (long)h * DA_PR;
+  float m = -INFINITY;
+  for (int c = tid; c < nchunks; c += 256) m = fmaxf(m, ph[c * cs + DA_DH]);
+  m = wave_max(m);
+  if (lane == 0) wm[tid >> 6] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  const int cg = tid >> 5, dq = tid & 31;
+  float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
+#pragma unroll 4
+  for (int c = cg; c < nchunks; c += 8) {
+    const float* pc = ph + c * cs;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(pc + dq * 4);
+    const float mc = pc[DA_DH], lc = pc[DA_DH + 1];
+    const float a = __builtin_amdgcn_exp2f(mc - M);
+    n0 = __builtin_fmaf(a, v[0], n0);
+    n1 = __builtin_fmaf(a, v[1], n1);
+    n2 = __builtin_fmaf(a, v[2], n2);
+    n3 = __builtin_fmaf(a, v[3], n3);
+    den = __builtin_fmaf(a, lc, den);
   }
-  o[(long)h * DA_DH + d] = f2bf(num / den);
+  red[cg][dq * 4] = n0;
+  red[cg][dq * 4 + 1] = n1;
+  red[cg][dq * 4 + 2] = n2;
+  red[cg][dq * 4 + 3] = n3;
+  if (dq == 0) red[cg][DA_DH] = den;
+  __syncthreads();
+  if (tid < DA_DH) {
+    float num = 0.f, dn = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      num += red[g][tid];
+      dn += red[g][DA_DH];
+    }
+    o[(long)h * DA_DH + tid] = f2bf(num / dn);
+  }
 }
+
+// keys per workgroup: a multiple of 64 giving about 512 workgroups over the
+// KV heads (two resident per compute unit at this kernel's register use), so
+// that every workgroup streams a few tiles
+int decode_attn_chunk(int L, int Hkv) {
+  const long tiles = ((long)L * Hkv + 512L * 64 - 1) / (512L * 64);
+  return (int)(tiles < 1 ? 64 : tiles * 64);
+}
+
+size_t round_up256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
-
-size_t decode_attn_workspace(int L, int Hq) {
-  const size_t nchunks = (size_t)(L + DA_CHUNK - 1) / DA_CHUNK;
-  return nchunks * Hq * (DA_DH + 2) * sizeof(float);
-}
-
-hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int L, int Hq, int Hkv,
-                              float scale, uint16_t* o, void* ws, hipStream_t s) {
-  const int nchunks = (L + DA_CHUNK - 1) / DA_CHUNK;
-  float* part = reinterpret_cast<float*>(ws);
-  hipLaunchKernelGGL(decode_attn_partial_kernel, dim3(nchunks, Hkv), dim3(256), 0, s, q, kc, vc, L, Hq, Hkv,
-                     scale * kLog2e, part);
-  hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(Hq), dim3(DA_DH), 0, s, part, nchunks, Hq, o);
-  return hipGetLastError();
-}
 
 bool gemv_supported_k(int K) { return K > 0 && K % 512 == 0 && K <= GV_MAXK; }
 
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint16_t* w2, int K, int N, uint16_t* out,
                        int epi, int pos, const float* table, hipStream_t s) {
-  switch (epi) {
-    case 0: return launch_gemv_k<0>(x, w, w2, K, N, out, pos, table, s);
-    case 1: return launch_gemv_k<1>(x, w, w2, K, N, out, pos, table, s);
-    case 2: return launch_gemv_k<2>(x, w, w2, K, N, out, pos, table, s);
-    case 3: return launch_gemv_k<3>(x, w, w2, K, N, out, pos, table, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (epi < GV_STORE || epi > GV_ADD) return hipErrorInvalidValue;
+  GemvArgs a{};
+  a.x = x;
+  a.w[0] = w;
+  a.w[1] = w2;
+  a.out[0] = out;
+  a.K = K;
+  a.N = N;
+  a.pos = pos;
+  a.table = table;
+  return launch_gemv_n<false>(epi, a, s);
+}
+
+size_t decode_attn_workspace(int L, int Hq) {
+  const size_t nchunks = (size_t)(L + DA_MINCH - 1) / DA_MINCH;   // bound for every length up to L
+  return nchunks * Hq * DA_PR * sizeof(float);
+}
+
+hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int L, int Hq, int Hkv,
+                              float scale, uint16_t* o, void* ws, hipStream_t s) {
+  const int ch = decode_attn_chunk(L, Hkv);
+  const int nchunks = (L + ch - 1) / ch;
+  float* part = reinterpret_cast<float*>(ws);
+  hipLaunchKernelGGL(decode_attn_partial_kernel, dim3(nchunks, Hkv), dim3(256), 0, s, q, kc, vc, L, ch, Hq, Hkv,
+                     scale * kLog2e, part);
+  hipLaunchKernelGGL(decode_attn_combine_kernel, dim3(Hq), dim3(256), 0, s, part, nchunks, Hq, o);
+  return hipGetLastError();
+}
+
+size_t decode_layer_workspace(int max_len, int Hq, int f) {
+  const size_t vec = round_up256((size_t)Hq * DA_DH * 2);
+  return 2 * vec + round_up256((size_t)f * 2) + decode_attn_workspace(max_len, Hq);
+}
+
+// One layer of a decode step, six launches: QKV (with the attention norm; K
+// and V into cache row L), attention partials + combine over L + 1 rows, O
+// projection added into x, gate/up (with the feed-forward norm), down added
+// into x.  Workspace: q, o, h vectors, then the attention partials.
+hipError_t launch_decode_layer(uint16_t* x, int d, int pos, const DecodeLayerPtrs& w, int L, int Hq, int Hkv,
+                               int f, float eps, bool prenorm, const float* table, float scale, void* ws,
+                               hipStream_t s) {
+  const size_t vec = round_up256((size_t)Hq * DA_DH * 2);
+  char* base = reinterpret_cast<char*>(ws);
+  uint16_t* qv = reinterpret_cast<uint16_t*>(base);
+  uint16_t* ov = reinterpret_cast<uint16_t*>(base + vec);
+  uint16_t* hv = reinterpret_cast<uint16_t*>(base + 2 * vec);
+  void* attn_ws = base + 2 * vec + round_up256((size_t)f * 2);
+  const long kv_row = (long)Hkv * DA_DH;
+  hipError_t e;
+  GemvArgs a{};
+  a.x = x;
+  a.w[0] = w.wq;
+  a.w[1] = w.wk;
+  a.w[2] = w.wv;
+  a.out[0] = qv;
+  a.out[1] = w.k_cache + (long)L * kv_row;
+  a.out[2] = w.v_cache + (long)L * kv_row;
+  a.K = d;
+  a.N = Hq * DA_DH;
+  a.nkv = Hkv * DA_DH;
+  a.pos = pos;
+  a.table = table;
+  a.eps = eps;
+  e = prenorm ? launch_gemv_n<true>(GV_QKV, a, s) : launch_gemv_n<false>(GV_QKV, a, s);
+  if (e != hipSuccess) return e;
+  e = launch_decode_attn(qv, w.k_cache, w.v_cache, L + 1, Hq, Hkv, scale, ov, attn_ws, s);
+  if (e != hipSuccess) return e;
+  GemvArgs o{};
+  o.x = ov;
+  o.w[0] = w.wo;
+  o.out[0] = x;
+  o.K = Hq * DA_DH;
+  o.N = d;
+  e = launch_gemv_n<false>(GV_ADD, o, s);
+  if (e != hipSuccess) return e;
+  GemvArgs g{};
+  g.x = x;
+  g.w[0] = w.w_gate;
+  g.w[1] = w.w_up;
+  g.out[0] = hv;
+  g.K = d;
+  g.N = f;
+  g.eps = eps;
+  e = prenorm ? launch_gemv_n<true>(GV_SWIGLU, g, s) : launch_gemv_n<false>(GV_SWIGLU, g, s);
+  if (e != hipSuccess) return e;
+  GemvArgs dn{};
+  dn.x = hv;
+  dn.w[0] = w.w_down;
+  dn.out[0] = x;
+  dn.K = f;
+  dn.N = d;
+  return launch_gemv_n<false>(GV_ADD, dn, s);
 }
 
 }  // namespace spts

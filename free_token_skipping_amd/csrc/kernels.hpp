@@ -82,6 +82,16 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* w, const uint16_t* w2,
 size_t decode_attn_workspace(int L, int Hq);
 hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int L, int Hq, int Hkv,
                               float scale, uint16_t* o, void* ws, hipStream_t s);
+// one layer of a decode step (projections, attention over cache rows 0..L
+// after writing row L, feed-forward); weights as in spts_decode_step
+struct DecodeLayerPtrs {
+  const uint16_t *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+  uint16_t *k_cache, *v_cache;
+};
+size_t decode_layer_workspace(int max_len, int Hq, int f);
+hipError_t launch_decode_layer(uint16_t* x, int d, int pos, const DecodeLayerPtrs& w, int L, int Hq, int Hkv,
+                               int f, float eps, bool prenorm, const float* table, float scale, void* ws,
+                               hipStream_t s);
 
 // ------------------------------------------------------------- row ops
 hipError_t launch_gather(const void* src, const int32_t* idx, int k, long row_bytes, void* dst,

@@ -82,19 +82,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   const long row = blockIdx.x;
   const uint16_t* xr = x + row * d;
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    const u32x4 v = ld16(xr + c);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = lo_bf(v[w]), b = hi_bf(v[w]);
-      ss += a * a + b * b;
-    }
-  }
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) ss = sumsq8(ld16(xr + c), ss);
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+  const float r = rms_inv(red, d, eps);
   uint16_t* orow = out + row * d;
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
     const u32x4 v = ld16(xr + c);

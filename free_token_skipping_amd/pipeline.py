@@ -340,6 +340,14 @@ class DecodeCaches:
     def nbytes(self):
         return sum(2 * l * k[0].numel() * k.element_size() for l, k in zip(self.lengths, self.k))
 
+    def layer_table(self, layers):
+        """The native step's per-layer pointer table (built once per weight list)."""
+        key = tuple(id(w) for w in layers)
+        if getattr(self, "_table_key", None) != key:
+            self._table = capi.decode_layer_table(layers, self.k, self.v)
+            self._table_key = key
+        return self._table
+
 
 def decode_step(x, pos, layers, caches: DecodeCaches, cfg: LayerConfig, rope_table, tm=NO_TIMER):
     """One new token (residual row x [d] bf16, updated in place) at original
@@ -372,6 +380,15 @@ def decode_step(x, pos, layers, caches: DecodeCaches, cfg: LayerConfig, rope_tab
             h = capi.spts_decode_swiglu(z, w["wg"], w["wu"])
             capi.spts_decode_linear(h, w["wd"], out=x, accumulate=True)
     return x
+
+
+def decode_step_native(x, pos, layers, caches: DecodeCaches, cfg: LayerConfig, rope_table):
+    """decode_step as one library call (spts_decode_step): the same layer
+    arithmetic, with the norms fused into the projections and the three
+    projections of a layer in one launch."""
+    f = layers[0]["wg"].shape[0]
+    return capi.spts_decode_step(x, pos, caches.layer_table(layers), caches.lengths, cfg.Hq, cfg.Hkv, cfg.dh, f,
+                                 cfg.eps, cfg.prenorm, rope_table if cfg.theta is not None else None)
 
 
 def msdp_stack(x0, layers, cfg: LayerConfig, points, fused=True, traces=None, tm=NO_TIMER):

@@ -80,6 +80,7 @@ size_t spts_score_topk_workspace(int n);
 size_t spts_ltp_probe_workspace(int n, int d, int r);
 size_t spts_ltp_structured_workspace(int n, int d, int r, int d_low);
 size_t spts_decode_attention_workspace(int L, int Hq);
+size_t spts_decode_step_workspace(int max_len, int Hq, int f);
 size_t spts_reduced_ffn_workspace(int k, int f);
 size_t spts_msdp_stage_workspace(int n_prev);
 /* Workspace with which spts_linear / spts_linear_rope split the inner
@@ -281,11 +282,49 @@ spts_status spts_decode_swiglu(spts_ctx* ctx, const void* x, const void* w_gate,
 /* One query row against a layer's cache, every cached row visible:
  *   o[h] = sum_j softmax_j(scale * q[h] . k_cache[j, g]) v_cache[j, g],  g = h / (Hq/Hkv),
  *   j < L.  q [Hq, 128], k_cache, v_cache [>= L, Hkv, 128], o [Hq, 128], bf16.
- * Split over 256-key chunks, merged in chunk order.  Requires dh == 128,
+ * Split over chunks of 64, 128 or 256 keys (by L), merged in chunk order.
+ * Requires dh == 128,
  * Hq/Hkv == 4.  Workspace: spts_decode_attention_workspace(L, Hq). */
 spts_status spts_decode_attention(spts_ctx* ctx, const void* q, const void* k_cache,
                                   const void* v_cache, int L, int Hq, int Hkv, int dh, float scale,
                                   void* o);
+
+/* One layer's weights and cache for spts_decode_step (device pointers, bf16,
+ * 16-byte aligned, owned by the caller): wq [Hq*dh, d], wk, wv [Hkv*dh, d],
+ * wo [d, Hq*dh], w_gate, w_up [f, d], w_down [d, f]; k_cache, v_cache
+ * [cap, Hkv, dh] rows of this layer's cache. */
+typedef struct spts_decode_layer {
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  void* k_cache;
+  void* v_cache;
+  int cap;
+} spts_decode_layer;
+
+/* A whole decode step in one call: the new token's residual row x [d] (bf16,
+ * device, updated in place) at position pos through layers[0 .. n_layers) in
+ * order.  Per layer, with z = RMSNorm(x) when prenorm (unit gain, eps) else x:
+ *   q, k, v = z Wq^T, z Wk^T, z Wv^T (RoPE at pos on q and k when rope_table
+ *   is not NULL); k, v go to row lengths[l] of the layer's cache;
+ *   x += Wo decode_attention(q, rows 0 .. lengths[l]);
+ *   x += Wd (silu(z' Wg^T) * (z' Wu^T)),  z' = RMSNorm(x) when prenorm,
+ * each product rounded to bf16 as in the single calls above (the decode
+ * phase of [SPTS] Fig. A(c): every layer attends to its own cache, which after
+ * MSDP holds that layer's candidates, Table 5).  lengths: host int[n_layers],
+ * rows filled in each cache, incremented on success.  rope_table: from
+ * spts_rope_table with table_rows rows (pos < table_rows), or NULL.
+ * Requires dh == 128, Hq/Hkv == 4; d, f and Hq*dh multiples of 512, at most
+ * 16384; lengths[l] < cap for every layer.  Every argument is checked before
+ * the first launch: on an error nothing runs and lengths is unchanged.
+ * Workspace: spts_decode_step_workspace(1 + max lengths[l], Hq, f). */
+spts_status spts_decode_step(spts_ctx* ctx, void* x, int d, int pos, const spts_decode_layer* layers,
+                             int n_layers, int* lengths, int Hq, int Hkv, int dh, int f, float eps,
+                             int prenorm, const float* rope_table, int table_rows, float scale);
 
 /* table[p, c, 0..1] = (cos, sin)(p * theta^(-2c/dh)) for p < max_pos, c < dh/2,
  * angle formed in fp64 and rounded to fp32. */

@@ -155,6 +155,36 @@ def test_decode_validation(L, ctx):
     assert a(ctx, FAKE, MIS, FAKE, 10, 32, 8, 128, 0.1, FAKE) == ALIGN
 
 
+def test_decode_step_validation(L, ctx):
+    lay = (capi.DecodeLayer * 2)()
+    for i in range(2):
+        lay[i] = capi.DecodeLayer(*([FAKE] * 9), 100)
+    lens = (ctypes.c_int * 2)(10, 99)
+    f = L.spts_decode_step
+    args = lambda **kw: dict(dict(x=FAKE, d=4096, pos=5, layers=lay, n=2, lens=lens, Hq=32, Hkv=8, dh=128, f=14336,
+                                  eps=1e-5, pre=1, table=FAKE, rows=64, scale=0.1), **kw)
+    call = lambda a: f(ctx, a["x"], a["d"], a["pos"], a["layers"], a["n"], a["lens"], a["Hq"], a["Hkv"], a["dh"],
+                       a["f"], a["eps"], a["pre"], a["table"], a["rows"], a["scale"])
+    assert call(args()) == NOMEM                                        # every check passed, no workspace
+    assert call(args(d=4000)) == UNSUPPORTED
+    assert call(args(Hkv=16)) == UNSUPPORTED
+    assert call(args(pre=2)) == INVALID
+    assert call(args(pos=64)) == SHAPE                                  # outside the RoPE table
+    assert call(args(pos=64, table=None)) == NOMEM                      # no RoPE: no table bound
+    assert call(args(x=MIS)) == ALIGN
+    assert call(args(n=0, layers=None, lens=None)) == OK                # no layers: no-op
+    lens[1] = 100                                                       # layer 1 full
+    assert call(args()) == SHAPE
+    assert b"layer 1" in L.spts_last_error(ctx)
+    lens[1] = 50
+    lay[1].w_up = None
+    assert call(args()) == INVALID
+    lay[1].w_up = MIS
+    assert call(args()) == ALIGN
+    assert list(lens) == [10, 50]                                       # unchanged on every error
+    assert L.spts_decode_step_workspace(32769, 32, 14336) >= L.spts_decode_attention_workspace(32769, 32)
+
+
 def test_product_path_has_no_cpu_fallback():
     """The binding refuses CPU tensors instead of computing on the host."""
     import torch

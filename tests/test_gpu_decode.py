@@ -56,7 +56,7 @@ def test_decode_linear_rope_and_swiglu():
     assert_close(np64(h), numerics.bf16(g / (1.0 + np.exp(-g)) * u), BF16_REL, "decode swiglu")
 
 
-@pytest.mark.parametrize("L", [1, 200, 256, 257, 3000, 32768])
+@pytest.mark.parametrize("L", [1, 200, 256, 257, 3000, 4096, 9000, 16384, 32768])
 def test_decode_attention(L):
     _log(f"decode attention L={L}")
     Hq, Hkv, dh, cap = 32, 8, 128, L + 37
@@ -84,12 +84,14 @@ def _small_model(n=300):
     return sh, st, cfg, ocfg
 
 
-def test_decode_after_dense_prefill():
+@pytest.mark.parametrize("native", [False, True])
+def test_decode_after_dense_prefill(native):
     sh, st, cfg, ocfg = _small_model()
+    step = pipeline.decode_step_native if native else pipeline.decode_step
     ws = [{k: w[k].to(DEV) for k in WKEYS} for w in st["layers"]]
     steps = 3
     new = W.randn((steps, sh.d), seed=90)
-    _log("gpu dense prefill + decode")
+    _log(f"gpu dense prefill + decode (native step: {native})")
     kvs = []
     x, pos = pipeline.prefill_schedule(st["x"].to(DEV), ws, cfg, n_layers=2, first_skip_layer=2, points={},
                                        kv_out=kvs)
@@ -98,7 +100,7 @@ def test_decode_after_dense_prefill():
     outs = []
     for s in range(steps):
         xr = _cuda(new[s]).clone()
-        outs.append(np64(pipeline.decode_step(xr, sh.n + s, ws, caches, cfg, table)))
+        outs.append(np64(step(xr, sh.n + s, ws, caches, cfg, table)))
     assert caches.lengths == [sh.n + steps] * 2
     _log("oracle dense prefill + decode")
     ows = [{k: W.as_f64(w[k]) for k in WKEYS} for w in st["layers"]]
@@ -125,3 +127,40 @@ def test_decode_after_spts_prefill_structure():
     x = pipeline.decode_step(_cuda(W.randn((sh.d,), seed=91)).clone(), sh.n, ws, caches, cfg, table)
     assert caches.lengths == [501, 301]
     assert torch.isfinite(x.float()).all()
+
+
+def test_native_step_matches_per_call_step_after_spts_prefill():
+    """The one-call step (fused norms, one QKV launch) against the per-call
+    composition on the same SPTS caches: outputs and the cache rows written."""
+    sh, st, cfg, _ = _small_model(n=700)
+    ws = [{k: w[k].to(DEV) for k in WKEYS} for w in st["layers"]]
+    kvs = []
+    pipeline.prefill_schedule(st["x"].to(DEV), ws, cfg, n_layers=2, first_skip_layer=0, points={0: 500, 1: 300},
+                              kv_out=kvs)
+    steps = 3
+    a, b = pipeline.DecodeCaches(kvs, steps), pipeline.DecodeCaches(kvs, steps)
+    table = capi.spts_rope_table(sh.n + steps, 128, 500000.0, DEV)
+    for s in range(steps):
+        x0 = _cuda(W.randn((sh.d,), seed=92 + s))
+        xa = pipeline.decode_step(x0.clone(), sh.n + s, ws, a, cfg, table)
+        xb = pipeline.decode_step_native(x0.clone(), sh.n + s, ws, b, cfg, table)
+        assert_close(np64(xb), np64(xa), BF16_REL, f"native step {s}")
+    assert a.lengths == b.lengths == [503, 303]
+    for li in range(2):
+        L = a.lengths[li]
+        assert_close(np64(b.k[li][:L]), np64(a.k[li][:L]), BF16_REL, f"layer {li} k cache")
+        assert_close(np64(b.v[li][:L]), np64(a.v[li][:L]), BF16_REL, f"layer {li} v cache")
+
+
+def test_native_step_rejects_a_full_cache():
+    sh, st, cfg, _ = _small_model()
+    ws = [{k: w[k].to(DEV) for k in WKEYS} for w in st["layers"]]
+    kvs = [(torch.zeros((10, 2, 128), dtype=torch.bfloat16, device=DEV),) * 2 for _ in range(2)]
+    caches = pipeline.DecodeCaches(kvs, 1)
+    table = capi.spts_rope_table(16, 128, 500000.0, DEV)
+    x = _cuda(W.randn((sh.d,), seed=95))
+    pipeline.decode_step_native(x, 10, ws, caches, cfg, table)
+    assert caches.lengths == [11, 11]
+    with pytest.raises(capi.SptsError, match="cache holds 11 of 11"):
+        pipeline.decode_step_native(x, 11, ws, caches, cfg, table)
+    assert caches.lengths == [11, 11]
