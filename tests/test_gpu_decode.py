@@ -164,3 +164,34 @@ def test_native_step_rejects_a_full_cache():
     with pytest.raises(capi.SptsError, match="cache holds 11 of 11"):
         pipeline.decode_step_native(x, 11, ws, caches, cfg, table)
     assert caches.lengths == [11, 11]
+
+
+def test_decode_step_full_llama_shape():
+    """One decode step at the LLaMA-3.1-8B layer shape (d 4096, 32/8 heads,
+    d_head 128, SwiGLU 14336), two layers whose caches hold different row
+    counts (as after MSDP), through the one-call step and the per-call step,
+    against the oracle's decode of the same caches."""
+    sh = W.LayerShape(n=64)
+    st = W.make_stack(sh, 2, seed=11)
+    ws = [{k: w[k].to(DEV) for k in WKEYS} for w in st["layers"]]
+    cfg = pipeline.LayerConfig(Hq=32, Hkv=8, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35, prenorm=True, eps=1e-5,
+                               theta=500000.0)
+    ocfg = dict(Hq=32, Hkv=8, dh=128, prenorm=True, eps=1e-5, theta=500000.0)
+    lens, pos = [3000, 700], 5000
+    kvs = [(W.randn((L, 8, 128), seed=100 + 2 * i), W.randn((L, 8, 128), seed=101 + 2 * i)) for i, L in enumerate(lens)]
+    x = W.randn((4096,), seed=99)
+    _log("oracle decode at the LLaMA shape")
+    ows = [{k: W.as_f64(w[k]) for k in WKEYS} for w in st["layers"]]
+    ocaches = [[W.as_f64(k), W.as_f64(v)] for k, v in kvs]
+    ref = odecode.decode_step(W.as_f64(x), pos, ocaches, ows, ocfg)
+    table = capi.spts_rope_table(pos + 1, 128, 500000.0, DEV)
+    for native in (True, False):
+        _log(f"gpu decode at the LLaMA shape (native step: {native})")
+        caches = pipeline.DecodeCaches([(k.to(DEV), v.to(DEV)) for k, v in kvs], 1)
+        step = pipeline.decode_step_native if native else pipeline.decode_step
+        out = step(_cuda(x).clone(), pos, ws, caches, cfg, table)
+        assert caches.lengths == [3001, 701]
+        assert_close(np64(out), ref, BF16_REL, f"decode output (native {native})")
+        for li in range(2):
+            assert_close(np64(caches.k[li][lens[li]]), ocaches[li][0][-1], BF16_REL, f"layer {li} new key")
+            assert_close(np64(caches.v[li][lens[li]]), ocaches[li][1][-1], BF16_REL, f"layer {li} new value")

@@ -161,7 +161,7 @@ def test_gather_scatter_bit_exact(width):
 
 # ----------------------------------------------------------- reduced attention
 
-@pytest.mark.parametrize("n,kq,Hq,Hkv", [(1000, 350, 8, 2), (300, 300, 4, 1), (2500, 97, 8, 1)])
+@pytest.mark.parametrize("n,kq,Hq,Hkv", [(1000, 350, 8, 2), (300, 300, 4, 1), (2500, 97, 8, 1), (1, 1, 4, 1), (65, 1, 8, 2), (129, 65, 32, 8)])
 def test_reduced_attention_bf16(n, kq, Hq, Hkv):
     _log(f"reduced attention bf16 n={n} kq={kq}")
     q = W.randn((kq, Hq, 128), seed=13, std=1.3)
