@@ -34,6 +34,13 @@ constexpr int GV_BATCH = 8;        // 16-byte weight loads in flight per lane an
 
 enum GemvEpi { GV_STORE = 0, GV_ROPE = 1, GV_SWIGLU = 2, GV_ADD = 3, GV_QKV = 4 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// c + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2c_f32_bf16):
+// the bf16 products are exact in fp32, accumulated in fp32
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 struct GemvArgs {
   const uint16_t* x;
   const uint16_t* w[3];   // STORE/ROPE/ADD: w[0]; SWIGLU: gate, up; QKV: wq, wk, wv
@@ -70,10 +77,7 @@ __device__ __forceinline__ float row_dot(const uint16_t* __restrict__ w, const u
       if (s0 + b * 512 >= K) break;
       const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + s0 + b * 512 + lane * 8);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc = __builtin_fmaf(lo_bf(xv[q]), lo_bf(wr[b][q]), acc);
-        acc = __builtin_fmaf(hi_bf(xv[q]), hi_bf(wr[b][q]), acc);
-      }
+      for (int q = 0; q < 4; ++q) acc = dot2bf(xv[q], wr[b][q], acc);
     }
     if (more) {
 #pragma unroll
@@ -271,16 +275,9 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(const uint16_t
   const int jw = wave * 16 + sub;                     // this lane's first key of a tile; then + 4 s
   DecodeTile ta, tb;
   load_tile(ta, kb, vb, row, jw, nk, sl);
-  float qv[DA_G][8];                                  // this lane's 8 dims of each head, times scale*log2(e)
+  u32x4 qv[DA_G];                                     // this lane's 8 dims of each head (bf16 pairs)
 #pragma unroll
-  for (int h = 0; h < DA_G; ++h) {
-    const u32x4 qr = ld16(q + (long)(h0 + h) * DA_DH + sl * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[h][2 * e] = lo_bf(qr[e]) * sl2;
-      qv[h][2 * e + 1] = hi_bf(qr[e]) * sl2;
-    }
-  }
+  for (int h = 0; h < DA_G; ++h) qv[h] = ld16(q + (long)(h0 + h) * DA_DH + sl * 8);
   float m[DA_G], l[DA_G], acc[DA_G][8];
 #pragma unroll
   for (int h = 0; h < DA_G; ++h) {
@@ -295,19 +292,13 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(const uint16_t
     float lg[4][DA_G];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float kf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = lo_bf(t.k[s][e]);
-        kf[2 * e + 1] = hi_bf(t.k[s][e]);
-      }
       const bool ok = jb + s * 4 < nk;
 #pragma unroll
       for (int h = 0; h < DA_G; ++h) {
         float a = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(kf[e], qv[h][e], a);
-        a = row16_sum(a);
+        for (int e = 0; e < 4; ++e) a = dot2bf(t.k[s][e], qv[h][e], a);
+        a = row16_sum(a) * sl2;                           // logit in exp2 units
         lg[s][h] = ok ? a : -INFINITY;
       }
     }
