@@ -401,8 +401,8 @@ def cpu_baseline(sh, st, n_layers, points, frac):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of "
-              f"this build -- the sharding design is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the SPTS path here runs on a "
+              f"single GPU and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     import torch
     from free_token_skipping_amd import capi, pipeline
