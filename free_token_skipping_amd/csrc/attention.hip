@@ -373,13 +373,17 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
                                                              float* __restrict__ part_m,
                                                              float* __restrict__ part_l) {
   constexpr int P = 32 * PT;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * DH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int h = blockIdx.y * 4 + wave;
   const int g = (blockIdx.y * 4) / (Hq / Hkv);
   const int chunk = blockIdx.x;
+  const int nt = min(CHUNK / KT, (n - chunk * CHUNK + KT - 1) / KT);   // key tiles of this chunk
 
+  // tile t is read from Ks[t & 1] while tile t+1 is in flight in registers
+  TileRegs tr;
+  load_tile(tr, k, nullptr, chunk * CHUNK, n, Hkv, g, tid, false);
   bf16x8 qf[PT][8];
 #pragma unroll
   for (int c = 0; c < PT; ++c)
@@ -389,15 +393,13 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
   float m[PT], l[PT];
 #pragma unroll
   for (int c = 0; c < PT; ++c) { m[c] = -INFINITY; l[c] = 0.f; }
+  store_tile(tr, Ks[0], nullptr, tid, false);
+  __syncthreads();
 
-  TileRegs tr;
-  for (int t = 0; t < CHUNK / KT; ++t) {
+  for (int t = 0; t < nt; ++t) {
     const int j0 = chunk * CHUNK + t * KT;
-    if (j0 >= n) break;
-    load_tile(tr, k, nullptr, j0, n, Hkv, g, tid, false);
-    __syncthreads();
-    store_tile(tr, Ks, nullptr, tid, false);
-    __syncthreads();
+    if (t + 1 < nt) load_tile(tr, k, nullptr, j0 + KT, n, Hkv, g, tid, false);
+    const uint16_t* kt_s = Ks[t & 1];
 #pragma unroll
     for (int c = 0; c < PT; ++c) {
       const int prow = n - P + c * 32 + l32;
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
         for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
           s[kt] = mfma32x32x16(kf, qf[c][kk], s[kt]);
         }
       }
@@ -429,10 +431,14 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) rs += exp2f(s[kt][r] - mnew);
-      l[c] = l[c] * exp2f(m[c] - mnew) + rs;
+        for (int r = 0; r < 16; ++r) rs += __builtin_amdgcn_exp2f(s[kt][r] - mnew);
+      l[c] = l[c] * __builtin_amdgcn_exp2f(m[c] - mnew) + rs;
       m[c] = mnew;
     }
+    // the next tile goes to the other buffer, read last in step t-1 (before
+    // the barrier that ended it)
+    if (t + 1 < nt) store_tile(tr, Ks[(t + 1) & 1], nullptr, tid, false);
+    __syncthreads();
   }
   // merge the two half-waves (they hold different keys of the same probes)
 #pragma unroll
@@ -483,16 +489,20 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
                                                               const float* __restrict__ fin_il,
                                                               float* __restrict__ quad_sum) {
   constexpr int P = 32 * PT;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * DH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * DH];
   __shared__ __attribute__((aligned(16))) float st_m[4][P];
   __shared__ __attribute__((aligned(16))) float st_il[4][P];
-  __shared__ float red[4][KT];
+  __shared__ float red[2][4][KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int h = blockIdx.y * 4 + wave;
   const int g = (blockIdx.y * 4) / (Hq / Hkv);
   const int chunk = blockIdx.x;
+  const int nt = min(CHUNK / KT, (n - chunk * CHUNK + KT - 1) / KT);   // key tiles of this chunk
 
+  // tile t is read from Ks[t & 1] while tile t+1 is in flight in registers
+  TileRegs tr;
+  load_tile(tr, k, nullptr, chunk * CHUNK, n, Hkv, g, tid, false);
   for (int i = tid; i < 4 * P; i += 256) {
     const int hh = blockIdx.y * 4 + i / P, p = i % P;
     st_m[i / P][p] = fin_m[hh * P + p];
@@ -505,14 +515,12 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
     for (int kk = 0; kk < 8; ++kk)
       qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)(c * 32 + l32) * Hq + h) * DH + kk * 16 + half * 8);
 
-  TileRegs tr;
-  for (int t = 0; t < CHUNK / KT; ++t) {
+  store_tile(tr, Ks[0], nullptr, tid, false);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
     const int j0 = chunk * CHUNK + t * KT;
-    if (j0 >= n) break;
-    load_tile(tr, k, nullptr, j0, n, Hkv, g, tid, false);
-    __syncthreads();
-    store_tile(tr, Ks, nullptr, tid, false);
-    __syncthreads();
+    if (t + 1 < nt) load_tile(tr, k, nullptr, j0 + KT, n, Hkv, g, tid, false);
+    const uint16_t* kt_s = Ks[t & 1];
     float colsum[2] = {0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
       bf16x8 kf[8];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        kf[kk] = *reinterpret_cast<const bf16x8*>(Ks + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+        kf[kk] = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
 #pragma unroll
       for (int c = 0; c < PT; ++c) {
         f32x16 s;
@@ -537,7 +545,7 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int prow = n - P + pb + e;
-            if (key <= prow) colsum[kt] += exp2f(s[qd * 4 + e] * sl2 - mm[e]) * il[e];
+            if (key <= prow) colsum[kt] += __builtin_amdgcn_exp2f(s[qd * 4 + e] * sl2 - mm[e]) * il[e];
           }
         }
       }
@@ -545,13 +553,15 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
     // add the other half-wave (other probe rows), then the 4 heads
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) colsum[kt] += __shfl_xor(colsum[kt], 32);
+    float(*rd)[KT] = red[t & 1];
     if (half == 0) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) red[wave][kt * 32 + perm32(l32)] = colsum[kt];
+      for (int kt = 0; kt < 2; ++kt) rd[wave][kt * 32 + perm32(l32)] = colsum[kt];
     }
+    if (t + 1 < nt) store_tile(tr, Ks[(t + 1) & 1], nullptr, tid, false);
     __syncthreads();
     if (tid < KT && j0 + tid < n)
-      quad_sum[(long)blockIdx.y * n + j0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      quad_sum[(long)blockIdx.y * n + j0 + tid] = ((rd[0][tid] + rd[1][tid]) + rd[2][tid]) + rd[3][tid];
   }
 }
 
