@@ -86,9 +86,14 @@ class SptsError(RuntimeError):
 
 
 def lib():
-    """Load libspts.so (raises if it has not been built)."""
+    """Load libspts.so, building it in-tree first if it is not there (hipcc
+    for gfx950); raises if it cannot be built or loaded -- there is no
+    fallback."""
     global _lib
     if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build(verbose=False)
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m free_token_skipping_amd.build")
         L = ctypes.CDLL(LIB_PATH)
