@@ -341,7 +341,9 @@ class DecodeCaches:
         return sum(2 * l * k[0].numel() * k.element_size() for l, k in zip(self.lengths, self.k))
 
     def layer_table(self, layers):
-        """The native step's per-layer pointer table (built once per weight list)."""
+        """The native step's per-layer pointer table, built once per list of
+        weight dicts (keyed by the dicts' identities): replace a weight by
+        passing a new dict, not by assigning into one already used here."""
         key = tuple(id(w) for w in layers)
         if getattr(self, "_table_key", None) != key:
             self._table = capi.decode_layer_table(layers, self.k, self.v)
