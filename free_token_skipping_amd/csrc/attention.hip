@@ -362,13 +362,23 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 }
 
 // =============================================================== PAP probe
-// Pass 1: per key chunk of 256, per head, partial (max, sum) of the probe
-// softmax in log2 units.  grid (ceil(n/256), Hq/4), 4 waves = 4 heads.
-constexpr int CHUNK = 256;
+// Pass 1: per key chunk, per head, partial (max, sum) of the probe softmax
+// in log2 units.  grid (ceil(n/chunk), Hq/4), 4 waves = 4 heads.  A chunk is
+// 256, 512 or 1024 keys (a multiple of the 64-key tile): every workgroup
+// also loads all P probe queries of its 4 heads, so longer chunks cut that
+// traffic once the grid still has about two workgroups per compute unit.
+constexpr int MIN_CHUNK = 256;
+
+int probe_chunk(int n, int Hq) {
+  int c = MIN_CHUNK;
+  while (c < 1024 && (long)((n + 2 * c - 1) / (2 * c)) * (Hq / 4) >= 512) c *= 2;
+  return c;
+}
 
 template <int PT>   // probe column tiles of 32 (P = 32*PT)
 __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k, int n,
+                                                             int chunk_keys,
                                                              int Hq, int Hkv, float sl2,
                                                              float* __restrict__ part_m,
                                                              float* __restrict__ part_l) {
@@ -379,11 +389,11 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
   const int h = blockIdx.y * 4 + wave;
   const int g = (blockIdx.y * 4) / (Hq / Hkv);
   const int chunk = blockIdx.x;
-  const int nt = min(CHUNK / KT, (n - chunk * CHUNK + KT - 1) / KT);   // key tiles of this chunk
+  const int nt = min(chunk_keys / KT, (n - chunk * chunk_keys + KT - 1) / KT);   // key tiles of this chunk
 
   // tile t is read from Ks[t & 1] while tile t+1 is in flight in registers
   TileRegs tr;
-  load_tile(tr, k, nullptr, chunk * CHUNK, n, Hkv, g, tid, false);
+  load_tile(tr, k, nullptr, chunk * chunk_keys, n, Hkv, g, tid, false);
   bf16x8 qf[PT][8];
 #pragma unroll
   for (int c = 0; c < PT; ++c)
@@ -397,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
-    const int j0 = chunk * CHUNK + t * KT;
+    const int j0 = chunk * chunk_keys + t * KT;
     if (t + 1 < nt) load_tile(tr, k, nullptr, j0 + KT, n, Hkv, g, tid, false);
     const uint16_t* kt_s = Ks[t & 1];
 #pragma unroll
@@ -484,6 +494,7 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restr
 template <int PT>
 __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k, int n,
+                                                              int chunk_keys,
                                                               int Hq, int Hkv, float sl2,
                                                               const float* __restrict__ fin_m,
                                                               const float* __restrict__ fin_il,
@@ -498,11 +509,11 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
   const int h = blockIdx.y * 4 + wave;
   const int g = (blockIdx.y * 4) / (Hq / Hkv);
   const int chunk = blockIdx.x;
-  const int nt = min(CHUNK / KT, (n - chunk * CHUNK + KT - 1) / KT);   // key tiles of this chunk
+  const int nt = min(chunk_keys / KT, (n - chunk * chunk_keys + KT - 1) / KT);   // key tiles of this chunk
 
   // tile t is read from Ks[t & 1] while tile t+1 is in flight in registers
   TileRegs tr;
-  load_tile(tr, k, nullptr, chunk * CHUNK, n, Hkv, g, tid, false);
+  load_tile(tr, k, nullptr, chunk * chunk_keys, n, Hkv, g, tid, false);
   for (int i = tid; i < 4 * P; i += 256) {
     const int hh = blockIdx.y * 4 + i / P, p = i % P;
     st_m[i / P][p] = fin_m[hh * P + p];
@@ -518,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
   store_tile(tr, Ks[0], nullptr, tid, false);
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
-    const int j0 = chunk * CHUNK + t * KT;
+    const int j0 = chunk * chunk_keys + t * KT;
     if (t + 1 < nt) load_tile(tr, k, nullptr, j0 + KT, n, Hkv, g, tid, false);
     const uint16_t* kt_s = Ks[t & 1];
     float colsum[2] = {0.f, 0.f};
@@ -644,7 +655,7 @@ __global__ void attn_f32_kernel(const float* q, const int32_t* idx, const float*
 
 // ---------------------------------------------------------------- launchers
 size_t probe_workspace(int n, int P, int Hq) {
-  const size_t nchunks = (size_t)(n + CHUNK - 1) / CHUNK;
+  const size_t nchunks = (size_t)(n + MIN_CHUNK - 1) / MIN_CHUNK;   // bound for every chunk size
   const size_t HP = (size_t)Hq * P;
   // part_m, part_l [nchunks*HP]; fin_m, fin_il [HP]; quad_sum [Hq/4 * n]
   size_t b = 2 * nchunks * HP * 4 + 2 * HP * 4 + (size_t)((Hq + 3) / 4) * n * 4;
@@ -653,7 +664,8 @@ size_t probe_workspace(int n, int P, int Hq) {
 
 hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P, int Hq, int Hkv,
                              float scale, float* scores, void* ws, hipStream_t s) {
-  const int nchunks = (n + CHUNK - 1) / CHUNK;
+  const int ck = probe_chunk(n, Hq);
+  const int nchunks = (n + ck - 1) / ck;
   const long HP = (long)Hq * P;
   float* part_m = reinterpret_cast<float*>(ws);
   float* part_l = part_m + nchunks * HP;
@@ -665,11 +677,11 @@ hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P,
   switch (P / 32) {
 #define SPTS_PROBE_CASE(PT)                                                                        \
   case PT:                                                                                         \
-    hipLaunchKernelGGL(probe_stats_kernel<PT>, grid, dim3(256), 0, s, q, k, n, Hq, Hkv, sl2,      \
+    hipLaunchKernelGGL(probe_stats_kernel<PT>, grid, dim3(256), 0, s, q, k, n, ck, Hq, Hkv, sl2,  \
                        part_m, part_l);                                                            \
     hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_m,         \
                        part_l, nchunks, (int)HP, fin_m, fin_il);                                   \
-    hipLaunchKernelGGL(probe_colsum_kernel<PT>, grid, dim3(256), 0, s, q, k, n, Hq, Hkv, sl2,     \
+    hipLaunchKernelGGL(probe_colsum_kernel<PT>, grid, dim3(256), 0, s, q, k, n, ck, Hq, Hkv, sl2, \
                        fin_m, fin_il, quad);                                                       \
     break;
     SPTS_PROBE_CASE(1)
