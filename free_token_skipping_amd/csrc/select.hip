@@ -81,7 +81,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     ma = block_max(la, red);
     mb = block_max(lb, red);
   }
-  constexpr int UNROLL_J = IPT > 0 ? IPT : 1;
+  constexpr int UNROLL_J = IPT > 0 ? IPT : 8;      // workspace keys: 8 loads in flight per lane
   const int nfree = n - nf;
   const int J = IPT > 0 ? IPT : (n + TPB - 1) / TPB;   // rows per lane (a constant if IPT > 0)
   const int base = w * J * 64 + lane;                  // row of (w, j, lane) = base + 64 j
