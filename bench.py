@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-ttft", action="store_true", help="skip the 32-layer prefill schedule vs dense table")
     ap.add_argument("--no-hbm", action="store_true", help="skip the cold/warm gather and scatter-add table")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode / end-to-end table")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the 8K attention layer and the 128K score path / 16K prefix layer")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode table (prefill + decode at 32K), printed as one JSON line")
     ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
@@ -266,6 +268,79 @@ def decode_table(x0, layers, cfg, tokens=16, gen=(32, 128, 512)):
     out["prompt_tokens"] = n
     out["weights"] = f"{len(layers)} generated layers cycled over {nl}; {wbytes / 1e9:.2f} GB read per token"
     out["end_to_end"] = e2e
+    return out
+
+
+def other_workloads(dev, steps, warmup):
+    """The remaining workloads, each timed like the headline (warm-up, then
+    steps bracketed by events, per-call breakdown):
+      attn_layer_8k     attention-only layer, 8192 tokens, 64 needles, P 64, keep 0.5
+      long_128k_score   probe queries -> PAP score -> top-k at 131072 tokens (clustered
+                        keys, 512 needles, P 128, keep 0.25)
+      long_16k_prefix   the 128K recipe as a full layer on a 16384-token prefix"""
+    import torch
+    import workloads as W
+    from free_token_skipping_amd import capi, pipeline
+    from free_token_skipping_amd.pipeline import LayerConfig, keep_count
+    keys = ["wq", "wk", "wv", "wo", "wg", "wu", "wd", "u_t", "v_t"]
+    out = {}
+
+    def record(name, fn, tokens, extra):
+        total_ms, _, summ = timed(fn, steps, warmup)
+        ms = total_ms / steps
+        out[name] = dict(extra, ms_per_step=round(ms, 4), tokens_per_s=round(tokens / (ms * 1e-3), 1),
+                         breakdown=breakdown(summ, steps))
+        log(f"{name}: {ms:.3f} ms/step, {tokens / (ms * 1e-3):,.0f} tokens/s")
+
+    c2 = W.CONFIGS["attn_layer_8k"]
+    sh = c2["shape"]
+    inp = W.make_layer(sh, seed=c2["seed"], with_ffn=False, needles=c2["needles"])
+    w = {k: inp[k].to(dev) for k in ("wq", "wk", "wv", "wo")}
+    x0 = inp["x"].to(dev)
+    pos = torch.arange(sh.n, dtype=torch.int32, device=dev)
+    cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=c2["keep_attn"], keep_ffn=None)
+
+    def step8k(tm):
+        x = x0.clone()
+        pipeline.spts_layer(x, pos, w, cfg, tm=tm)
+    record("attn_layer_8k", step8k, sh.n, {"tokens": sh.n, "keep_attn": c2["keep_attn"], "probes": sh.P,
+                                           "needles": c2["needles"]})
+    del inp, w, x0
+
+    c5 = W.CONFIGS["long_layer_128k"]
+    sh = c5["shape"]
+    inp = W.make_layer(sh, seed=c5["seed"], with_ffn=False, needles=c5["needles"],
+                       clustered_keys=(c5["centroids"], c5["sigma"]))
+    xp = inp["x"][-sh.P:].to(dev).contiguous()
+    wq = inp["wq"].to(dev)
+    kk = inp["k"].to(dev)
+    k = keep_count(c5["keep_attn"], sh.n)
+
+    def score128k(tm):
+        with tm("probe_q_proj", 2.0 * sh.P * sh.d * sh.Hq * sh.dh):
+            qp = capi.spts_linear(xp, wq)
+        with tm("pap_probe", 2.0 * sh.Hq * sh.dh * sh.P * sh.n):
+            S = capi.spts_probe_attention(qp.view(sh.P, sh.Hq, sh.dh), kk)
+        with tm("select_attn", 4.0 * sh.n + 4.0 * k):
+            capi.spts_score_topk(S, k, sh.P)
+    record("long_128k_score", score128k, sh.n, {"tokens": sh.n, "probes": sh.P, "keep": c5["keep_attn"],
+                                                 "needles": c5["needles"], "keys": "clustered"})
+    del inp, xp, wq, kk
+
+    shp = W.LayerShape(n=c5["prefix"], P=sh.P)
+    inp = W.make_layer(shp, seed=c5["seed"], needles=64, clustered_keys=(c5["centroids"], c5["sigma"]))
+    w = {k2: inp[k2].to(dev) for k2 in keys if k2 in inp}   # no Wk: the keys are given
+    x0 = inp["x"].to(dev)
+    kg = inp["k"].to(dev)
+    pos = torch.arange(shp.n, dtype=torch.int32, device=dev)
+    cfg = LayerConfig(Hq=shp.Hq, Hkv=shp.Hkv, dh=shp.dh, P=shp.P, keep_attn=c5["keep_attn"], keep_ffn=c5["keep_ffn"],
+                      w_fuse=c5["w_fuse"])
+
+    def prefix16k(tm):
+        x = x0.clone()
+        pipeline.spts_layer(x, pos, w, cfg, k_given=kg, tm=tm)
+    record("long_16k_prefix", prefix16k, shp.n, {"tokens": shp.n, "probes": shp.P, "keep": c5["keep_attn"],
+                                                  "keys": "clustered, given"})
     return out
 
 
@@ -521,6 +596,9 @@ def main():
     if not args.no_ttft:
         log("timing the 32-layer prefill schedule against dense")
         rec.setdefault("also", {})["prefill_32_layers"] = ttft_table(x0, layers, stack_cfg)
+    if not args.no_other:
+        log("timing the 8K attention layer, the 128K score path and the 16K prefix layer")
+        rec.setdefault("also", {}).update(other_workloads(dev, args.steps, args.warmup))
     if not args.no_decode:
         log("timing decode after the 32-layer prefill, SPTS against full caches")
         rec.setdefault("also", {})["decode_32_layers"] = decode_table(x0, layers, stack_cfg)
