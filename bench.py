@@ -344,6 +344,38 @@ def other_workloads(dev, steps, warmup):
     return out
 
 
+def select_batched_table(dev, rows=256, n=32768, k=11469, nf=64, reps=10):
+    """Capability micro-benchmark of the top-k kernel: one call holds only
+    128 KiB of scores, so its time is latency, not bandwidth; a batch of
+    independent 32K rows in one launch (one workgroup per row) shows the
+    kernel's throughput.  Bytes: scores read + indices written."""
+    import torch
+    from free_token_skipping_amd import capi
+    g = torch.Generator(device="cpu").manual_seed(0)
+    s = torch.empty(rows, n).exponential_(generator=g).to(dev)
+    idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    one = torch.empty(k, dtype=torch.int32, device=dev)
+
+    def clock(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    ms_b = clock(lambda: capi.spts_score_topk_batched(s, k, nf, idx))
+    ms_1 = clock(lambda: capi.spts_score_topk(s[0], k, nf, idx=one))
+    nbytes = rows * n * 4 + rows * k * 4
+    gbs = nbytes / (ms_b * 1e-3) / 1e9
+    log(f"select: one 32K row {ms_1 * 1e3:.1f} us; {rows} rows in one launch {ms_b * 1e3:.1f} us, {gbs:,.0f} GB/s")
+    return {"rows": rows, "n": n, "k": k, "forced": nf, "one_row_us": round(ms_1 * 1e3, 1),
+            "batch_us": round(ms_b * 1e3, 1), "batch_bytes": nbytes, "batch_gbs": round(gbs, 1),
+            "batch_frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 # ------------------------------------------------- HBM-bound row kernels
 
 def hbm_table(x0, reps=5):
@@ -593,6 +625,7 @@ def main():
     if not args.no_hbm:
         log("timing the standalone gather / scatter-add, cold and warm")
         rec.setdefault("also", {})["hbm_row_kernels"] = hbm_table(x0)
+        rec["also"]["select_batched"] = select_batched_table(dev)
     if not args.no_ttft:
         log("timing the 32-layer prefill schedule against dense")
         rec.setdefault("also", {})["prefill_32_layers"] = ttft_table(x0, layers, stack_cfg)

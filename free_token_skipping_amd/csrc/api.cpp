@@ -206,6 +206,23 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
                     "score_topk");
 }
 
+spts_status spts_score_topk_batched(spts_ctx* ctx, const float* s, int64_t s_stride, int batch, int n, int k,
+                                    int n_forced, int32_t* idx, int64_t idx_stride) {
+  CHECK_CTX();
+  REQUIRE(batch >= 0, SPTS_ERR_SHAPE, "batch must be >= 0");
+  REQUIRE(n >= 1, SPTS_ERR_SHAPE, "n must be >= 1");
+  REQUIRE(n <= 32768, SPTS_ERR_UNSUPPORTED, "batched top-k holds a row in registers: n <= 32768 (got %d)", n);
+  REQUIRE(n_forced >= 0 && n_forced <= k && n_forced <= n, SPTS_ERR_SHAPE,
+          "need 0 <= n_forced <= k and n_forced <= n (n=%d k=%d n_forced=%d)", n, k, n_forced);
+  REQUIRE(s_stride >= n && idx_stride >= (k < n ? k : n), SPTS_ERR_SHAPE, "row strides shorter than the rows");
+  if (batch == 0) return SPTS_OK;
+  REQUIRE_PTR(s); REQUIRE_PTR(idx);
+  REQUIRE_ALIGN(s); REQUIRE_ALIGN(idx);
+  return hip_status(ctx, launch_topk_batched(s, (long)s_stride, batch, n, k, n_forced, idx, (long)idx_stride,
+                                             ctx->stream),
+                    "score_topk_batched");
+}
+
 spts_status spts_score_topk_multiply(spts_ctx* ctx, const float* s_a, const float* s_b, int n, int k,
                                      int n_forced, int32_t* idx, float* fused_out) {
   CHECK_CTX();

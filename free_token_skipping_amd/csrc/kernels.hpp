@@ -72,6 +72,9 @@ size_t topk_workspace(int n);
 // or by their product (multiply == true)
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
                        int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s);
+// one workgroup per score row (rows of at most 1024 * 32 scores, keys in registers)
+hipError_t launch_topk_batched(const float* s, long s_stride, int batch, int n, int k, int n_forced, int32_t* idx,
+                               long idx_stride, hipStream_t st);
 
 // -------------------------------------------------------------- decode
 // y = x W^T for one row x [K]; epi 0 store, 1 RoPE at pos (pairs c, c+64 of

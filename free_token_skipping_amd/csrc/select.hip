@@ -60,7 +60,8 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
                                                    const float* __restrict__ s_b, float wa, float wb,
                                                    int mult, int n, int k, int nf, int32_t* __restrict__ idx,
                                                    float* __restrict__ fused_out,
-                                                   uint32_t* __restrict__ keys) {
+                                                   uint32_t* __restrict__ keys, long s_stride,
+                                                   long idx_stride) {
   __shared__ int hist[NW][256];          // one histogram per wave (less atomic contention)
   __shared__ int tot_hist[256];
   __shared__ float red[NW];
@@ -68,6 +69,8 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   __shared__ int cnt_sh[2][NW];
   __shared__ int sel[2];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  s_a += (long)blockIdx.x * s_stride;    // batched rows (a single call: one workgroup, offsets 0)
+  idx += (long)blockIdx.x * idx_stride;
 
   if (k >= n) {
     for (int i = tid; i < n; i += TPB) idx[i] = i;
@@ -222,6 +225,18 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 
 }  // namespace
 
+hipError_t launch_topk_batched(const float* s, long s_stride, int batch, int n, int k, int n_forced, int32_t* idx,
+                               long idx_stride, hipStream_t st) {
+  if (batch == 0) return hipSuccess;
+  if (n <= TPB * 8)
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(batch), dim3(TPB), 0, st, s, nullptr, 0.f, 0.f, 0, n, k, n_forced, idx,
+                       nullptr, nullptr, s_stride, idx_stride);
+  else
+    hipLaunchKernelGGL(topk_kernel<32>, dim3(batch), dim3(TPB), 0, st, s, nullptr, 0.f, 0.f, 0, n, k, n_forced, idx,
+                       nullptr, nullptr, s_stride, idx_stride);
+  return hipGetLastError();
+}
+
 size_t topk_workspace(int n) { return (((size_t)n * 4) + 255) & ~(size_t)255; }
 
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
@@ -229,11 +244,11 @@ hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b,
   uint32_t* keys = reinterpret_cast<uint32_t*>(ws);
   const int mult = multiply ? 1 : 0;
   if (n <= TPB * 8)
-    hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys);
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys, 0L, 0L);
   else if (n <= TPB * 32)
-    hipLaunchKernelGGL(topk_kernel<32>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys);
+    hipLaunchKernelGGL(topk_kernel<32>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys, 0L, 0L);
   else
-    hipLaunchKernelGGL(topk_kernel<0>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys);
+    hipLaunchKernelGGL(topk_kernel<0>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys, 0L, 0L);
   return hipGetLastError();
 }
 

@@ -122,6 +122,16 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
                             float w_b, int n, int k, int n_forced, int32_t* idx,
                             float* fused_out);
 
+/* spts_score_topk (one score, no fusion) on `batch` independent rows in one
+ * launch, one workgroup per row: row b reads s + b * s_stride and writes
+ * min(k, n) ascending indices to idx + b * idx_stride (same rule: last
+ * n_forced rows forced, ties to the lower index).  Requires n <= 32768 (a
+ * row's keys stay in registers; no workspace); strides in elements, at
+ * least the row lengths (rows are read and written 4 bytes at a time, so
+ * only s and idx themselves must be 16-byte aligned).  batch == 0 is a no-op. */
+spts_status spts_score_topk_batched(spts_ctx* ctx, const float* s, int64_t s_stride, int batch, int n,
+                                    int k, int n_forced, int32_t* idx, int64_t idx_stride);
+
 /* As spts_score_topk with Table D's "Multiply" fusion, the pages' default
  * (the criterion C^FFN * S^MHA of [SPTS] Table 6): ranking score
  *     c = fl(s_a * s_b)   (one float32 product; s_b required),

@@ -132,6 +132,17 @@ def test_attention_and_rows_validation(L, ctx):
     assert L.spts_scatter(ctx, capi.BF16, FAKE, MIS, 4, 8, FAKE, 1) == ALIGN
 
 
+def test_select_batched_validation(L, ctx):
+    b = L.spts_score_topk_batched
+    assert b(ctx, FAKE, 32768, 4, 32769, 10, 1, FAKE, 16) == UNSUPPORTED                  # row too long
+    assert b(ctx, FAKE, 100, 4, 100, 10, 11, FAKE, 16) == SHAPE                           # forced > k
+    assert b(ctx, FAKE, 96, 4, 100, 10, 1, FAKE, 16) == SHAPE                             # stride < n
+    assert b(ctx, FAKE, 100, 4, 100, 10, 1, FAKE, 9) == SHAPE                             # idx stride < k
+    assert b(ctx, MIS, 100, 4, 100, 10, 1, FAKE, 16) == ALIGN
+    assert b(ctx, None, 100, 4, 100, 10, 1, FAKE, 16) == INVALID
+    assert b(ctx, None, 100, 0, 100, 10, 1, None, 16) == OK                               # empty batch
+
+
 def test_decode_validation(L, ctx):
     assert L.spts_decode_linear(ctx, FAKE, FAKE, 4000, 64, FAKE, 0) == UNSUPPORTED        # kdim % 512
     assert L.spts_decode_linear(ctx, FAKE, FAKE, 32768, 64, FAKE, 0) == UNSUPPORTED       # kdim > 16384

@@ -103,6 +103,18 @@ def test_select_special_values():
         assert idx.cpu().numpy().tolist() == select.select_topk(s.numpy(), k, nf).tolist()
 
 
+@pytest.mark.parametrize("n,k,nf,batch", [(1000, 350, 64, 5), (32768, 11469, 64, 3), (700, 900, 16, 2),
+                                          (8193, 4097, 0, 4)])
+def test_select_batched_bit_exact(n, k, nf, batch):
+    _log(f"batched select n={n} k={k} nf={nf} batch={batch}")
+    rows = [W.make_scores(n, seed=100 * b + n, ties=(b % 2) * 30, dist="exp" if b % 3 else "few") for b in range(batch)]
+    s = torch.stack(rows)
+    idx = capi.spts_score_topk_batched(_cuda(s), k, nf).cpu().numpy().astype(np.int64)
+    assert idx.shape == (batch, min(k, n))
+    for b in range(batch):
+        assert np.array_equal(idx[b], select.select_topk(rows[b].numpy(), k, nf)), f"row {b}"
+
+
 @pytest.mark.parametrize("n,k,nf", [(1000, 350, 64), (32768, 11469, 64)])
 def test_select_fused_bit_exact(n, k, nf):
     _log(f"fused select n={n}")
