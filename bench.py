@@ -500,7 +500,9 @@ def cpu_baseline(sh, st, n_layers, points, frac):
                        f"{frac:.4f} of their rows scaled by 1/{frac:.4f}; stack = 2 x sum over stages, the "
                        f"first layer's K/V + probe scaled to the outgoing row count; "
                        f"{measured:.1f}s measured on {cores} BLAS threads"),
-            "seconds_per_step_est": round(t_stack, 2)}
+            "seconds_per_step_est": round(t_stack, 2),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
+            "numpy": np.__version__}
 
 
 # --------------------------------------------------------------------- main
