@@ -16,6 +16,7 @@
 // The MFMA is issued as (B fragment, A fragment) so each lane's accumulators
 // hold ONE row of C and 4 groups of 4 consecutive columns; every epilogue
 // (row scatter, RoPE pairs, SwiGLU pairs, row norms) is then lane-local.
+#include <atomic>
 #include <cmath>
 
 #include "common.hpp"
@@ -384,12 +385,18 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
   const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
   const size_t lds = 2 * 2 * TILE_ELEMS * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tn_kernel<EPI, GATHER>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // the dynamic-LDS limit is a per-device kernel attribute: set it once on
+  // each device this instantiation is launched on (idempotent if two threads race)
+  static std::atomic<unsigned long long> attr_devices{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = 1ull << (dev & 63);
+  if (!(attr_devices.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tn_kernel<EPI, GATHER>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_devices.fetch_or(bit, std::memory_order_release);
   }
   const int ks = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
   const int grid = ((tiles_m * tiles_n * ks + 7) / 8) * 8;     // a multiple of the 8 XCDs
