@@ -287,3 +287,99 @@ def test_dense_layers_and_schedule_small():
     assert x2.shape == (400, sh.d) and len(p2) == 400 and np.all(np.diff(p2) > 0)
     assert set(range(sh.n - 64, sh.n)) <= set(p2.tolist())
     assert torch.isfinite(x2.float()).all()
+
+
+def test_msdp_stack_32k_full_size():
+    """The timed workload itself: the 8-layer pre-norm RoPE stack at 32768
+    tokens with the [SPTS] Sec. 3.3 stage schedule, in the configuration the
+    benchmark runs.  Checked at full size:
+      * structure that holds at any size: candidate counts per layer, nested
+        ascending candidate sets that keep the probe rows, selection sizes,
+        probe-score mass Hq*P, rows never selected passing through
+        bit-identically;
+      * the first pruning decision against the oracle's own probe score over
+        all 32768 rows (window rule);
+      * layer 0's attention output on sampled selected rows against the
+        oracle's own projections, on rows before the first position where the
+        two prune sets differ (causality makes those rows independent of it)."""
+    from oracle.attention import reduced_attention
+    from oracle.normrope import rmsnorm, rope
+    from oracle.select import select_topk
+
+    cfgd = W.CONFIGS["msdp_stack_32k"]
+    sh = cfgd["shape"]
+    N, P, Hq, Hkv, dh = sh.n, sh.P, sh.Hq, sh.Hkv, sh.dh
+    _log("generate 32K stack inputs")
+    st = W.make_stack(sh, cfgd["layers"], seed=cfgd["seed"])
+    budgets = [numerics.keep_count(r, N) for r in cfgd["budget_ratios"]]
+    pts = pipeline.prune_points(0, cfgd["stage_ends"], budgets)
+    assert pts == olayer.prune_points(0, cfgd["stage_ends"], budgets)
+    cfg = pipeline.LayerConfig(Hq=Hq, Hkv=Hkv, dh=dh, P=P, keep_attn=cfgd["keep_attn"], keep_ffn=cfgd["keep_ffn"],
+                               w_fuse=cfgd["w_fuse"], prenorm=True, eps=cfgd["eps"], theta=cfgd["theta"])
+    x0 = st["x"].to(DEV)
+    traces = []
+    _log("gpu 32K stack")
+    x, pos = pipeline.msdp_stack(x0, [_gpu_w(w) for w in st["layers"]], cfg, pts, traces=traces)
+    torch.cuda.synchronize()
+
+    # ---- structure of every layer
+    counts = olayer.candidate_counts(N, cfgd["layers"], pts)
+    prev = np.arange(N)
+    selected_pos = set()
+    for li, tr in enumerate(traces):
+        cur = tr["pos"].cpu().numpy().astype(np.int64)
+        n = len(cur)
+        assert n == counts[li] and np.all(np.diff(cur) > 0), li
+        assert np.isin(cur, prev).all() and np.isin(np.arange(N - P, N), cur).all(), li
+        assert abs(float(tr["S_pre"].double().sum()) - Hq * P) < 0.5, li
+        k = numerics.keep_count(cfgd["keep_attn"], n)
+        for name in ("idx", "idx_f"):
+            sel = tr[name].cpu().numpy().astype(np.int64)
+            assert len(sel) == k and np.all(np.diff(sel) > 0), (li, name)
+            assert np.isin(np.arange(n - P, n), sel).all(), (li, name)
+            selected_pos.update(cur[sel].tolist())
+        prev = cur
+    final = pos.cpu().numpy().astype(np.int64)
+    assert np.array_equal(final, prev)
+    got = np64(x)
+    assert np.isfinite(got).all()
+    x0_64 = W.as_f64(st["x"])
+    untouched = ~np.isin(final, np.fromiter(selected_pos, dtype=np.int64))
+    _log(f"final candidates never selected by any layer: {int(untouched.sum())}")
+    assert np.array_equal(got[untouched], x0_64[final[untouched]])
+
+    # ---- layer 0 against the oracle's own projections
+    _log("oracle layer-0 projections at 32K")
+    w0 = st["layers"][0]
+    theta, scale = cfgd["theta"], dh ** -0.5
+    xt = numerics.bf16(rmsnorm(x0_64, cfgd["eps"]))
+    allpos = np.arange(N)
+
+    def proj(rows, wname, heads, rope_pos):
+        acc = numerics.f32(xt[rows] @ W.as_f64(w0[wname]).T).reshape(len(rows), heads, dh)
+        return numerics.bf16(rope(acc, rope_pos, theta) if rope_pos is not None else acc)
+
+    K = proj(allpos, "wk", Hkv, allpos)
+    V = proj(allpos, "wv", Hkv, None)
+    Qp = proj(allpos[-P:], "wq", Hq, allpos[-P:])
+    S_ref = pap.pap_scores(Qp, K, scale)
+    tr0 = traces[0]
+    assert_close(np64(tr0["S_pre"]), S_ref, 1e-2, "layer-0 probe score over 32K (chain)")
+    keep_gpu = tr0["keep"].cpu().numpy().astype(np.int64)
+    assert window_violations(S_ref, keep_gpu, budgets[0], P, rel=CHAIN_WINDOW) == 0
+    keep_ref = select_topk(numerics.f32(S_ref), budgets[0], P)
+    differ = np.setxor1d(keep_gpu, keep_ref)
+    first_diff = int(differ.min()) if len(differ) else N
+    idx_ref = select_topk(numerics.f32(S_ref[keep_ref]), numerics.keep_count(cfgd["keep_attn"], budgets[0]), P)
+    idx_gpu = tr0["idx"].cpu().numpy().astype(np.int64)
+    rows_ref = keep_ref[idx_ref]                      # original positions of the oracle's queries
+    rows_gpu = keep_gpu[idx_gpu]
+    common = np.intersect1d(rows_ref[rows_ref < first_diff], rows_gpu)
+    assert len(common) >= 64
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(common, size=32, replace=False))
+    loc_ref = np.searchsorted(keep_ref, sample)       # query rows within the oracle's candidate set
+    Qs = proj(sample, "wq", Hq, sample)
+    O_ref = numerics.bf16(reduced_attention(Qs, loc_ref, K[keep_ref], V[keep_ref], scale))
+    O_gpu = np64(tr0["O"]).reshape(-1, Hq, dh)[np.searchsorted(rows_gpu, sample)]
+    assert_close(O_gpu, O_ref, BF16_REL, "layer-0 attention output, sampled rows at 32K")
