@@ -12,8 +12,11 @@
 // w owns the contiguous rows [w*C, (w+1)*C) and its lanes walk them 64 at a
 // time, so every load is one coalesced 256-byte access.  The radix passes
 // skip the leading key bits that all free rows share (found by an OR/AND
-// reduction), so the first 8-bit digit already spreads the keys over many
-// histogram bins instead of piling them onto one sign/exponent bin.
+// reduction).  The first digit is 11 bits wide and is counted in one shared
+// 2048-bin histogram.  When the bin holding the threshold has at most CAP keys
+// (the usual case), those keys are copied to LDS and a single wave finishes
+// the remaining digits over them, with no workgroup barrier per digit; a
+// larger bin (many equal scores) continues with 8-bit workgroup passes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,6 +25,9 @@ namespace {
 
 constexpr int TPB = 1024;
 constexpr int NW = TPB / 64;
+constexpr int B1 = 11;                 // width of the first digit
+constexpr int NB1 = 1 << B1;           // its histogram bins
+constexpr int CAP = 8192;              // keys a single wave finishes from LDS
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) return 0u;                 // NaN ranks below everything
@@ -53,6 +59,66 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Wave-wide inclusive scans on DPP (no LDS round trip): Hillis-Steele within
+// each 16-lane row (row_shr 1, 2, 4, 8), then row_bcast:15 carries row 0's and
+// row 2's totals into rows 1 and 3, and row_bcast:31 carries rows 0-1 into
+// rows 2-3.  A lane whose source is outside its row, or whose row is masked
+// off, receives the operation's identity.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, uint32_t id, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xa, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  return (int)wave_scan_dpp((uint32_t)v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(v, 0u, [](uint32_t a, uint32_t b) { return a | b; }), 63);
+}
+
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_scan_dpp(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a & b; }), 63);
+}
+
+// Suffix search over NB bins held NB/64 per lane, highest digit first (lane t
+// holds bins NB-1-t*(NB/64) downwards): the digit d holding the rem-th
+// largest key, how many keys lie above that digit's bin and the bin's count.
+// Called by one whole wave; the result is valid in every lane.
+template <int NB>
+__device__ __forceinline__ void wave_find_digit(const int* h, int rem, int lane, int& d, int& above, int& cnt) {
+  constexpr int PER = NB / 64;
+  const int top = NB - 1 - lane * PER;
+  int part = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) part += h[top - q];
+  const int incl = wave_incl_scan(part);
+  const int excl = incl - part;
+  const bool mine = excl < rem && rem <= incl;
+  int dd = 0, ab = 0, cc = 0;
+  if (mine) {
+    ab = excl;
+    for (int q = 0; q < PER; ++q) {
+      const int c = h[top - q];
+      if (ab + c >= rem) { dd = top - q; cc = c; break; }
+      ab += c;
+    }
+  }
+  const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(mine)) - 1);
+  d = __builtin_amdgcn_readlane(dd, src);
+  above = __builtin_amdgcn_readlane(ab, src);
+  cnt = __builtin_amdgcn_readlane(cc, src);
+}
+
 // IPT > 0: each lane keeps the keys of its IPT rows in registers across all
 // passes (n <= 1024 * IPT).  IPT == 0: keys are re-read from the workspace.
 template <int IPT>
@@ -62,12 +128,16 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
                                                    float* __restrict__ fused_out,
                                                    uint32_t* __restrict__ keys, long s_stride,
                                                    long idx_stride) {
-  __shared__ int hist[NW][256];          // one histogram per wave (less atomic contention)
+  __shared__ int hist1[NB1];             // first digit
+  __shared__ uint32_t pool[CAP];         // candidate keys, or the per-wave histograms of the fallback passes
+  __shared__ int h8[256];                // the finishing wave's histogram
   __shared__ int tot_hist[256];
   __shared__ float red[NW];
   __shared__ uint32_t bits_sh[2][NW];
   __shared__ int cnt_sh[2][NW];
-  __shared__ int sel[2];
+  __shared__ int sel[3];
+  __shared__ int ccount;
+  int (*hist)[256] = reinterpret_cast<int (*)[256]>(pool);   // [NW][256] fallback, one per wave
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   s_a += (long)blockIdx.x * s_stride;    // batched rows (a single call: one workgroup, offsets 0)
   idx += (long)blockIdx.x * idx_stride;
@@ -117,11 +187,8 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   int need_eq = 0;
   if (kp > 0) {
     // bits shared by every free key need no radix pass
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      k_or |= __shfl_xor(k_or, o);
-      k_and &= __shfl_xor(k_and, o);
-    }
+    k_or = wave_or(k_or);
+    k_and = wave_and(k_and);
     if (lane == 0) { bits_sh[0][w] = k_or; bits_sh[1][w] = k_and; }
     __syncthreads();
     k_or = 0u; k_and = 0xFFFFFFFFu;
@@ -131,6 +198,92 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     uint32_t mask = R >= 32 ? 0u : ~((1u << R) - 1u);
     uint32_t prefix = k_and & mask;
     int rem = kp;
+    // ---- first digit: B1 bits, one shared histogram (every free key carries the prefix)
+    if (R > 0) {
+      const int width = R < B1 ? R : B1;
+      const int shift = R - width;
+      const uint32_t dmask = (1u << width) - 1u;
+      for (int i = tid; i < NB1; i += TPB) hist1[i] = 0;
+      if (tid == 0) ccount = 0;
+      __syncthreads();
+#pragma unroll UNROLL_J
+      for (int j = 0; j < J; ++j) {
+        const int i = base + 64 * j;
+        if (i < nfree) atomicAdd(&hist1[(key_at(j) >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      if (w == 0) {
+        int d, above, cnt;
+        wave_find_digit<NB1>(hist1, rem, lane, d, above, cnt);
+        if (lane == 0) { sel[0] = d; sel[1] = rem - above; sel[2] = cnt; }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)sel[0] << shift;
+      rem = sel[1];
+      mask |= dmask << shift;
+      R = shift;
+      const int c = sel[2];
+      if (R > 0 && c <= CAP) {
+        // ---- the c keys of that bin go to LDS (any order); one wave finishes them
+        int mc = 0;
+#pragma unroll UNROLL_J
+        for (int j = 0; j < J; ++j) {
+          const int i = base + 64 * j;
+          mc += (i < nfree && (key_at(j) & mask) == prefix) ? 1 : 0;
+        }
+        const int incl_c = wave_incl_scan(mc);
+        const int excl = incl_c - mc;
+        const int tot = __builtin_amdgcn_readlane(incl_c, 63);
+        int wb = 0;
+        if (lane == 0 && tot > 0) wb = atomicAdd(&ccount, tot);
+        int slot = __builtin_amdgcn_readfirstlane(wb) + excl;
+#pragma unroll UNROLL_J
+        for (int j = 0; j < J; ++j) {
+          const int i = base + 64 * j;
+          const uint32_t key = key_at(j);
+          if (i < nfree && (key & mask) == prefix) pool[slot++] = key;
+        }
+        __syncthreads();
+        if (w == 0) {
+          // bits every candidate shares need no digit (all equal: done at once)
+          uint32_t o = 0u, an = 0xFFFFFFFFu;
+#pragma unroll 8
+          for (int q = lane; q < c; q += 64) { o |= pool[q]; an &= pool[q]; }
+          o = wave_or(o);
+          an = wave_and(an);
+          const uint32_t low = (1u << R) - 1u;
+          const uint32_t var = (o & ~an) & low;
+          const int Rn = var ? 32 - __clz(var) : 0;
+          const uint32_t fixed = low & ~(Rn >= 32 ? 0u : ((1u << Rn) - 1u));
+          prefix |= an & fixed;
+          mask |= fixed;
+          R = Rn;
+          while (R > 0) {
+            const int wd = R < 8 ? R : 8;
+            const int sft = R - wd;
+            const uint32_t dm = (1u << wd) - 1u;
+            for (int q = lane; q < 256; q += 64) h8[q] = 0;
+#pragma unroll 8
+            for (int q = lane; q < c; q += 64) {
+              const uint32_t key = pool[q];
+              if ((key & mask) == prefix) atomicAdd(&h8[(key >> sft) & dm], 1);
+            }
+            int d, above, cnt;
+            wave_find_digit<256>(h8, rem, lane, d, above, cnt);
+            prefix |= (uint32_t)d << sft;
+            rem -= above;
+            mask |= dm << sft;
+            R = sft;
+          }
+          if (lane == 0) { sel[0] = (int)prefix; sel[1] = rem; }
+        }
+        __syncthreads();
+        prefix = (uint32_t)sel[0];
+        rem = sel[1];
+        R = 0;
+      }
+    }
+    // ---- a large bin (many equal keys): 8-bit digits over the whole workgroup
     while (R > 0) {
       const int width = R < 8 ? R : 8;
       const int shift = R - width;
@@ -150,29 +303,10 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
         tot_hist[tid] = t;
       }
       __syncthreads();
-      if (tid < 64) {
-        // suffix sums over 256 bins, 4 bins per lane, highest digit first
-        const int b0 = 255 - tid * 4;
-        const int c0 = tot_hist[b0], c1 = tot_hist[b0 - 1], c2 = tot_hist[b0 - 2], c3 = tot_hist[b0 - 3];
-        const int part = c0 + c1 + c2 + c3;
-        int incl = part;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o);
-          if (tid >= o) incl += y;
-        }
-        const int excl = incl - part;   // keys with a larger digit than b0
-        // the digit holding the rem-th largest lies in this lane's 4 bins iff excl < rem <= incl
-        if (excl < rem && rem <= incl) {
-          int above = excl, d = b0;
-          const int cs[4] = {c0, c1, c2, c3};
-          for (int q = 0; q < 4; ++q) {
-            if (above + cs[q] >= rem) { d = b0 - q; break; }
-            above += cs[q];
-          }
-          sel[0] = d;
-          sel[1] = rem - above;
-        }
+      if (w == 0) {
+        int d, above, cnt;
+        wave_find_digit<256>(tot_hist, rem, lane, d, above, cnt);
+        if (lane == 0) { sel[0] = d; sel[1] = rem - above; }
       }
       __syncthreads();
       prefix |= (uint32_t)sel[0] << shift;
@@ -195,29 +329,49 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     const uint32_t key = key_at(j);
     const bool forced = i >= nfree && i < n;
     const bool free_row = i < nfree;
-    n_gt += __popcll(__ballot(forced || (free_row && key > T)));
-    n_eq += __popcll(__ballot(free_row && key == T));
+    n_gt += (forced || (free_row && key > T)) ? 1 : 0;
+    n_eq += (free_row && key == T) ? 1 : 0;
   }
+  n_gt = wave_sum_int(n_gt);
+  n_eq = wave_sum_int(n_eq);
   if (lane == 0) { cnt_sh[0][w] = n_gt; cnt_sh[1][w] = n_eq; }
   __syncthreads();
-  int eq_before = 0, out = 0;
-  for (int q = 0; q < w; ++q) {
-    const int e = cnt_sh[1][q];
-    out += cnt_sh[0][q] + min(max(need_eq - eq_before, 0), e);
-    eq_before += e;
+  // wave q's output starts after the rows taken by waves 0..q-1: lanes 0..NW-1
+  // hold the per-wave counts and scan them
+  const int g_q = lane < NW ? cnt_sh[0][lane] : 0;
+  const int e_q = lane < NW ? cnt_sh[1][lane] : 0;
+  const int e_excl = wave_incl_scan(e_q) - e_q;               // equal rows in earlier waves
+  const int t_q = g_q + min(max(need_eq - e_excl, 0), e_q);    // rows wave q takes
+  const int t_excl = wave_incl_scan(t_q) - t_q;
+  int eq_before = __builtin_amdgcn_readlane(e_excl, w), out = __builtin_amdgcn_readlane(t_excl, w);
+  const int e_total = __builtin_amdgcn_readlane(e_excl + e_q, NW - 1);
+  if (need_eq >= e_total) {
+    // every row equal to T is taken (no tie at the threshold): take key >= T
+#pragma unroll UNROLL_J
+    for (int j = 0; j < J; ++j) {
+      const int i = base + 64 * j;
+      const uint32_t key = key_at(j);
+      const bool take = (i >= nfree) & (i < n) | (i < nfree) & (key >= T);
+      const uint64_t tm = __ballot(take);
+      const int pos = out + lanes_below(tm);
+      if (take & (pos < k)) idx[pos] = i;  // exactly k are taken; the bound only guards memory
+      out += __popcll(tm);
+    }
+    return;
   }
+  // a tie at the threshold: the lowest-index need_eq of the rows equal to T
 #pragma unroll UNROLL_J
   for (int j = 0; j < J; ++j) {
     const int i = base + 64 * j;
     const uint32_t key = key_at(j);
     const bool free_row = i < nfree;
-    const bool eq = free_row && key == T;
+    const bool eq = free_row & (key == T);
     const uint64_t eqm = __ballot(eq);
-    const bool take = (i >= nfree && i < n) || (free_row && key > T) ||
-                      (eq && eq_before + lanes_below(eqm) < need_eq);
+    const bool take = (i >= nfree) & (i < n) | free_row & (key > T) |
+                      eq & (eq_before + lanes_below(eqm) < need_eq);
     const uint64_t tm = __ballot(take);
     const int pos = out + lanes_below(tm);
-    if (take && pos < k) idx[pos] = i;     // exactly k are taken; the bound only guards memory
+    if (take & (pos < k)) idx[pos] = i;    // exactly k are taken; the bound only guards memory
     out += __popcll(tm);
     eq_before += __popcll(eqm);
   }
