@@ -51,36 +51,26 @@ void gemm_tn_kernel(GemmArgs g) {
   const int l32 = lane & 31, half = lane >> 5;
 
   // ---- tile order.  Workgroups are dealt round-robin to the 8 XCDs, so
-  // workgroup b runs on XCD b % 8.  Within an XCD the order walks groups of
-  // GROUP_M row tiles across the XCD's column tiles, so the ~32 tiles resident
-  // on one XCD at a time form a 4 x 8 block that shares A and B k-slices in
-  // that XCD's L2.  Wide problems (at least 32 column tiles, a multiple of 8)
-  // split the columns: XCD x owns column tiles [x*tn8, (x+1)*tn8) of every row
-  // tile and all XCDs walk the row groups in step, so an A panel fetched by
-  // one XCD is still in the shared last-level cache when the others reach it
-  // (4 % faster on the gate/up GEMM).  Otherwise each XCD takes a contiguous
-  // run of the logical tile order over all column tiles.
+  // workgroup b runs on XCD b % 8.  Each XCD gets a contiguous run of the
+  // logical tile order, and that order walks groups of GROUP_M row tiles
+  // across all column tiles, so the ~32 tiles resident on one XCD at a time
+  // form a 4 x 8 block that shares A and B k-slices in that XCD's L2.
   const int tiles_m = (g.m + BM - 1) / BM;
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
   const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
   const int ksplit = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
   const int total = tiles_m * tiles_n * ksplit;
-  constexpr int GROUP_M = 4;
-  const int xcd = (int)blockIdx.x & 7, local = (int)blockIdx.x >> 3;
-  const int tn8 = tiles_n / 8;
-  const bool split_n = ksplit == 1 && tiles_n % 8 == 0 && tn8 >= 4;
-  const int run = split_n ? tiles_m * tn8 : total;    // tiles in this XCD's order
   const int per_xcd = (total + 7) / 8;
-  const int logical_k = split_n ? local : xcd * per_xcd + local;
-  if (split_n ? local >= run : logical_k >= total) return;   // padding workgroups
+  const int logical_k = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+  if (logical_k >= total) return;                     // padding workgroups of the last XCD run
   const int kslice = logical_k % ksplit;              // split-K slice (0 without split)
   const int logical = logical_k / ksplit;
-  const int cols = split_n ? tn8 : tiles_n;           // column tiles walked by a row group
-  const int in_group = GROUP_M * cols;
+  constexpr int GROUP_M = 4;
+  const int in_group = GROUP_M * tiles_n;
   const int first_m = (logical / in_group) * GROUP_M;
   const int gm = min(GROUP_M, tiles_m - first_m);
   const int tile_m = first_m + (logical % in_group) % gm;
-  const int tile_n = (split_n ? xcd * tn8 : 0) + (logical % in_group) / gm;
+  const int tile_n = (logical % in_group) / gm;
 
   // KV: tiles at or past column n0 read b1 and write out2
   const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
