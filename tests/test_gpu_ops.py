@@ -87,7 +87,10 @@ def test_probe_f32_tiny_config():
     (1, 1, 1, "exp", 0), (2, 1, 0, "exp", 0), (17, 5, 2, "few", 0), (1000, 350, 64, "exp", 40),
     (1000, 999, 64, "few", 0), (1000, 64, 64, "exp", 0), (1000, 1000, 64, "exp", 0),
     (1000, 1200, 10, "exp", 0), (32768, 11469, 64, "exp", 500), (32768, 11469, 64, "few", 0),
-    (131072, 32768, 128, "exp", 2000), (4097, 2049, 0, "few", 0)])
+    (131072, 32768, 128, "exp", 2000), (4097, 2049, 0, "few", 0),
+    # more than 8192 keys share the threshold's first digit: workgroup passes finish
+    (32768, 16384, 64, "band", 0), (32768, 16384, 64, "band", 300), (32768, 11469, 64, "few3", 0),
+    (131072, 65536, 128, "band", 0)])
 def test_select_bit_exact(n, k, nf, dist, ties):
     _log(f"select n={n} k={k} nf={nf} {dist}")
     s = W.make_scores(n, seed=n + k, ties=ties, dist=dist)

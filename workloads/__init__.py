@@ -272,12 +272,19 @@ def sorted_rows(n, k, n_forced, seed=0):
 def make_scores(n, seed=0, ties=0, dist="exp"):
     """Synthetic non-negative fp32 score vectors for selection tests.
 
-    dist "exp": Exp(1) draws; "few": values from a small set (many ties).
+    dist "exp": Exp(1) draws; "few": values from a small set of 8 (many ties);
+    "few3": 3 values; "band": 70 % of the rows in [1, 1 + 2^-20) (distinct
+    values packed into a narrow range), the rest in [2, 4).
     `ties` extra rows copy a random earlier row's value.
     """
     rng = np.random.default_rng(seed)
     if dist == "few":
         s = rng.integers(0, 8, size=n).astype(np.float32) / np.float32(4)
+    elif dist == "few3":
+        s = rng.integers(0, 3, size=n).astype(np.float32)
+    elif dist == "band":
+        dense = rng.random(size=n) < 0.7
+        s = np.where(dense, 1.0 + rng.random(size=n) * 2.0 ** -20, 2.0 + 2.0 * rng.random(size=n)).astype(np.float32)
     else:
         s = rng.exponential(size=n).astype(np.float32)
     if ties and n > 1:
