@@ -142,14 +142,17 @@ class Context:
         _check(self, lib().spts_check(self.handle), "spts_check")
 
 
-_ctx = None
+_ctxs = {}
 
 
 def context():
-    global _ctx
-    if _ctx is None:
-        _ctx = Context()
-    return _ctx
+    """The context of the current torch stream: each stream has its own, so
+    calls on two streams never share a workspace."""
+    key = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    ctx = _ctxs.get(key)
+    if ctx is None:
+        ctx = _ctxs[key] = Context()
+    return ctx
 
 
 def _check(ctx, status, what):
