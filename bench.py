@@ -292,29 +292,29 @@ def other_workloads(dev, steps, warmup):
                          breakdown=breakdown(summ, steps))
         log(f"{name}: {ms:.3f} ms/step, {tokens / (ms * 1e-3):,.0f} tokens/s")
 
-    c2 = W.CONFIGS["attn_layer_8k"]
-    sh = c2["shape"]
-    inp = W.make_layer(sh, seed=c2["seed"], with_ffn=False, needles=c2["needles"])
+    cfg8k = W.CONFIGS["attn_layer_8k"]
+    sh = cfg8k["shape"]
+    inp = W.make_layer(sh, seed=cfg8k["seed"], with_ffn=False, needles=cfg8k["needles"])
     w = {k: inp[k].to(dev) for k in ("wq", "wk", "wv", "wo")}
     x0 = inp["x"].to(dev)
     pos = torch.arange(sh.n, dtype=torch.int32, device=dev)
-    cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=c2["keep_attn"], keep_ffn=None)
+    cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=cfg8k["keep_attn"], keep_ffn=None)
 
     def step8k(tm):
         x = x0.clone()
         pipeline.spts_layer(x, pos, w, cfg, tm=tm)
-    record("attn_layer_8k", step8k, sh.n, {"tokens": sh.n, "keep_attn": c2["keep_attn"], "probes": sh.P,
-                                           "needles": c2["needles"]})
+    record("attn_layer_8k", step8k, sh.n, {"tokens": sh.n, "keep_attn": cfg8k["keep_attn"], "probes": sh.P,
+                                           "needles": cfg8k["needles"]})
     del inp, w, x0
 
-    c5 = W.CONFIGS["long_layer_128k"]
-    sh = c5["shape"]
-    inp = W.make_layer(sh, seed=c5["seed"], with_ffn=False, needles=c5["needles"],
-                       clustered_keys=(c5["centroids"], c5["sigma"]))
+    cfg128k = W.CONFIGS["long_layer_128k"]
+    sh = cfg128k["shape"]
+    inp = W.make_layer(sh, seed=cfg128k["seed"], with_ffn=False, needles=cfg128k["needles"],
+                       clustered_keys=(cfg128k["centroids"], cfg128k["sigma"]))
     xp = inp["x"][-sh.P:].to(dev).contiguous()
     wq = inp["wq"].to(dev)
     kk = inp["k"].to(dev)
-    k = keep_count(c5["keep_attn"], sh.n)
+    k = keep_count(cfg128k["keep_attn"], sh.n)
 
     def score128k(tm):
         with tm("probe_q_proj", 2.0 * sh.P * sh.d * sh.Hq * sh.dh):
@@ -323,23 +323,23 @@ def other_workloads(dev, steps, warmup):
             S = capi.spts_probe_attention(qp.view(sh.P, sh.Hq, sh.dh), kk)
         with tm("select_attn", 4.0 * sh.n + 4.0 * k):
             capi.spts_score_topk(S, k, sh.P)
-    record("long_128k_score", score128k, sh.n, {"tokens": sh.n, "probes": sh.P, "keep": c5["keep_attn"],
-                                                 "needles": c5["needles"], "keys": "clustered"})
+    record("long_128k_score", score128k, sh.n, {"tokens": sh.n, "probes": sh.P, "keep": cfg128k["keep_attn"],
+                                                 "needles": cfg128k["needles"], "keys": "clustered"})
     del inp, xp, wq, kk
 
-    shp = W.LayerShape(n=c5["prefix"], P=sh.P)
-    inp = W.make_layer(shp, seed=c5["seed"], needles=64, clustered_keys=(c5["centroids"], c5["sigma"]))
+    shp = W.LayerShape(n=cfg128k["prefix"], P=sh.P)
+    inp = W.make_layer(shp, seed=cfg128k["seed"], needles=64, clustered_keys=(cfg128k["centroids"], cfg128k["sigma"]))
     w = {k2: inp[k2].to(dev) for k2 in keys if k2 in inp}   # no Wk: the keys are given
     x0 = inp["x"].to(dev)
     kg = inp["k"].to(dev)
     pos = torch.arange(shp.n, dtype=torch.int32, device=dev)
-    cfg = LayerConfig(Hq=shp.Hq, Hkv=shp.Hkv, dh=shp.dh, P=shp.P, keep_attn=c5["keep_attn"], keep_ffn=c5["keep_ffn"],
-                      w_fuse=c5["w_fuse"])
+    cfg = LayerConfig(Hq=shp.Hq, Hkv=shp.Hkv, dh=shp.dh, P=shp.P, keep_attn=cfg128k["keep_attn"], keep_ffn=cfg128k["keep_ffn"],
+                      w_fuse=cfg128k["w_fuse"])
 
     def prefix16k(tm):
         x = x0.clone()
         pipeline.spts_layer(x, pos, w, cfg, k_given=kg, tm=tm)
-    record("long_16k_prefix", prefix16k, shp.n, {"tokens": shp.n, "probes": shp.P, "keep": c5["keep_attn"],
+    record("long_16k_prefix", prefix16k, shp.n, {"tokens": shp.n, "probes": shp.P, "keep": cfg128k["keep_attn"],
                                                   "keys": "clustered, given"})
     return out
 
