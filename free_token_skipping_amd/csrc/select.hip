@@ -160,18 +160,54 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   const int base = w * J * 64 + lane;                  // row of (w, j, lane) = base + 64 j
   uint32_t kr[IPT > 0 ? IPT : 1];
   uint32_t k_or = 0u, k_and = 0xFFFFFFFFu;             // over the free rows
-#pragma unroll UNROLL_J
-  for (int j = 0; j < J; ++j) {
-    const int i = base + 64 * j;
-    uint32_t key = 0u;
-    if (i < n) {
-      const float x = !s_b ? s_a[i] : mult ? __fmul_rn(s_a[i], s_b[i]) : fuse(s_a[i], s_b[i], ma, mb, wa, wb);
-      if (fused_out) fused_out[i] = x;
-      key = order_key(x);
-      if (i < nfree) { k_or |= key; k_and &= key; }
-      if (IPT == 0) keys[i] = key;
+  if (IPT > 0) {
+    // every load is issued before any is used (the score/fusion choice is
+    // made outside the row loop), so a lane's loads are in flight together;
+    // kr holds the raw score bits until they become keys
+    if (!s_b) {
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const int i = base + 64 * j;
+        kr[IPT > 0 ? j : 0] = i < n ? __float_as_uint(s_a[i]) : 0u;
+      }
+    } else {
+      float xb[IPT > 0 ? IPT : 1];
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const int i = base + 64 * j;
+        kr[IPT > 0 ? j : 0] = i < n ? __float_as_uint(s_a[i]) : 0u;
+        xb[j] = i < n ? s_b[i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const float a = __uint_as_float(kr[IPT > 0 ? j : 0]);
+        kr[IPT > 0 ? j : 0] = __float_as_uint(mult ? __fmul_rn(a, xb[j]) : fuse(a, xb[j], ma, mb, wa, wb));
+      }
     }
-    if (IPT > 0) kr[IPT > 0 ? j : 0] = key;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int i = base + 64 * j;
+      uint32_t key = 0u;
+      if (i < n) {
+        const float x = __uint_as_float(kr[IPT > 0 ? j : 0]);
+        if (fused_out) fused_out[i] = x;
+        key = order_key(x);
+        if (i < nfree) { k_or |= key; k_and &= key; }
+      }
+      kr[IPT > 0 ? j : 0] = key;
+    }
+  } else {
+#pragma unroll UNROLL_J
+    for (int j = 0; j < J; ++j) {
+      const int i = base + 64 * j;
+      if (i < n) {
+        const float x = !s_b ? s_a[i] : mult ? __fmul_rn(s_a[i], s_b[i]) : fuse(s_a[i], s_b[i], ma, mb, wa, wb);
+        if (fused_out) fused_out[i] = x;
+        const uint32_t key = order_key(x);
+        if (i < nfree) { k_or |= key; k_and &= key; }
+        keys[i] = key;
+      }
+    }
   }
   if (k >= n) return;
   if (IPT == 0) __threadfence_block();
