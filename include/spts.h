@@ -292,9 +292,10 @@ spts_status spts_decode_swiglu(spts_ctx* ctx, const void* x, const void* w_gate,
 /* One query row against a layer's cache, every cached row visible:
  *   o[h] = sum_j softmax_j(scale * q[h] . k_cache[j, g]) v_cache[j, g],  g = h / (Hq/Hkv),
  *   j < L.  q [Hq, 128], k_cache, v_cache [>= L, Hkv, 128], o [Hq, 128], bf16.
- * Split over chunks of 64, 128 or 256 keys (by L), merged in chunk order.
- * Requires dh == 128,
- * Hq/Hkv == 4.  Workspace: spts_decode_attention_workspace(L, Hq). */
+ * Split over chunks of keys (a multiple of 64, sized for about 512
+ * workgroups); a second launch merges the chunk partials in chunk order.
+ * Requires dh == 128, Hq/Hkv == 4.  Workspace:
+ * spts_decode_attention_workspace(L, Hq). */
 spts_status spts_decode_attention(spts_ctx* ctx, const void* q, const void* k_cache,
                                   const void* v_cache, int L, int Hq, int Hkv, int dh, float scale,
                                   void* o);
