@@ -128,16 +128,19 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
                                                    float* __restrict__ fused_out,
                                                    uint32_t* __restrict__ keys, long s_stride,
                                                    long idx_stride) {
-  __shared__ int hist1[NB1];             // first digit
-  __shared__ uint32_t pool[CAP];         // candidate keys, or the per-wave histograms of the fallback passes
-  __shared__ int h8[256];                // the finishing wave's histogram
+  // Every per-key update below is unconditional: a row that does not count
+  // goes to a dummy slot of its own lane (index + lane past the end), so the
+  // loops carry no branches and the dummies never collide.
+  __shared__ int hist1[NB1 + 64];        // first digit
+  __shared__ uint32_t pool[CAP + 64];    // candidate keys, or the per-wave histograms of the fallback passes
+  __shared__ int h8[256 + 64];           // the finishing wave's histogram
   __shared__ int tot_hist[256];
   __shared__ float red[NW];
   __shared__ uint32_t bits_sh[2][NW];
   __shared__ int cnt_sh[2][NW];
   __shared__ int sel[3];
   __shared__ int ccount;
-  int (*hist)[256] = reinterpret_cast<int (*)[256]>(pool);   // [NW][256] fallback, one per wave
+  int (*hist)[320] = reinterpret_cast<int (*)[320]>(pool);   // [NW][256 + 64] fallback, one per wave
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   s_a += (long)blockIdx.x * s_stride;    // batched rows (a single call: one workgroup, offsets 0)
   idx += (long)blockIdx.x * idx_stride;
@@ -158,6 +161,13 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   const int nfree = n - nf;
   const int J = IPT > 0 ? IPT : (n + TPB - 1) / TPB;   // rows per lane (a constant if IPT > 0)
   const int base = w * J * 64 + lane;                  // row of (w, j, lane) = base + 64 j
+  // a lane's rows base + 64 j are valid (< n) for j < jv and free (< nfree)
+  // for j < jf; loops test j against these instead of keeping a mask per row
+  int jv = n > base ? (n - base + 63) / 64 : 0;
+  int jf = nfree > base ? (nfree - base + 63) / 64 : 0;
+  // an empty asm that "changes" jv and jf before each loop keeps the compiler
+  // from holding 2 x J row masks in scalar registers across loops
+#define SPTS_FRESH_ROWS() asm volatile("" : "+v"(jv), "+v"(jf))
   uint32_t kr[IPT > 0 ? IPT : 1];
   uint32_t k_or = 0u, k_and = 0xFFFFFFFFu;             // over the free rows
   if (IPT > 0) {
@@ -184,16 +194,20 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
         kr[IPT > 0 ? j : 0] = __float_as_uint(mult ? __fmul_rn(a, xb[j]) : fuse(a, xb[j], ma, mb, wa, wb));
       }
     }
+    if (fused_out) {
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const int i = base + 64 * j;
+        if (i < n) fused_out[i] = __uint_as_float(kr[IPT > 0 ? j : 0]);
+      }
+    }
+    SPTS_FRESH_ROWS();
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      const int i = base + 64 * j;
-      uint32_t key = 0u;
-      if (i < n) {
-        const float x = __uint_as_float(kr[IPT > 0 ? j : 0]);
-        if (fused_out) fused_out[i] = x;
-        key = order_key(x);
-        if (i < nfree) { k_or |= key; k_and &= key; }
-      }
+      const uint32_t key = j < jv ? order_key(__uint_as_float(kr[IPT > 0 ? j : 0])) : 0u;
+      const bool fr = j < jf;
+      k_or |= fr ? key : 0u;
+      k_and &= fr ? key : 0xFFFFFFFFu;
       kr[IPT > 0 ? j : 0] = key;
     }
   } else {
@@ -242,11 +256,10 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
       for (int i = tid; i < NB1; i += TPB) hist1[i] = 0;
       if (tid == 0) ccount = 0;
       __syncthreads();
+      SPTS_FRESH_ROWS();
 #pragma unroll UNROLL_J
-      for (int j = 0; j < J; ++j) {
-        const int i = base + 64 * j;
-        if (i < nfree) atomicAdd(&hist1[(key_at(j) >> shift) & dmask], 1);
-      }
+      for (int j = 0; j < J; ++j)
+        atomicAdd(&hist1[j < jf ? (int)((key_at(j) >> shift) & dmask) : NB1 + lane], 1);
       __syncthreads();
       if (w == 0) {
         int d, above, cnt;
@@ -262,22 +275,22 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
       if (R > 0 && c <= CAP) {
         // ---- the c keys of that bin go to LDS (any order); one wave finishes them
         int mc = 0;
+        SPTS_FRESH_ROWS();
 #pragma unroll UNROLL_J
-        for (int j = 0; j < J; ++j) {
-          const int i = base + 64 * j;
-          mc += (i < nfree && (key_at(j) & mask) == prefix) ? 1 : 0;
-        }
+        for (int j = 0; j < J; ++j) mc += ((j < jf) & ((key_at(j) & mask) == prefix)) ? 1 : 0;
         const int incl_c = wave_incl_scan(mc);
         const int excl = incl_c - mc;
         const int tot = __builtin_amdgcn_readlane(incl_c, 63);
         int wb = 0;
         if (lane == 0 && tot > 0) wb = atomicAdd(&ccount, tot);
         int slot = __builtin_amdgcn_readfirstlane(wb) + excl;
+        SPTS_FRESH_ROWS();
 #pragma unroll UNROLL_J
         for (int j = 0; j < J; ++j) {
-          const int i = base + 64 * j;
           const uint32_t key = key_at(j);
-          if (i < nfree && (key & mask) == prefix) pool[slot++] = key;
+          const bool match = (j < jf) & ((key & mask) == prefix);
+          pool[match ? slot : CAP + lane] = key;
+          slot += match ? 1 : 0;
         }
         __syncthreads();
         if (w == 0) {
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 #pragma unroll 8
             for (int q = lane; q < c; q += 64) {
               const uint32_t key = pool[q];
-              if ((key & mask) == prefix) atomicAdd(&h8[(key >> sft) & dm], 1);
+              atomicAdd(&h8[(key & mask) == prefix ? (int)((key >> sft) & dm) : 256 + lane], 1);
             }
             int d, above, cnt;
             wave_find_digit<256>(h8, rem, lane, d, above, cnt);
@@ -324,13 +337,13 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
       const int width = R < 8 ? R : 8;
       const int shift = R - width;
       const uint32_t dmask = (1u << width) - 1u;
-      for (int i = tid; i < NW * 256; i += TPB) (&hist[0][0])[i] = 0;
+      for (int i = tid; i < NW * 320; i += TPB) (&hist[0][0])[i] = 0;
       __syncthreads();
+      SPTS_FRESH_ROWS();
 #pragma unroll UNROLL_J
       for (int j = 0; j < J; ++j) {
-        const int i = base + 64 * j;
         const uint32_t key = key_at(j);
-        if (i < nfree && (key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & dmask], 1);
+        atomicAdd(&hist[w][(j < jf) & ((key & mask) == prefix) ? (int)((key >> shift) & dmask) : 256 + lane], 1);
       }
       __syncthreads();
       if (tid < 256) {
@@ -359,14 +372,14 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   // and rows equal to T; then each wave knows how many equal rows precede it
   // and so how many of its own equal rows it takes, and where its output starts.
   int n_gt = 0, n_eq = 0;
+  SPTS_FRESH_ROWS();
 #pragma unroll UNROLL_J
   for (int j = 0; j < J; ++j) {
-    const int i = base + 64 * j;
     const uint32_t key = key_at(j);
-    const bool forced = i >= nfree && i < n;
-    const bool free_row = i < nfree;
-    n_gt += (forced || (free_row && key > T)) ? 1 : 0;
-    n_eq += (free_row && key == T) ? 1 : 0;
+    const bool forced = (j >= jf) & (j < jv);
+    const bool free_row = j < jf;
+    n_gt += (forced | (free_row & (key > T))) ? 1 : 0;
+    n_eq += (free_row & (key == T)) ? 1 : 0;
   }
   n_gt = wave_sum_int(n_gt);
   n_eq = wave_sum_int(n_eq);
@@ -383,11 +396,12 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   const int e_total = __builtin_amdgcn_readlane(e_excl + e_q, NW - 1);
   if (need_eq >= e_total) {
     // every row equal to T is taken (no tie at the threshold): take key >= T
+    SPTS_FRESH_ROWS();
 #pragma unroll UNROLL_J
     for (int j = 0; j < J; ++j) {
       const int i = base + 64 * j;
       const uint32_t key = key_at(j);
-      const bool take = (i >= nfree) & (i < n) | (i < nfree) & (key >= T);
+      const bool take = (j >= jf) & (j < jv) | (j < jf) & (key >= T);
       const uint64_t tm = __ballot(take);
       const int pos = out + lanes_below(tm);
       if (take & (pos < k)) idx[pos] = i;  // exactly k are taken; the bound only guards memory
@@ -396,14 +410,15 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     return;
   }
   // a tie at the threshold: the lowest-index need_eq of the rows equal to T
+  SPTS_FRESH_ROWS();
 #pragma unroll UNROLL_J
   for (int j = 0; j < J; ++j) {
     const int i = base + 64 * j;
     const uint32_t key = key_at(j);
-    const bool free_row = i < nfree;
+    const bool free_row = j < jf;
     const bool eq = free_row & (key == T);
     const uint64_t eqm = __ballot(eq);
-    const bool take = (i >= nfree) & (i < n) | free_row & (key > T) |
+    const bool take = (j >= jf) & (j < jv) | free_row & (key > T) |
                       eq & (eq_before + lanes_below(eqm) < need_eq);
     const uint64_t tm = __ballot(take);
     const int pos = out + lanes_below(tm);
@@ -411,6 +426,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     out += __popcll(tm);
     eq_before += __popcll(eqm);
   }
+#undef SPTS_FRESH_ROWS
 }
 
 }  // namespace
