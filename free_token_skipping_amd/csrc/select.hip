@@ -44,17 +44,6 @@ __device__ __forceinline__ float fuse(float a, float b, float ma, float mb, floa
   return __fadd_rn(ta, tb);
 }
 
-__device__ float block_max(float v, float* sh) {
-  v = wave_max(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  float r = -INFINITY;
-  for (int i = 0; i < NW; ++i) r = fmaxf(r, sh[i]);
-  __syncthreads();
-  return r;
-}
-
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
@@ -88,6 +77,26 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_and(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane(
       (int)wave_scan_dpp(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a & b; }), 63);
+}
+
+__device__ __forceinline__ float wave_fmax(float v) {
+  const uint32_t r = wave_scan_dpp(__float_as_uint(v), __float_as_uint(-INFINITY), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+}
+
+// maxima of a and b over the workgroup (fmaxf: NaN is ignored), one barrier pair
+__device__ void block_max2(float a, float b, float* sh, float& ma, float& mb) {
+  a = wave_fmax(a);
+  b = wave_fmax(b);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) { sh[w] = a; sh[NW + w] = b; }
+  __syncthreads();
+  ma = -INFINITY;
+  mb = -INFINITY;
+  for (int i = 0; i < NW; ++i) { ma = fmaxf(ma, sh[i]); mb = fmaxf(mb, sh[NW + i]); }
+  __syncthreads();
 }
 
 // Suffix search over NB bins held NB/64 per lane, highest digit first (lane t
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   __shared__ uint32_t pool[CAP + 64];    // candidate keys, or the per-wave histograms of the fallback passes
   __shared__ int h8[256 + 64];           // the finishing wave's histogram
   __shared__ int tot_hist[256];
-  __shared__ float red[NW];
+  __shared__ float red[2 * NW];
   __shared__ uint32_t bits_sh[2][NW];
   __shared__ int cnt_sh[2][NW];
   __shared__ int sel[3];
@@ -151,11 +160,10 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   }
 
   float ma = 0.f, mb = 0.f;
-  if (s_b && !mult) {
+  if (IPT == 0 && s_b && !mult) {           // (with IPT > 0 the maxima come from the loaded rows below)
     float la = -INFINITY, lb = -INFINITY;
     for (int i = tid; i < n; i += TPB) { la = fmaxf(la, s_a[i]); lb = fmaxf(lb, s_b[i]); }
-    ma = block_max(la, red);
-    mb = block_max(lb, red);
+    block_max2(la, lb, red, ma, mb);
   }
   constexpr int UNROLL_J = IPT > 0 ? IPT : 8;      // workspace keys: 8 loads in flight per lane
   const int nfree = n - nf;
@@ -187,6 +195,16 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
         const int i = base + 64 * j;
         kr[IPT > 0 ? j : 0] = i < n ? __float_as_uint(s_a[i]) : 0u;
         xb[j] = i < n ? s_b[i] : 0.f;
+      }
+      if (!mult) {
+        float la = -INFINITY, lb = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+          const bool v = j < jv;
+          la = fmaxf(la, v ? __uint_as_float(kr[IPT > 0 ? j : 0]) : -INFINITY);
+          lb = fmaxf(lb, v ? xb[j] : -INFINITY);
+        }
+        block_max2(la, lb, red, ma, mb);
       }
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
