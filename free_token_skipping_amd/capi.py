@@ -24,6 +24,7 @@ EXPORTS = [
     "spts_status_name", "spts_check",
     "spts_probe_attention_workspace", "spts_score_topk_workspace", "spts_ltp_probe_workspace",
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
+    "spts_linear_kv_workspace", "spts_linear_swiglu_workspace",
     "spts_ltp_structured_workspace", "spts_ltp_probe_structured",
     "spts_decode_attention_workspace", "spts_decode_linear", "spts_decode_linear_rope", "spts_decode_swiglu",
     "spts_decode_attention", "spts_decode_step_workspace", "spts_decode_step",
@@ -49,6 +50,8 @@ _SIGS = {
     "spts_reduced_ffn_workspace": (_SZ, [_I, _I]),
     "spts_msdp_stage_workspace": (_SZ, [_I]),
     "spts_linear_workspace": (_SZ, [_I, _I, _I]),
+    "spts_linear_kv_workspace": (_SZ, [_I, _I, _I, _I]),
+    "spts_linear_swiglu_workspace": (_SZ, [_I, _I, _I]),
     "spts_ltp_structured_workspace": (_SZ, [_I, _I, _I, _I]),
     "spts_decode_attention_workspace": (_SZ, [_I, _I]),
     "spts_decode_linear": (_I, [_P, _P, _P, _I, _I, _P, _I]),
@@ -494,7 +497,7 @@ def spts_linear_kv(a, wk, wv, pos=None, table=None, a_rows=None):
     k_out = torch.empty((m, nk), dtype=torch.bfloat16, device=a.device)
     v_out = torch.empty((m, nv), dtype=torch.bfloat16, device=a.device)
     ctx = context()
-    h = ctx.bind(0, a.device)
+    h = ctx.bind(lib().spts_linear_kv_workspace(m, kdim, nk, nv), a.device)
     bf = torch.bfloat16
     _check(ctx, lib().spts_linear_kv(h, _ptr(a, bf, "a"), _ptr(a_rows, torch.int32, "a_rows"), m, kdim,
                                      _ptr(wk, bf, "wk"), nk, _ptr(wv, bf, "wv"), nv, _ptr(k_out, bf, "k_out"),
@@ -510,7 +513,7 @@ def spts_linear_swiglu(a, w_gate, w_up, a_rows=None, out=None):
     if out is None:
         out = torch.empty((m, f), dtype=torch.bfloat16, device=a.device)
     ctx = context()
-    h = ctx.bind(0, a.device)
+    h = ctx.bind(lib().spts_linear_swiglu_workspace(m, kdim, f), a.device)
     bf = torch.bfloat16
     _check(ctx, lib().spts_linear_swiglu(h, _ptr(a, bf, "a"), _ptr(a_rows, torch.int32, "a_rows"), m, kdim,
                                          _ptr(w_gate, bf, "w_gate"), _ptr(w_up, bf, "w_up"), f,

@@ -152,6 +152,14 @@ size_t spts_linear_workspace(int m, int kdim, int n) {
   if (m <= 0 || kdim <= 0 || n <= 0) return 0;
   return gemm_split_workspace(m, kdim, n, EPI_STORE);
 }
+size_t spts_linear_kv_workspace(int m, int kdim, int nk, int nv) {
+  if (m <= 0 || kdim <= 0 || nk <= 0 || nv <= 0) return 0;
+  return gemm_split_workspace(m, kdim, nk + nv, EPI_KV);
+}
+size_t spts_linear_swiglu_workspace(int m, int kdim, int f) {
+  if (m <= 0 || kdim <= 0 || f <= 0) return 0;
+  return gemm_split_workspace(m, kdim, 2 * f, EPI_SWIGLU);
+}
 size_t spts_reduced_ffn_workspace(int k, int f) {
   if (k <= 0 || f <= 0) return 0;
   return ((size_t)k * f * 2 + 255) & ~(size_t)255;
@@ -383,6 +391,7 @@ spts_status spts_linear_kv(spts_ctx* ctx, const void* a, const int32_t* a_rows, 
   g.ldb = kdim; g.n = nk + nv; g.n0 = nk;
   g.out = k_out; g.ldc = nk; g.out2 = v_out; g.ldc2 = nv;
   g.pos = pos; g.rope_table = table;
+  g.partial = reinterpret_cast<float*>(ctx->ws); g.partial_bytes = ctx->ws_bytes;
   return hip_status(ctx, launch_gemm(g, EPI_KV, ctx->stream), "linear_kv");
 }
 
@@ -399,6 +408,7 @@ spts_status spts_linear_swiglu(spts_ctx* ctx, const void* a, const int32_t* a_ro
   g.a = reinterpret_cast<const uint16_t*>(a); g.a_rows = a_rows; g.m = m; g.k = kdim; g.lda = kdim;
   g.b0 = reinterpret_cast<const uint16_t*>(w_gate); g.b1 = reinterpret_cast<const uint16_t*>(w_up);
   g.ldb = kdim; g.n = 2 * f; g.out = h_out; g.ldc = f;
+  g.partial = reinterpret_cast<float*>(ctx->ws); g.partial_bytes = ctx->ws_bytes;
   return hip_status(ctx, launch_gemm(g, EPI_SWIGLU, ctx->stream), "linear_swiglu");
 }
 

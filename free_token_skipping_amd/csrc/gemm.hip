@@ -37,190 +37,14 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
+// Epilogue of one finished 256 x 256 tile (STORE, ROPE, KV, SWIGLU,
+// SWIGLU_SPLIT, SPLIT).  Lane holds C[row][col] for row = tile_m*BM + wm*64 +
+// i*32 + l32 and col = (tile base) + wn*128 + j*32 + q*8 + half*4 + e, with
+// accumulator register r = q*4 + e.
 template <int EPI, bool GATHER>
-__global__ __launch_bounds__(NTHREADS, 1)
-void gemm_tn_kernel(GemmArgs g) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* As = smem;                       // [2][BM*BK]
-  uint16_t* Bs = smem + 2 * TILE_ELEMS;      // [2][BN*BK]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS addresses in SGPRs
-  const int wm = wave >> 1, wn = wave & 1;          // 4 x 2 waves
-  const int l32 = lane & 31, half = lane >> 5;
-
-  // ---- tile order.  Workgroups are dealt round-robin to the 8 XCDs, so
-  // workgroup b runs on XCD b % 8.  Each XCD gets a contiguous run of the
-  // logical tile order, and that order walks groups of GROUP_M row tiles
-  // across all column tiles, so the ~32 tiles resident on one XCD at a time
-  // form a 4 x 8 block that shares A and B k-slices in that XCD's L2.
-  const int tiles_m = (g.m + BM - 1) / BM;
+__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16 (&acc)[2][4], int tile_m, int tile_n,
+                                           bool part1, int wm, int wn, int l32, int half) {
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
-  const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
-  const int ksplit = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
-  const int total = tiles_m * tiles_n * ksplit;
-  const int per_xcd = (total + 7) / 8;
-  const int logical_k = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
-  if (logical_k >= total) return;                     // padding workgroups of the last XCD run
-  const int kslice = logical_k % ksplit;              // split-K slice (0 without split)
-  const int logical = logical_k / ksplit;
-  constexpr int GROUP_M = 4;
-  const int in_group = GROUP_M * tiles_n;
-  const int first_m = (logical / in_group) * GROUP_M;
-  const int gm = min(GROUP_M, tiles_m - first_m);
-  const int tile_m = first_m + (logical % in_group) % gm;
-  const int tile_n = (logical % in_group) / gm;
-
-  // KV: tiles at or past column n0 read b1 and write out2
-  const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
-
-  // ---- direct global -> LDS staging by waves 0-3.  Loading wave w,
-  // instruction i writes the 1 KiB block of tile rows rb*8 .. rb*8+7,
-  // rb = 4*i + w; lane L lands at row r = rb*8 + L/8, physical chunk L%8, so
-  // it fetches the logical chunk (L%8) ^ ((r >> 1) & 7) -- the swizzle of
-  // swz() applied on the global side.
-  const bool loader = wave < 4;
-  const int lw = wave & 3;
-  const int ld_sub = lane >> 3;                       // row within the 8-row block
-  uint32_t a_off[8], b_off[8];                        // byte offsets of the staged rows
-  unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rb = 4 * i + lw;
-    const int r = rb * 8 + ld_sub;                    // row within the 256-row tile
-    const int ld_ch = (lane & 7) ^ ((r >> 1) & 7);    // logical 16-byte chunk fetched
-    int ar = tile_m * BM + r;
-    if (ar >= g.m) ar = g.m - 1;
-    if (GATHER) ar = g.a_rows[ar];
-    a_off[i] = ((uint32_t)ar * (uint32_t)g.lda + ld_ch * 8) * 2u;
-    if (kSwiglu) {
-      // wave column block r / 128: rows 0..63 gate, 64..127 up, same 64 outputs
-      const int within = r & 127;
-      const uint32_t brow = (uint32_t)tile_n * 128 + (r >> 7) * 64 + (within & 63);
-      if (within >= 64) b_from_up |= 1u << i;
-      b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
-    } else {
-      const uint32_t brow = (uint32_t)(tile_n * BN - (part1 ? g.n0 : 0)) + r;
-      b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
-    }
-  }
-  const char* abase = reinterpret_cast<const char*>(g.a);
-  const char* b0base = reinterpret_cast<const char*>(part1 ? g.b1 : g.b0);
-  const char* b1base = reinterpret_cast<const char*>(g.b1);
-  const int KT = g.k / BK / ksplit;                    // k-steps of this slice
-  const int kt_base = kslice * KT;
-
-  auto issue = [&](int kt_local, int stage) {
-    if (!loader) return;
-    const int kt = kt_base + kt_local;
-    const uint32_t ka = (uint32_t)kt * BK * 2u;
-    const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
-    uint16_t* a_s = As + stage * TILE_ELEMS;
-    uint16_t* b_s = Bs + stage * TILE_ELEMS;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rb = 4 * i + lw;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(abase + a_off[i] + ka),
-          (__attribute__((address_space(3))) void*)(a_s + rb * 512), 16, 0, 0);
-      const char* bb = (kSwiglu && ((b_from_up >> i) & 1u)) ? b1base : b0base;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(bb + b_off[i] + kb),
-          (__attribute__((address_space(3))) void*)(b_s + rb * 512), 16, 0, 0);
-    }
-  };
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // k-step kt reads stage kt & 1 while the loads of k-step kt+1 fill the
-  // other stage; the wait + barrier at its end hands both stages over.
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    // the last k-step reloads its own tile into the idle stage (never read)
-    issue(kt + 1 < KT ? kt + 1 : kt, cur ^ 1);
-    const uint16_t* a_s = As + cur * TILE_ELEMS;
-    const uint16_t* b_s = Bs + cur * TILE_ELEMS;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + half;
-      bf16x8 af[2], bfm[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 64 + i * 32 + l32, ch));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfm[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[j], af[i], acc[i][j]);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-  // ------------------------------------------------------------ epilogues
-  // lane holds C[row][col] for row = tile_m*BM + wm*64 + i*32 + l32 and
-  // col = (tile base) + wn*128 + j*32 + q*8 + half*4 + e, r = q*4 + e.
-  if (EPI == EPI_PARTIAL) {
-    float* part = g.partial + (long)kslice * g.m * g.n;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = tile_m * BM + wm * 64 + i * 32 + l32;
-      if (row >= g.m) continue;
-      float* prow = part + (long)row * g.n;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4;
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
-          *reinterpret_cast<f32x4*>(prow + col) = v;
-        }
-    }
-    return;
-  }
-  if (EPI == EPI_SUMSQ) {
-    float* red = reinterpret_cast<float*>(smem);   // [4 wm][2 i][32 rows] from wn == 1
-    float ss[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      float t = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t += acc[i][j][r] * acc[i][j][r];
-      t += __shfl_xor(t, 32);
-      ss[i] = t;
-    }
-    if (wn == 1 && half == 0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) red[(wm * 2 + i) * 32 + l32] = ss[i];
-    }
-    __syncthreads();
-    if (wn == 0 && half == 0) {
-      float* out = reinterpret_cast<float*>(g.out);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = tile_m * BM + wm * 64 + i * 32 + l32;
-        if (row < g.m) out[(long)row * tiles_n + tile_n] = ss[i] + red[(wm * 2 + i) * 32 + l32];
-      }
-    }
-    return;
-  }
-
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = tile_m * BM + wm * 64 + i * 32 + l32;
@@ -316,6 +140,301 @@ void gemm_tn_kernel(GemmArgs g) {
   }
 }
 
+// Logical tile -> (tile_m, tile_n): the order walks groups of GROUP_M row
+// tiles across all column tiles.
+__device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, int& tile_m, int& tile_n) {
+  constexpr int GROUP_M = 4;
+  const int in_group = GROUP_M * tiles_n;
+  const int first_m = (logical / in_group) * GROUP_M;
+  const int gm = min(GROUP_M, tiles_m - first_m);
+  tile_m = first_m + (logical % in_group) % gm;
+  tile_n = (logical % in_group) / gm;
+}
+
+// One fp32 tail piece of a tile, in the lanes' own register order: 32 groups
+// of 16 bytes per thread, group-major, so each store covers 8 KiB contiguously.
+__device__ __forceinline__ float* piece_base(const GemmArgs& g, int slot, int tid) {
+  return g.partial + (size_t)slot * (BM * BN) + tid * 4;
+}
+__device__ __forceinline__ int piece_group(int i, int j, int q) { return ((i * 4 + j) * 4 + q) * (NTHREADS * 4); }
+
+template <int EPI, bool GATHER>
+__global__ __launch_bounds__(NTHREADS, 1)
+void gemm_tn_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* As = smem;                       // [2][BM*BK]
+  uint16_t* Bs = smem + 2 * TILE_ELEMS;      // [2][BN*BK]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS addresses in SGPRs
+  const int wm = wave >> 1, wn = wave & 1;          // 4 x 2 waves
+  const int l32 = lane & 31, half = lane >> 5;
+
+  // ---- work of this workgroup.  Workgroups are dealt round-robin to the 8
+  // XCDs, so workgroup b runs on XCD b % 8.  Each XCD gets a contiguous run of
+  // the logical tile order (see tile_of), so the ~32 tiles resident on one XCD
+  // at a time form a 4 x 8 block that shares A and B k-slices in that XCD's L2.
+  const int tiles_m = (g.m + BM - 1) / BM;
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
+  constexpr bool kTail = (EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_KV || EPI == EPI_SWIGLU);
+  const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
+  const int ksplit = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
+  const int b = (int)blockIdx.x;
+  int logical, kslice = 0, k0, k1;
+  int slot = -1, step = 0;             // tail piece slot; ends workgroups: tail tiles between jobs
+  if (!kTail || g.tail_tiles == 0 || b < g.tail_full) {
+    const int total = (kTail && g.tail_tiles) ? g.tail_full : tiles_m * tiles_n * ksplit;
+    const int per_xcd = (total + 7) / 8;
+    const int logical_k = (b & 7) * per_xcd + (b >> 3);
+    if (logical_k >= total) return;                   // padding workgroups of the last XCD run
+    kslice = logical_k % ksplit;                      // split-K slice (0 without split)
+    logical = logical_k / ksplit;
+    k0 = kslice * (g.k / BK / ksplit);
+    k1 = k0 + g.k / BK / ksplit;
+  } else {
+    // tail units after the tail_full whole tiles (tail_full is a multiple of
+    // 256, so b % 8 is still the XCD); units of one piece index (equal
+    // pieces) or of one kind (heads, ends) run side by side at the same k.
+    const int tb = b - g.tail_full;
+    const int T = g.tail_tiles, KT = g.k / BK;
+    const int E = g.tail_ends ? (T + g.tail_ends - 1) / g.tail_ends : 0;
+    const int units = g.tail_ends ? T + E : T * g.tail_np;
+    const int per_xcd = (units + 7) / 8;
+    const int u = (tb & 7) * per_xcd + (tb >> 3);
+    if (u >= units) return;
+    int tt;
+    if (g.tail_ends == 0) {
+      const int piece = u / T;
+      tt = u - piece * T;
+      k0 = piece * KT / g.tail_np;
+      k1 = (piece + 1) * KT / g.tail_np;
+      slot = u;
+    } else if (u < T) {
+      tt = u; k0 = 0; k1 = g.tail_kx; slot = u;
+    } else {
+      tt = u - T; k0 = g.tail_kx; k1 = KT; slot = T + tt; step = E;
+    }
+    logical = g.tail_full + tt;
+  }
+
+  for (;;) {
+    int tile_m, tile_n;
+    tile_of(logical, tiles_m, tiles_n, tile_m, tile_n);
+
+    // KV: tiles at or past column n0 read b1 and write out2
+    const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
+
+    // ---- direct global -> LDS staging by waves 0-3.  Loading wave w,
+    // instruction i writes the 1 KiB block of tile rows rb*8 .. rb*8+7,
+    // rb = 4*i + w; lane L lands at row r = rb*8 + L/8, physical chunk L%8, so
+    // it fetches the logical chunk (L%8) ^ ((r >> 1) & 7) -- the swizzle of
+    // swz() applied on the global side.
+    const bool loader = wave < 4;
+    const int lw = wave & 3;
+    const int ld_sub = lane >> 3;                       // row within the 8-row block
+    uint32_t a_off[8], b_off[8];                        // byte offsets of the staged rows
+    unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rb = 4 * i + lw;
+      const int r = rb * 8 + ld_sub;                    // row within the 256-row tile
+      const int ld_ch = (lane & 7) ^ ((r >> 1) & 7);    // logical 16-byte chunk fetched
+      int ar = tile_m * BM + r;
+      if (ar >= g.m) ar = g.m - 1;
+      if (GATHER) ar = g.a_rows[ar];
+      a_off[i] = ((uint32_t)ar * (uint32_t)g.lda + ld_ch * 8) * 2u;
+      if (kSwiglu) {
+        // wave column block r / 128: rows 0..63 gate, 64..127 up, same 64 outputs
+        const int within = r & 127;
+        const uint32_t brow = (uint32_t)tile_n * 128 + (r >> 7) * 64 + (within & 63);
+        if (within >= 64) b_from_up |= 1u << i;
+        b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
+      } else {
+        const uint32_t brow = (uint32_t)(tile_n * BN - (part1 ? g.n0 : 0)) + r;
+        b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
+      }
+    }
+    const char* abase = reinterpret_cast<const char*>(g.a);
+    const char* b0base = reinterpret_cast<const char*>(part1 ? g.b1 : g.b0);
+    const char* b1base = reinterpret_cast<const char*>(g.b1);
+    const int KT = k1 - k0;                              // k-steps of this job
+    const int kt_base = k0;
+
+    auto issue = [&](int kt_local, int stage) {
+      if (!loader) return;
+      const int kt = kt_base + kt_local;
+      const uint32_t ka = (uint32_t)kt * BK * 2u;
+      const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
+      uint16_t* a_s = As + stage * TILE_ELEMS;
+      uint16_t* b_s = Bs + stage * TILE_ELEMS;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rb = 4 * i + lw;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(abase + a_off[i] + ka),
+            (__attribute__((address_space(3))) void*)(a_s + rb * 512), 16, 0, 0);
+        const char* bb = (kSwiglu && ((b_from_up >> i) & 1u)) ? b1base : b0base;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(bb + b_off[i] + kb),
+            (__attribute__((address_space(3))) void*)(b_s + rb * 512), 16, 0, 0);
+      }
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // k-step kt reads stage kt & 1 while the loads of k-step kt+1 fill the
+    // other stage; the wait + barrier at its end hands both stages over.
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      // the last k-step reloads its own tile into the idle stage (never read)
+      issue(kt + 1 < KT ? kt + 1 : kt, cur ^ 1);
+      const uint16_t* a_s = As + cur * TILE_ELEMS;
+      const uint16_t* b_s = Bs + cur * TILE_ELEMS;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int ch = kk * 2 + half;
+        bf16x8 af[2], bfm[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 64 + i * 32 + l32, ch));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bfm[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[j], af[i], acc[i][j]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+
+    if (kTail && slot >= 0) {
+      float* ps = piece_base(g, slot, tid);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
+            *reinterpret_cast<f32x4*>(ps + piece_group(i, j, q)) = v;
+          }
+      if (step == 0) return;
+      logical += step;
+      slot += step;
+      if (logical - g.tail_full >= g.tail_tiles) return;
+      continue;
+    }
+
+    // ------------------------------------------------------------ epilogues
+    // lane holds C[row][col] for row = tile_m*BM + wm*64 + i*32 + l32 and
+    // col = (tile base) + wn*128 + j*32 + q*8 + half*4 + e, r = q*4 + e.
+    if (EPI == EPI_PARTIAL) {
+      float* part = g.partial + (long)kslice * g.m * g.n;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = tile_m * BM + wm * 64 + i * 32 + l32;
+        if (row >= g.m) continue;
+        float* prow = part + (long)row * g.n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4;
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
+            *reinterpret_cast<f32x4*>(prow + col) = v;
+          }
+      }
+      return;
+    }
+    if (EPI == EPI_SUMSQ) {
+      float* red = reinterpret_cast<float*>(smem);   // [4 wm][2 i][32 rows] from wn == 1
+      float ss[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t += acc[i][j][r] * acc[i][j][r];
+        t += __shfl_xor(t, 32);
+        ss[i] = t;
+      }
+      if (wn == 1 && half == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) red[(wm * 2 + i) * 32 + l32] = ss[i];
+      }
+      __syncthreads();
+      if (wn == 0 && half == 0) {
+        float* out = reinterpret_cast<float*>(g.out);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = tile_m * BM + wm * 64 + i * 32 + l32;
+          if (row < g.m) out[(long)row * tiles_n + tile_n] = ss[i] + red[(wm * 2 + i) * 32 + l32];
+        }
+      }
+      return;
+    }
+
+    store_tile<EPI, GATHER>(g, acc, tile_m, tile_n, part1, wm, wn, l32, half);
+    return;
+  }
+}
+
+// Tail fixup: tile tail_full + blockIdx.x is the fp32 sum of its tail_np
+// pieces, added in k order, then finished by the GEMM's own epilogue.
+template <int EPI, bool GATHER>
+__global__ __launch_bounds__(NTHREADS) void gemm_tail_fixup_kernel(GemmArgs g) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, half = lane >> 5;
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU);
+  const int tiles_m = (g.m + BM - 1) / BM;
+  const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
+  const int tt = (int)blockIdx.x;
+  int tile_m, tile_n;
+  tile_of(g.tail_full + tt, tiles_m, tiles_n, tile_m, tile_n);
+  const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int p = 0; p < g.tail_np; ++p) {
+    const float* ps = piece_base(g, p * g.tail_tiles + tt, tid);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ps + piece_group(i, j, q));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][q * 4 + e] += v[e];
+        }
+  }
+  store_tile<EPI, GATHER>(g, acc, tile_m, tile_n, part1, wm, wn, l32, half);
+}
+
 // Split-K finish: sum the fp32 slices in slice order and apply the epilogue.
 // Thread = (row, 4-column group); for RoPE only groups in the first half of
 // a 128-wide head work, each handling its pair group c+64.
@@ -399,45 +518,103 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
     attr_devices.fetch_or(bit, std::memory_order_release);
   }
   const int ks = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
-  const int grid = ((tiles_m * tiles_n * ks + 7) / 8) * 8;     // a multiple of the 8 XCDs
+  int grid = ((tiles_m * tiles_n * ks + 7) / 8) * 8;           // a multiple of the 8 XCDs
+  if (g.tail_tiles > 0) {
+    const int units = g.tail_ends ? g.tail_tiles + (g.tail_tiles + g.tail_ends - 1) / g.tail_ends
+                                  : g.tail_tiles * g.tail_np;
+    grid = g.tail_full + ((units + 7) / 8) * 8;
+  }
   hipLaunchKernelGGL((gemm_tn_kernel<EPI, GATHER>), dim3(grid), dim3(NTHREADS), lds, s, g);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if constexpr (EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_KV || EPI == EPI_SWIGLU) {
+    if (e == hipSuccess && g.tail_tiles > 0) {
+      hipLaunchKernelGGL((gemm_tail_fixup_kernel<EPI, GATHER>), dim3(g.tail_tiles), dim3(NTHREADS), 0, s, g);
+      e = hipGetLastError();
+    }
+  }
+  return e;
 }
 
-// Cost model for the split count: workgroup waves over 256 CUs times the time
-// of one 256x256 tile over its k range, plus the partial-sum round trip.
-int choose_ksplit(int m, int k, int n) {
-  const double tiles = (double)((m + BM - 1) / BM) * (n / BN);
-  const double per_tile_s = 2.0 * BM * BN * (double)k / 4.4e12;     // ~1.1 PFLOP/s over 256 CUs
-  int best = 1;
-  double best_t = std::ceil(tiles / 256.0) * per_tile_s;
-  for (int ks = 2; ks <= 16; ++ks) {
-    if (k % (ks * BK) != 0) continue;
-    const double t = std::ceil(tiles * ks / 256.0) * per_tile_s / ks + (double)ks * m * n * 8.0 / 5.0e12 + 4e-6;
-    if (t < 0.9 * best_t) { best = ks; best_t = t; }
+// Cost model: workgroup rounds over 256 CUs times the time of one 256x256 tile
+// over its k range, plus the round trip of any fp32 partial results.
+//  - split-K (ksplit > 1): every tile in ksplit slices, summed by a reduce pass.
+//  - tail split: the whole rounds run unsplit, and the tiles of the last,
+//    partly filled round are cut along k so that they fill all 256 CUs.  With
+//    at most 128 tail tiles each is cut into equal pieces, one workgroup per
+//    piece; with more, each tile's head [0, kx) gets a workgroup and the other
+//    workgroups take the ends [kx, KT) of `ends` tiles each, kx chosen so a
+//    head and `ends` ends take equally long.  Workgroups that run side by
+//    side then sit at the same k, as in the unsplit rounds, so they still
+//    share operand k-slices in L2.  A second launch adds each tile's pieces.
+constexpr int kCUs = 256;
+constexpr double kTileFlops = 4.4e12;   // per-CU rate on one tile: ~1.1 PFLOP/s over 256 CUs
+constexpr double kPartialBps = 4.5e12;  // fp32 partials written, then read back
+
+struct Plan {
+  int ksplit = 1;
+  int full = 0, tiles = 0, np = 0, ends = 0, kx = 0;   // tail split when tiles > 0
+  size_t ws = 0;                                       // fp32 workspace bytes
+  double t = 0;                                        // modeled seconds
+};
+
+Plan choose_plan(int m, int k, int n, int epi) {
+  const bool swiglu = (epi == EPI_SWIGLU || epi == EPI_SWIGLU_SPLIT);
+  const int tiles = ((m + BM - 1) / BM) * (swiglu ? (n / 2) / 128 : n / BN);
+  const int KT = k / BK;
+  const double tile_s = 2.0 * BM * BN * (double)k / kTileFlops;
+  Plan best;
+  best.t = std::ceil(tiles / (double)kCUs) * tile_s;
+  if (epi == EPI_STORE || epi == EPI_ROPE || epi == EPI_SPLIT) {
+    for (int ks = 2; ks <= 16; ++ks) {
+      if (k % (ks * BK) != 0) continue;
+      const double t = std::ceil((double)tiles * ks / kCUs) * tile_s / ks + (double)ks * m * n * 8.0 / 5.0e12 + 4e-6;
+      if (t < 0.9 * best.t) {
+        best = Plan{};
+        best.ksplit = ks; best.t = t; best.ws = (size_t)ks * m * n * sizeof(float);
+      }
+    }
+  }
+  const int T = tiles % kCUs;
+  if ((epi == EPI_STORE || epi == EPI_ROPE || epi == EPI_KV || epi == EPI_SWIGLU) && T != 0 && KT >= 2) {
+    Plan p;
+    p.full = tiles - T;
+    p.tiles = T;
+    double steps;                        // k-steps of the longest tail workgroup
+    if (2 * T <= kCUs) {
+      p.np = std::min(kCUs / T, KT);
+      steps = (KT + p.np - 1) / p.np;
+    } else {
+      p.np = 2;
+      p.ends = (T + (kCUs - T) - 1) / (kCUs - T);
+      p.kx = std::min(KT - 1, std::max(1, (int)std::lround((double)KT * p.ends / (p.ends + 1))));
+      steps = std::max(p.kx, p.ends * (KT - p.kx));
+    }
+    p.ws = (size_t)T * p.np * BM * BN * sizeof(float);
+    p.t = (p.full / kCUs + steps / KT) * tile_s + 2.0 * p.ws / kPartialBps + 6e-6 + p.ends * 2e-6;
+    if (p.t < 0.97 * best.t) best = p;
   }
   return best;
 }
 
 }  // namespace
 
-int gemm_ksplit(int m, int k, int n, int epi) {
-  if (epi != EPI_STORE && epi != EPI_ROPE && epi != EPI_SPLIT) return 1;
-  return choose_ksplit(m, k, n);
-}
+int gemm_ksplit(int m, int k, int n, int epi) { return choose_plan(m, k, n, epi).ksplit; }
 
-size_t gemm_split_workspace(int m, int k, int n, int epi) {
-  const int ks = gemm_ksplit(m, k, n, epi);
-  return ks > 1 ? (size_t)ks * m * n * sizeof(float) : 0;
-}
+size_t gemm_split_workspace(int m, int k, int n, int epi) { return choose_plan(m, k, n, epi).ws; }
 
 hipError_t launch_gemm(const GemmArgs& g0, int epi, hipStream_t s) {
   const bool gather = g0.a_rows != nullptr;
   GemmArgs g = g0;
   g.ksplit = 1;
-  const int ks = gemm_ksplit(g.m, g.k, g.n, epi);
-  if (ks > 1 && g.partial && g.partial_bytes >= (size_t)ks * g.m * g.n * sizeof(float)) {
-    g.ksplit = ks;
+  g.tail_full = g.tail_tiles = g.tail_np = g.tail_ends = g.tail_kx = 0;
+  const Plan plan = choose_plan(g.m, g.k, g.n, epi);
+  const bool room = plan.ws > 0 && g.partial && g.partial_bytes >= plan.ws;
+  if (room && plan.tiles > 0) {
+    g.tail_full = plan.full; g.tail_tiles = plan.tiles; g.tail_np = plan.np;
+    g.tail_ends = plan.ends; g.tail_kx = plan.kx;
+  }
+  if (room && plan.ksplit > 1) {
+    g.ksplit = plan.ksplit;
     hipError_t e = gather ? launch_one<EPI_PARTIAL, true>(g, s) : launch_one<EPI_PARTIAL, false>(g, s);
     if (e != hipSuccess) return e;
     const long groups = (long)g.m * (g.n / 4);

@@ -41,13 +41,21 @@ struct GemmArgs {
   int n0;                   // KV: columns taken from b0 (a multiple of 256)
   void* out2;               // KV: output of the b1 columns
   int ldc2;
-  float* partial;           // split-K workspace (nullable: never split)
+  float* partial;           // split-K / tail-piece workspace (nullable: never split)
   size_t partial_bytes;
   int ksplit;               // set by the launcher
+  // Tail split, set by the launcher (tail_tiles == 0: off).  Logical tiles
+  // below tail_full run whole; each of the last tail_tiles tiles is cut along
+  // k into tail_np pieces whose fp32 sums a second launch adds and finishes.
+  // tail_ends == 0: tail_np equal pieces, one workgroup each.  tail_ends > 0:
+  // a head [0, tail_kx) per workgroup, and each remaining workgroup takes the
+  // ends [tail_kx, KT) of up to tail_ends tiles.
+  int tail_full, tail_tiles, tail_np, tail_ends, tail_kx;
 };
 
 // Split count the launcher would use for this problem (1 = no split) and the
-// workspace it then needs.
+// workspace it then needs (split-K slices or tail pieces, whichever the
+// launcher picks; 0 when it runs the problem unsplit).
 int gemm_ksplit(int m, int k, int n, int epilogue);
 size_t gemm_split_workspace(int m, int k, int n, int epilogue);
 hipError_t launch_gemm(const GemmArgs& g, int epilogue, hipStream_t s);

@@ -83,11 +83,17 @@ size_t spts_decode_attention_workspace(int L, int Hq);
 size_t spts_decode_step_workspace(int max_len, int Hq, int f);
 size_t spts_reduced_ffn_workspace(int k, int f);
 size_t spts_msdp_stage_workspace(int n_prev);
-/* Workspace with which spts_linear / spts_linear_rope split the inner
- * dimension across workgroups (fp32 partial sums, then a fixed-order
- * reduction); 0 when the problem is not split.  Smaller workspaces make the
- * call run unsplit (same result, possibly slower). */
+/* Workspace with which spts_linear / spts_linear_rope, spts_linear_kv and
+ * spts_linear_swiglu split the inner dimension across workgroups; 0 when the
+ * problem runs unsplit.  The split is either of every 256 x 256 output tile
+ * (linear / rope only) or of the tiles of the last, partly filled round of
+ * workgroups over the 256 CUs, so that round fills the chip.  The fp32
+ * partial sums are added in a fixed order, so a given problem always gives
+ * the same result; a smaller workspace makes the call run unsplit (same
+ * result up to the order of the fp32 additions, possibly slower). */
 size_t spts_linear_workspace(int m, int kdim, int n);
+size_t spts_linear_kv_workspace(int m, int kdim, int nk, int nv);
+size_t spts_linear_swiglu_workspace(int m, int kdim, int f);
 
 /* ----------------------------------------------------------------- PAP */
 
@@ -235,7 +241,8 @@ spts_status spts_msdp_stage(spts_ctx* ctx, const float* scores, int n_prev, int 
  *   accumulate == 1: out[o(i), :] = bf16(out[o(i), :] + bf16(A W^T)[i])
  *   with o(i) = out_rows[i] if out_rows != NULL (scatter on store), else i.
  * Requires kdim % 64 == 0, n % 256 == 0.  These projections are needed because
- * every step of the path runs in this library. */
+ * every step of the path runs in this library.
+ * Workspace (optional): spts_linear_workspace (spts_linear_rope too). */
 spts_status spts_linear(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
                         const void* w, int n, void* out, const int32_t* out_rows, int accumulate);
 
@@ -253,9 +260,11 @@ spts_status spts_linear_rope(spts_ctx* ctx, const void* a, const int32_t* a_rows
  *     v_out[i, :] = bf16(A Wv^T)[i],         A row i = a[a_rows ? a_rows[i] : i]
  *   a [*, kdim] bf16; wk [nk, kdim], wv [nv, kdim] bf16; k_out [m, nk],
  *   v_out [m, nv] bf16.  RoPE as in spts_linear_rope (pos, table required
- *   together).  Results equal spts_linear_rope / spts_linear on the same
- *   inputs; one launch fills the GPU better than two thin ones.
- * Requires kdim % 64 == 0, nk % 256 == 0, nv % 256 == 0. */
+ *   together).  Results agree with spts_linear_rope / spts_linear on the same
+ *   inputs up to the order of the fp32 additions; one launch fills the GPU
+ *   better than two thin ones.
+ * Requires kdim % 64 == 0, nk % 256 == 0, nv % 256 == 0.
+ * Workspace (optional): spts_linear_kv_workspace. */
 spts_status spts_linear_kv(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
                            const void* wk, int nk, const void* wv, int nv, void* k_out,
                            void* v_out, const int32_t* pos, const float* table);
@@ -263,7 +272,8 @@ spts_status spts_linear_kv(spts_ctx* ctx, const void* a, const int32_t* a_rows, 
 /* The first half of the reduced FFN as its own call:
  *     h_out[i, :] = bf16(silu(A Wg^T) * (A Wu^T))[i],  A row i = a[a_rows ? a_rows[i] : i]
  *   a [*, kdim] bf16, w_gate, w_up [f, kdim] bf16, h_out [m, f] bf16.
- * Requires kdim % 64 == 0, f % 128 == 0.  ([SPTS] Fig. 2(b), reduced feed-forward.) */
+ * Requires kdim % 64 == 0, f % 128 == 0.  ([SPTS] Fig. 2(b), reduced feed-forward.)
+ * Workspace (optional): spts_linear_swiglu_workspace. */
 spts_status spts_linear_swiglu(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
                                const void* w_gate, const void* w_up, int f, void* h_out);
 

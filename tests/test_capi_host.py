@@ -60,6 +60,33 @@ def test_workspace_queries(L):
     assert L.spts_probe_attention_workspace(0, 64, 32) == 0
 
 
+def test_gemm_split_plans(L):
+    """The split the GEMM launcher picks, read from the workspace it asks for:
+    split-K into ks slices needs ks*m*n fp32, a tail split T*np fp32 tiles of
+    256 x 256 (T tiles of the last, partly filled round over 256 CUs, each
+    cut into np pieces).  Shapes are the MSDP stack's at 32K tokens."""
+    tile = 256 * 256 * 4
+    lin, kv, swi = L.spts_linear_workspace, L.spts_linear_kv_workspace, L.spts_linear_swiglu_workspace
+    # FFN down projection, kept rows of the four stages (14336 -> 4096)
+    assert lin(6881, 14336, 4096) == 176 * 2 * tile       # 432 tiles: heads and ends
+    assert lin(5161, 14336, 4096) == 80 * 3 * tile        # 336 tiles: 3 equal pieces
+    assert lin(4014, 14336, 4096) == 0                    # 256 tiles: one whole round
+    assert lin(2867, 14336, 4096) == 192 * 2 * tile       # 192 tiles: heads and ends
+    # Q / O projections (4096 -> 4096): only the 336-tile stage pays
+    assert lin(6881, 4096, 4096) == 0
+    assert lin(5161, 4096, 4096) == 80 * 3 * tile
+    assert lin(2867, 4096, 4096) == 0
+    assert lin(64, 4096, 4096) == 16 * 64 * 4096 * 4      # probe queries: split-K, 16 slices
+    # gate/up (4096 -> 2 x 14336)
+    assert swi(6881, 4096, 14336) == 0                    # 3024 tiles: the tail is nearly full
+    assert swi(5161, 4096, 14336) == 48 * 5 * tile
+    assert swi(2867, 4096, 14336) == 64 * 4 * tile
+    # K/V over all candidates (4096 -> 1024 + 1024)
+    assert kv(19661, 4096, 1024, 1024) == 104 * 2 * tile
+    assert kv(32768, 4096, 1024, 1024) == 0
+    assert kv(0, 4096, 1024, 1024) == 0 and swi(10, 4096, 0) == 0
+
+
 def test_probe_validation(L, ctx):
     f = L.spts_probe_attention
     assert f(ctx, capi.BF16, None, FAKE, 100, 64, 32, 8, 128, 0.1, FAKE) == INVALID
