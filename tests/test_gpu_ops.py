@@ -337,14 +337,15 @@ def test_ltp_probe(n, d, r):
     assert (np.abs(got - ref) / ref).max() < 2e-5         # per row, not only at the max
 
 
-def test_ltp_full_size_sampled():
-    n, d, r = 32768, 4096, 256
-    _log("ltp full size (sampled rows)")
+@pytest.mark.parametrize("n", [32768, 19661])          # the 32K input and the first MSDP stage
+def test_ltp_full_size_sampled(n):
+    d, r = 4096, 256
+    _log(f"ltp full size n={n} (sampled rows)")
     z = W.randn((n, d), seed=38)
     u_t = W.randn((r, d), seed=39, std=0.3)
     v_t = W.randn((d, r), seed=40, std=0.06)
     L = capi.spts_ltp_probe(_cuda(z), _cuda(u_t), _cuda(v_t))
-    pick = np.random.default_rng(3).choice(n, 256, replace=False)
+    pick = np.concatenate([np.random.default_rng(3).choice(n, 256, replace=False), [n - 1]])
     ref = ltp.ltp_scores(W.as_f64(z[pick]), W.as_f64(u_t), W.as_f64(v_t))
     got = np64(L)[pick]
     assert (np.abs(got - ref) / ref).max() < 2e-5
