@@ -364,15 +364,19 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 // =============================================================== PAP probe
 // Pass 1: per key chunk, per head, partial (max, sum) of the probe softmax
 // in log2 units.  grid (ceil(n/chunk), Hq/4), 4 waves = 4 heads.  A chunk is
-// 256, 512 or 1024 keys (a multiple of the 64-key tile): every workgroup
-// also loads all P probe queries of its 4 heads, so longer chunks cut that
-// traffic once the grid still has about two workgroups per compute unit.
-constexpr int MIN_CHUNK = 256;
+// a multiple of the 64-key tile between 128 and 1024 keys: the shortest whose
+// grid still fits in one round of resident workgroups (two per compute unit
+// for P <= 64, one for P = 128, as the kernels' registers allow).  A partly
+// filled second round costs a whole chunk's time, while every workgroup also
+// loads all P probe queries of its 4 heads, so chunks stay as long as that
+// round allows; past 1024 keys the grid runs in several rounds.
+constexpr int MIN_CHUNK = 128;
 
-int probe_chunk(int n, int Hq) {
-  int c = MIN_CHUNK;
-  while (c < 1024 && (long)((n + 2 * c - 1) / (2 * c)) * (Hq / 4) >= 512) c *= 2;
-  return c;
+int probe_chunk(int n, int Hq, int P) {
+  const long slots = 256L * (P <= 64 ? 2 : 1);
+  const long need = ((long)n * (Hq / 4) + slots - 1) / slots;      // keys per chunk for one round
+  const int c = (int)(((need + KT - 1) / KT) * KT);
+  return c < MIN_CHUNK ? MIN_CHUNK : (c > 1024 ? 1024 : c);
 }
 
 template <int PT>   // probe column tiles of 32 (P = 32*PT)
@@ -664,7 +668,7 @@ size_t probe_workspace(int n, int P, int Hq) {
 
 hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P, int Hq, int Hkv,
                              float scale, float* scores, void* ws, hipStream_t s) {
-  const int ck = probe_chunk(n, Hq);
+  const int ck = probe_chunk(n, Hq, P);
   const int nchunks = (n + ck - 1) / ck;
   const long HP = (long)Hq * P;
   float* part_m = reinterpret_cast<float*>(ws);

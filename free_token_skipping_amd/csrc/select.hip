@@ -361,7 +361,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 #pragma unroll UNROLL_J
       for (int j = 0; j < J; ++j) {
         const uint32_t key = key_at(j);
-        atomicAdd(&hist[w][(j < jf) & ((key & mask) == prefix) ? (int)((key >> shift) & dmask) : 256 + lane], 1);
+        atomicAdd(&hist[w][((j < jf) & ((key & mask) == prefix)) ? (int)((key >> shift) & dmask) : 256 + lane], 1);
       }
       __syncthreads();
       if (tid < 256) {
