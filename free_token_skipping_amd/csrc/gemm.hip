@@ -218,6 +218,7 @@ void gemm_tn_kernel(GemmArgs g) {
     logical = g.tail_full + tt;
   }
 
+  // one job = one tile over k-steps [k0, k1); only ends workgroups run more than one
   for (;;) {
     int tile_m, tile_n;
     tile_of(logical, tiles_m, tiles_n, tile_m, tile_n);
