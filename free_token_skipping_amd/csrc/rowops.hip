@@ -75,26 +75,44 @@ __global__ void scatter_add_kernel(const T* __restrict__ src, const int32_t* __r
   }
 }
 
-// One workgroup per row; fp32 sum of squares, unit gain, bf16 output.
+// One workgroup per row; fp32 sum of squares, unit gain, bf16 output.  The
+// first 8192 columns of the row stay in registers between the two passes
+// (all their loads issued before the first is used); wider rows re-read the
+// rest.  Thread t sums its 8-column groups t, t + 256, ... in that order.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int d, float eps,
                                                       uint16_t* __restrict__ out) {
+  constexpr int R = 4;                       // 16-byte groups per thread held in registers
   __shared__ float red[4];
   const long row = blockIdx.x;
   const uint16_t* xr = x + row * d;
+  u32x4 v[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int c = (threadIdx.x + i * 256) * 8;
+    if (c < d) v[i] = ld16(xr + c);
+  }
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) ss = sumsq8(ld16(xr + c), ss);
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if ((threadIdx.x + i * 256) * 8 < d) ss = sumsq8(v[i], ss);
+  for (int c = (threadIdx.x + R * 256) * 8; c < d; c += 256 * 8) ss = sumsq8(ld16(xr + c), ss);
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float r = rms_inv(red, d, eps);
   uint16_t* orow = out + row * d;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    const u32x4 v = ld16(xr + c);
+  auto scale = [&](const u32x4& u, int c) {
     u32x4 o;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) o[w] = pack2bf(lo_bf(v[w]) * r, hi_bf(v[w]) * r);
+    for (int w = 0; w < 4; ++w) o[w] = pack2bf(lo_bf(u[w]) * r, hi_bf(u[w]) * r);
     st16(orow + c, o);
+  };
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int c = (threadIdx.x + i * 256) * 8;
+    if (c < d) scale(v[i], c);
   }
+  for (int c = (threadIdx.x + R * 256) * 8; c < d; c += 256 * 8) scale(ld16(xr + c), c);
 }
 
 // table[p, c] = (cos, sin)(p * theta^(-2c/dh)), angle in fp64.

@@ -305,8 +305,9 @@ def test_linear_full_size_sampled():
     assert_close(np64(out)[pick], ref, BF16_REL, "linear 32K sampled")
 
 
-def test_rmsnorm():
-    x = W.randn((333, 4096), seed=35, std=2.0)
+@pytest.mark.parametrize("d", [4096, 520, 12296])      # in registers, a partly filled group, past 8192 columns
+def test_rmsnorm(d):
+    x = W.randn((333, d), seed=35, std=2.0)
     out = capi.spts_rmsnorm(_cuda(x), 1e-5)
     ref = numerics.bf16(normrope.rmsnorm(W.as_f64(x), 1e-5))
     assert_close(np64(out), ref, BF16_REL, "rmsnorm")
