@@ -140,3 +140,32 @@ def test_tail_kv_rope(m, kd, plan):
     kref = numerics.bf16(normrope.rope(kacc, pos.numpy()[r], THETA)).reshape(len(pick), nk)
     _check_rows(np64(k_out)[pick], kref, "tail kv: K")
     _check_rows(np64(v_out)[pick], numerics.bf16(z @ W.as_f64(wv).T), "tail kv: V")
+
+
+def test_tail_shape_without_workspace_runs_unsplit():
+    """A caller that gives less workspace than the tail split needs gets the
+    unsplit launch: same oracle bar, and the documented status."""
+    import ctypes
+    m, kd, n = 5161, 4096, 4096                       # 80 tail tiles in 3 pieces with room
+    _log("tail shape, 1 MiB workspace")
+    L = capi.lib()
+    assert L.spts_linear_workspace(m, kd, n) > (1 << 20)
+    a = _cuda(_a(kd)[:m])
+    w = _cuda(_mat(n, kd, 91, 0.02))
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    h = ctypes.c_void_p()
+    assert L.spts_create(ctypes.byref(h), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    try:
+        assert L.spts_set_workspace(h, ctypes.c_void_p(ws.data_ptr()), ws.numel()) == 0
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        assert L.spts_linear(h, P(a), None, m, kd, P(w), n, P(out), None, 0) == 0
+        assert L.spts_check(h) == 0
+    finally:
+        L.spts_destroy(h)
+    pick = _pick(m, 6)
+    ref = numerics.bf16(W.as_f64(_a(kd)[:m][pick]) @ W.as_f64(_mat(n, kd, 91, 0.02)).T)
+    _check_rows(np64(out)[pick], ref, "unsplit fallback")
+    split = capi.spts_linear(a, w)                     # with room: the tail split
+    diff = (split.float() - out.float()).abs()
+    assert diff.max().item() <= 2 ** -6 * out.float().abs().max().item()   # one bf16 rounding apart at most
