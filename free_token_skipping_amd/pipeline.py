@@ -146,11 +146,20 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
     if trace is not None:
         trace.update(S_pre=S, K_pre=K, V_pre=V)
     # a14: MSDP boundary -- prune, then compact every per-candidate tensor
+    xt_rows, xt_pos = None, pos             # rows of xt (and their positions) behind candidate i
     if prune_to is not None and prune_to < n:
         with tm("msdp_stage", 4.0 * n + 4.0 * prune_to + 2.0 * prune_to * (4 + 2 * d)):
             keep, pos, x = capi.spts_msdp_stage(S, prune_to, P, pos, x)
-        with tm("msdp_compact", 2.0 * prune_to * (2 * Hkv * dh * 2 + 4 + (2 * d if cfg.prenorm else 0))):
-            xt = capi.spts_gather(xt, keep) if cfg.prenorm else x
+        # fused: the normalised rows stay where they are; the Q projection
+        # gathers them through keep
+        copy_xt = cfg.prenorm and not fused
+        with tm("msdp_compact", 2.0 * prune_to * (2 * Hkv * dh * 2 + 4 + (2 * d if copy_xt else 0))):
+            if not cfg.prenorm:
+                xt, xt_pos = x, pos
+            elif copy_xt:
+                xt, xt_pos = capi.spts_gather(xt, keep), pos
+            else:
+                xt_rows = keep
             K = capi.spts_gather(K, keep)
             V = capi.spts_gather(V, keep)
             S = capi.spts_gather(S, keep)
@@ -166,8 +175,9 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
     # a5 + a6: gather selected rows, Q projection
     if fused:
         with tm("q_proj", 2.0 * k_a * d * Hq * dh):
-            Qs = (capi.spts_linear_rope(xt, w["wq"], pos, rope_table, a_rows=idx) if rope
-                  else capi.spts_linear(xt, w["wq"], a_rows=idx))
+            rows = idx if xt_rows is None else capi.spts_gather(xt_rows, idx)
+            Qs = (capi.spts_linear_rope(xt, w["wq"], xt_pos, rope_table, a_rows=rows) if rope
+                  else capi.spts_linear(xt, w["wq"], a_rows=rows))
     else:
         with tm("gather_x", 4.0 * k_a * d):
             xs = capi.spts_gather(xt, idx)
