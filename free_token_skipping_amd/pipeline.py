@@ -45,23 +45,29 @@ NO_TIMER = _NoTimer()
 class CallTimer:
     """Records a start/end HIP event pair on the current stream around each
     named library call (the stream the call's kernels run on), with an
-    optional algorithmic work figure for the call."""
+    optional algorithmic work figure for the call.  only: if given, the set of
+    call names that get events; other calls run unbracketed."""
 
-    def __init__(self):
+    def __init__(self, only=None):
         self.records = []
         self._cur = None
+        self._only = only
 
     def __call__(self, name, work=None):
         self._cur = (name, work)
         return self
 
     def __enter__(self):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        self._start = e0
+        self._start = None
+        if self._only is None or self._cur[0] in self._only:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            self._start = e0
         return self
 
     def __exit__(self, *exc):
+        if self._start is None:
+            return False
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record()
         name, work = self._cur
