@@ -413,8 +413,13 @@ def msdp_stack(x0, layers, cfg: LayerConfig, points, fused=True, traces=None, tm
     """Run the stack on embeddings x0 [N, d] (not modified).  Returns the
     residual over the final candidates and their original positions."""
     N = x0.shape[0]
-    with tm("stack_setup", 4.0 * x0.numel()):
-        x = x0.clone()
+    # Layer 0 only reads the residual until its MSDP boundary, and the
+    # boundary gathers the kept rows into a new tensor; so when layer 0 prunes,
+    # x0 itself can be its input.  Otherwise the stack writes into a copy.
+    first = points.get(0)
+    copy_x0 = first is None or first >= N
+    with tm("stack_setup", 4.0 * x0.numel() if copy_x0 else 4.0 * N):
+        x = x0.clone() if copy_x0 else x0
         pos = torch.arange(N, dtype=torch.int32, device=x0.device)
         table = capi.spts_rope_table(N, cfg.dh, cfg.theta, x0.device) if cfg.theta is not None else None
     for li, w in enumerate(layers):

@@ -231,7 +231,9 @@ def test_msdp_stack_small():
     cfg = pipeline.LayerConfig(Hq=8, Hkv=2, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35, prenorm=True,
                                eps=1e-5, theta=500000.0)
     traces = []
-    x, pos = pipeline.msdp_stack(st["x"].to(DEV), [_gpu_w(w) for w in st["layers"]], cfg, pts, traces=traces)
+    x0 = st["x"].to(DEV)
+    x, pos = pipeline.msdp_stack(x0, [_gpu_w(w) for w in st["layers"]], cfg, pts, traces=traces)
+    assert torch.equal(x0.cpu(), st["x"])                 # the stack never writes its input
     torch.cuda.synchronize()
     ocfg = dict(Hq=8, Hkv=2, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35, prenorm=True, eps=1e-5,
                 theta=500000.0)
@@ -321,6 +323,7 @@ def test_msdp_stack_32k_full_size():
     _log("gpu 32K stack")
     x, pos = pipeline.msdp_stack(x0, [_gpu_w(w) for w in st["layers"]], cfg, pts, traces=traces)
     torch.cuda.synchronize()
+    assert torch.equal(x0.cpu(), st["x"])                 # the stack never writes its input
 
     # ---- structure of every layer
     counts = olayer.candidate_counts(N, cfgd["layers"], pts)
