@@ -15,9 +15,10 @@ A step is one pass of the whole hot path over one batch of synthetic input
 
 The metric is prefill tokens/s per layer: layers * N / seconds per step.
 One JSON line is printed.  It also carries the roofline of the dominant
-kernel (timed with HIP events on its own stream inside the timed region),
-a per-call breakdown, the single-layer figure and the CPU oracle's rate on a
-bounded row sample of the same workload.
+kernel (timed with HIP events on its own stream inside the timed region,
+where no other call carries events), a per-call breakdown (from K steps with
+every call bracketed, run before the timed ones), the single-layer figure and
+the CPU oracle's rate on a bounded row sample of the same workload.
 """
 
 import argparse
