@@ -47,7 +47,7 @@ _SIGS = {
     "spts_probe_attention_workspace": (_SZ, [_I, _I, _I]),
     "spts_score_topk_workspace": (_SZ, [_I]),
     "spts_ltp_probe_workspace": (_SZ, [_I, _I, _I]),
-    "spts_reduced_ffn_workspace": (_SZ, [_I, _I]),
+    "spts_reduced_ffn_workspace": (_SZ, [_I, _I, _I]),
     "spts_msdp_stage_workspace": (_SZ, [_I]),
     "spts_linear_workspace": (_SZ, [_I, _I, _I]),
     "spts_linear_kv_workspace": (_SZ, [_I, _I, _I, _I]),
@@ -428,7 +428,7 @@ def spts_reduced_ffn(z, w_gate, w_up, w_down, rows=None, y=None, y_rows=None, ac
     if y is None:
         y = torch.empty((k, d), dtype=torch.bfloat16, device=z.device)
     ctx = context()
-    h = ctx.bind(lib().spts_reduced_ffn_workspace(k, f), z.device)
+    h = ctx.bind(lib().spts_reduced_ffn_workspace(k, d, f), z.device)
     bf = torch.bfloat16
     _check(ctx, lib().spts_reduced_ffn(h, _ptr(z, bf, "z"), _ptr(rows, torch.int32, "rows"), _ptr(w_gate, bf, "w_gate"),
                                        _ptr(w_up, bf, "w_up"), _ptr(w_down, bf, "w_down"), k, d, f,

@@ -53,9 +53,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 #define REQUIRE_PTR(p) REQUIRE((p) != nullptr, SPTS_ERR_INVALID, "%s is NULL", #p)
 #define REQUIRE_ALIGN(p) REQUIRE(aligned16(p), SPTS_ERR_ALIGN, "%s is not 16-byte aligned", #p)
 
-// element offsets inside kernels are computed in 64-bit, but row counts and
-// per-row strides are int: keep every extent below 2^31 elements per row.
+// Upper bound on the elements of one K or V operand of the PAP probe (its
+// kernels form element offsets in 64 bits; row counts and strides are int).
 constexpr long kMaxElems = 1L << 40;
+// The GEMM forms the byte offset of a weight (B operand) row in 32 bits, so
+// every weight must stay below 4 GiB; activation (A) rows use 64-bit offsets.
+constexpr long kMaxWeightBytes = 1L << 32;
 
 }  // namespace
 
@@ -160,9 +163,12 @@ size_t spts_linear_swiglu_workspace(int m, int kdim, int f) {
   if (m <= 0 || kdim <= 0 || f <= 0) return 0;
   return gemm_split_workspace(m, kdim, 2 * f, EPI_SWIGLU);
 }
-size_t spts_reduced_ffn_workspace(int k, int f) {
-  if (k <= 0 || f <= 0) return 0;
-  return ((size_t)k * f * 2 + 255) & ~(size_t)255;
+// H [k, f] bf16, then the split workspace of whichever of the two GEMMs needs more
+size_t spts_reduced_ffn_workspace(int k, int d, int f) {
+  if (k <= 0 || d <= 0 || f <= 0) return 0;
+  const size_t s1 = gemm_split_workspace(k, d, 2 * f, EPI_SWIGLU);
+  const size_t s2 = gemm_split_workspace(k, f, d, EPI_STORE);
+  return round256((size_t)k * f * 2) + (s1 > s2 ? s1 : s2);
 }
 size_t spts_msdp_stage_workspace(int n_prev) { return n_prev > 0 ? topk_workspace(n_prev) : 0; }
 
@@ -328,11 +334,17 @@ spts_status spts_reduced_attention(spts_ctx* ctx, spts_dtype dtype, const void* 
 
 // ------------------------------------------------------------------------ GEMM
 
+static spts_status weight_size_ok(spts_ctx* ctx, long rows, long cols) {
+  REQUIRE(rows * cols * 2 < kMaxWeightBytes, SPTS_ERR_UNSUPPORTED,
+          "weight of %ld x %ld bf16 elements is 4 GiB or more", rows, cols);
+  return SPTS_OK;
+}
+
 static spts_status gemm_shape_ok(spts_ctx* ctx, int m, int kdim, int n) {
   REQUIRE(m >= 0 && kdim > 0 && n > 0, SPTS_ERR_SHAPE, "bad GEMM sizes m=%d k=%d n=%d", m, kdim, n);
   REQUIRE(kdim % 64 == 0, SPTS_ERR_UNSUPPORTED, "inner dimension %d is not a multiple of 64", kdim);
   REQUIRE(n % 256 == 0, SPTS_ERR_UNSUPPORTED, "output width %d is not a multiple of 256", n);
-  return SPTS_OK;
+  return weight_size_ok(ctx, n, kdim);
 }
 
 spts_status spts_linear(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim, const void* w,
@@ -400,6 +412,10 @@ spts_status spts_linear_swiglu(spts_ctx* ctx, const void* a, const int32_t* a_ro
   CHECK_CTX();
   REQUIRE(m >= 0 && kdim > 0 && f > 0, SPTS_ERR_SHAPE, "bad SwiGLU GEMM sizes");
   REQUIRE(kdim % 64 == 0 && f % 128 == 0, SPTS_ERR_UNSUPPORTED, "SwiGLU GEMM needs kdim %% 64 == 0, f %% 128 == 0");
+  {
+    const spts_status st = weight_size_ok(ctx, f, kdim);
+    if (st != SPTS_OK) return st;
+  }
   if (m == 0) return SPTS_OK;
   REQUIRE_PTR(a); REQUIRE_PTR(w_gate); REQUIRE_PTR(w_up); REQUIRE_PTR(h_out);
   REQUIRE_ALIGN(a); REQUIRE_ALIGN(w_gate); REQUIRE_ALIGN(w_up); REQUIRE_ALIGN(h_out);
@@ -436,6 +452,10 @@ spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const 
   CHECK_CTX();
   REQUIRE(n >= 0 && d > 0 && r > 0, SPTS_ERR_SHAPE, "bad LTP sizes");
   REQUIRE(d % 256 == 0 && r % 256 == 0, SPTS_ERR_UNSUPPORTED, "LTP needs d %% 256 == 0 and r %% 256 == 0");
+  {
+    const spts_status st = weight_size_ok(ctx, d, r);
+    if (st != SPTS_OK) return st;
+  }
   if (n == 0) return SPTS_OK;
   REQUIRE_PTR(z); REQUIRE_PTR(u_t); REQUIRE_PTR(v_t); REQUIRE_PTR(score);
   REQUIRE_ALIGN(z); REQUIRE_ALIGN(u_t); REQUIRE_ALIGN(v_t); REQUIRE_ALIGN(score);
@@ -471,6 +491,13 @@ spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* 
   REQUIRE(n >= 0 && d > 0 && r > 0 && d_low > 0, SPTS_ERR_SHAPE, "bad structured LTP sizes");
   REQUIRE(d % 256 == 0 && r % 256 == 0 && d_low % 256 == 0, SPTS_ERR_UNSUPPORTED,
           "structured LTP needs d, r and d_low multiples of 256 (d=%d r=%d d_low=%d)", d, r, d_low);
+  {
+    spts_status st = weight_size_ok(ctx, 2L * r, d);
+    if (st == SPTS_OK) st = weight_size_ok(ctx, d_low, 4L * r);
+    if (st == SPTS_OK) st = weight_size_ok(ctx, d, r);
+    if (st == SPTS_OK) st = weight_size_ok(ctx, r, d_low);
+    if (st != SPTS_OK) return st;
+  }
   if (n == 0) return SPTS_OK;
   REQUIRE_PTR(z); REQUIRE_PTR(a_gu_t); REQUIRE_PTR(b_gate); REQUIRE_PTR(b_up); REQUIRE_PTR(c_t);
   REQUIRE_PTR(d_t); REQUIRE_PTR(score);
@@ -655,24 +682,34 @@ spts_status spts_reduced_ffn(spts_ctx* ctx, const void* z, const int32_t* rows, 
   REQUIRE(k >= 0 && d > 0 && f > 0, SPTS_ERR_SHAPE, "bad FFN sizes");
   REQUIRE(d % 256 == 0 && f % 128 == 0, SPTS_ERR_UNSUPPORTED, "FFN needs d %% 256 == 0 and f %% 128 == 0");
   REQUIRE(accumulate == 0 || accumulate == 1, SPTS_ERR_INVALID, "accumulate must be 0 or 1");
+  {
+    const spts_status st = weight_size_ok(ctx, f, d);
+    if (st != SPTS_OK) return st;
+  }
   if (k == 0) return SPTS_OK;
   REQUIRE_PTR(z); REQUIRE_PTR(w_gate); REQUIRE_PTR(w_up); REQUIRE_PTR(w_down); REQUIRE_PTR(y_sel);
   REQUIRE_ALIGN(z); REQUIRE_ALIGN(w_gate); REQUIRE_ALIGN(w_up); REQUIRE_ALIGN(w_down); REQUIRE_ALIGN(y_sel);
   if (rows) REQUIRE_ALIGN(rows);
   if (y_rows) REQUIRE_ALIGN(y_rows);
-  const size_t need = spts_reduced_ffn_workspace(k, f);
-  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  // H must fit; the split part of the workspace is optional (a GEMM whose
+  // plan needs more than what is left runs unsplit)
+  const size_t h_bytes = round256((size_t)k * f * 2);
+  REQUIRE(ctx->ws_bytes >= h_bytes, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, h_bytes);
   uint16_t* H = reinterpret_cast<uint16_t*>(ctx->ws);
+  float* split_ws = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + h_bytes);
+  const size_t split_bytes = ctx->ws_bytes - h_bytes;
   GemmArgs g1{};
   g1.a = reinterpret_cast<const uint16_t*>(z); g1.a_rows = rows; g1.m = k; g1.k = d; g1.lda = d;
   g1.b0 = reinterpret_cast<const uint16_t*>(w_gate); g1.b1 = reinterpret_cast<const uint16_t*>(w_up);
   g1.ldb = d; g1.n = 2 * f; g1.out = H; g1.ldc = f;
+  g1.partial = split_bytes ? split_ws : nullptr; g1.partial_bytes = split_bytes;
   hipError_t e = launch_gemm(g1, EPI_SWIGLU, ctx->stream);
   if (e != hipSuccess) return hip_status(ctx, e, "reduced_ffn (gate/up)");
   GemmArgs g2{};
   g2.a = H; g2.m = k; g2.k = f; g2.lda = f;
   g2.b0 = reinterpret_cast<const uint16_t*>(w_down); g2.ldb = f; g2.n = d;
   g2.out = y_sel; g2.ldc = d; g2.out_rows = y_rows; g2.accumulate = accumulate;
+  g2.partial = split_bytes ? split_ws : nullptr; g2.partial_bytes = split_bytes;
   return hip_status(ctx, launch_gemm(g2, EPI_STORE, ctx->stream), "reduced_ffn (down)");
 }
 

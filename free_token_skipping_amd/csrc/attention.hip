@@ -14,8 +14,6 @@
 // V tile.
 #include <type_traits>
 
-#include <type_traits>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -134,9 +132,22 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   const int qi_raw = qw + l32;
   const int qi = qi_raw < kq ? qi_raw : kq - 1;
   const int qpos = idx[qi];
-  const int kmax = idx[min(q0 + 63, kq - 1)];
+  // The block's key range comes from the smallest and largest row among its
+  // 64 queries (idx need not be sorted): each lane reads two of them and the
+  // wave reduces.  Rows past kq repeat the last query's row.
+  int kmin, kmax;
+  {
+    const int ra = idx[min(q0 + l32, kq - 1)], rb = idx[min(q0 + 32 + l32, kq - 1)];
+    kmin = min(ra, rb);
+    kmax = max(ra, rb);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      kmin = min(kmin, __shfl_xor(kmin, o));
+      kmax = max(kmax, __shfl_xor(kmax, o));
+    }
+  }
   const int ntiles = kmax / KT + 1;
-  const int nfull = (idx[q0] + 1) / KT;             // tiles entirely below every query of the block
+  const int nfull = (kmin + 1) / KT;                // tiles entirely below every query of the block
 
   bf16x8 qf[8];
 #pragma unroll
@@ -334,6 +345,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   }
   logits(0, sa);
   prepare(0, sa, pb);                     // nothing pending yet (pb is zero)
+  // step 0 stages K_2 into Ks[0]: every wave must have read K_0 from it first
+  __syncthreads();
   step(std::false_type{}, 0, sa, sb, pb, pa);
   int t = 1;
   for (; t + 1 < ntiles; t += 2) {

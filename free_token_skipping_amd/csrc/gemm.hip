@@ -234,7 +234,11 @@ void gemm_tn_kernel(GemmArgs g) {
     const bool loader = wave < 4;
     const int lw = wave & 3;
     const int ld_sub = lane >> 3;                       // row within the 8-row block
-    uint32_t a_off[8], b_off[8];                        // byte offsets of the staged rows
+    // byte offsets of the staged rows: A rows in 64 bits (a gathered source
+    // can span more than 4 GiB), B rows in 32 bits (the host rejects weights
+    // of 4 GiB or more)
+    uint64_t a_off[8];
+    uint32_t b_off[8];
     unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -244,7 +248,7 @@ void gemm_tn_kernel(GemmArgs g) {
       int ar = tile_m * BM + r;
       if (ar >= g.m) ar = g.m - 1;
       if (GATHER) ar = g.a_rows[ar];
-      a_off[i] = ((uint32_t)ar * (uint32_t)g.lda + ld_ch * 8) * 2u;
+      a_off[i] = ((uint64_t)(uint32_t)ar * (uint32_t)g.lda + ld_ch * 8) * 2u;
       if (kSwiglu) {
         // wave column block r / 128: rows 0..63 gate, 64..127 up, same 64 outputs
         const int within = r & 127;

@@ -15,7 +15,8 @@
  *   - Layouts are row-major and token-major.  Weights use the nn.Linear
  *     layout [out_features, in_features].  "bf16" is IEEE bfloat16 stored in
  *     16 bits; accumulation is fp32.
- *   - Index arrays are int32, strictly ascending, in [0, n).
+ *   - Index arrays are int32, strictly ascending, in [0, n), except where a
+ *     call says otherwise.
  *   - Every compute call is asynchronous on the context's stream (a HIP
  *     stream borrowed from the caller, never destroyed here) and returns a
  *     status.  Arguments are validated on the host before anything is
@@ -81,7 +82,7 @@ size_t spts_ltp_probe_workspace(int n, int d, int r);
 size_t spts_ltp_structured_workspace(int n, int d, int r, int d_low);
 size_t spts_decode_attention_workspace(int L, int Hq);
 size_t spts_decode_step_workspace(int max_len, int Hq, int f);
-size_t spts_reduced_ffn_workspace(int k, int f);
+size_t spts_reduced_ffn_workspace(int k, int d, int f);
 size_t spts_msdp_stage_workspace(int n_prev);
 /* Workspace with which spts_linear / spts_linear_rope, spts_linear_kv and
  * spts_linear_swiglu split the inner dimension across workgroups; 0 when the
@@ -117,7 +118,8 @@ spts_status spts_probe_attention(spts_ctx* ctx, spts_dtype dtype, const void* q_
 /* Top-k token selection ([SPTS] Fig. 2(a)(b); fusion: Table D "MaxNorm-Add").
  * Ranking score: s_a if s_b == NULL, else the float32 value
  *     c = fl(fl(w_a*fl(s_a/max s_a)) + fl(w_b*fl(s_b/max s_b)))
- * (a term is 0 when its max is not positive).  The last n_forced rows are
+ * (the maxima are taken over all n rows and ignore NaN; a term is 0 when
+ * its max is not positive).  The last n_forced rows are
  * always kept and count toward k; the other k-n_forced rows are the largest
  * ranking scores among rows 0..n-n_forced-1, ties to the lower index; NaN
  * ranks lowest and -0 equals +0.  idx[0..min(k,n)-1] receives the kept rows
@@ -169,7 +171,10 @@ spts_status spts_scatter(spts_ctx* ctx, spts_dtype dtype, const void* src, const
  *     o_sel[i,h] = sum_{j<=idx[i]} softmax_j(scale*q_sel[i,h].k[j,g]) v[j,g],
  *     g = h / (Hq/Hkv).
  *   q_sel [kq, Hq, dh], k and v [n, Hkv, dh], o_sel [kq, Hq, dh]; all dtype.
- * dtype SPTS_BF16: dh == 128, (Hq/Hkv) % 4 == 0.  SPTS_F32: dh <= 128. */
+ * idx may be in any order and may repeat rows: each query's causal range
+ * comes from its own row (ascending idx, as selections produce, is fastest).
+ * dtype SPTS_BF16: dh == 128, (Hq/Hkv) % 4 == 0, n*Hkv*dh < 2^31.
+ * SPTS_F32: dh <= 128. */
 spts_status spts_reduced_attention(spts_ctx* ctx, spts_dtype dtype, const void* q_sel,
                                    const int32_t* idx, const void* k, const void* v, int kq,
                                    int n, int Hq, int Hkv, int dh, float scale, void* o_sel);
@@ -214,7 +219,14 @@ spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* 
  * residual add of the selected tokens), accumulate == 0 stores Y[i].
  *   z [*, d] bf16, w_gate, w_up [f, d], w_down [d, f], y [*, d] bf16.
  * y must not alias the rows of z being read when y_rows == NULL.
- * Requires d % 256 == 0, f % 128 == 0.  Workspace (H): spts_reduced_ffn_workspace. */
+ * Requires d % 256 == 0, f % 128 == 0, and each weight below 4 GiB.
+ * Workspace: spts_reduced_ffn_workspace(k, d, f) bytes = H [k, f] bf16 plus
+ * the fp32 pieces with which the two GEMMs split their last, partly filled
+ * round of tiles along the inner dimension (as spts_linear_swiglu and
+ * spts_linear do).  At least the H part (k*f*2 bytes rounded up to 256) is
+ * required (SPTS_ERR_NOMEM otherwise); with less than the full size a GEMM
+ * whose split does not fit runs unsplit (same result up to the order of
+ * the fp32 additions). */
 spts_status spts_reduced_ffn(spts_ctx* ctx, const void* z, const int32_t* rows, const void* w_gate,
                              const void* w_up, const void* w_down, int k, int d, int f, void* y,
                              const int32_t* y_rows, int accumulate);
@@ -240,8 +252,10 @@ spts_status spts_msdp_stage(spts_ctx* ctx, const float* scores, int n_prev, int 
  *   accumulate == 0: out[o(i), :] = bf16(A W^T)[i]
  *   accumulate == 1: out[o(i), :] = bf16(out[o(i), :] + bf16(A W^T)[i])
  *   with o(i) = out_rows[i] if out_rows != NULL (scatter on store), else i.
- * Requires kdim % 64 == 0, n % 256 == 0.  These projections are needed because
- * every step of the path runs in this library.
+ * Requires kdim % 64 == 0, n % 256 == 0, and W below 4 GiB (n*kdim*2 < 2^32;
+ * the same bound holds for every weight of the calls below, else
+ * SPTS_ERR_UNSUPPORTED).  A (gathered or not) may span any size.  These
+ * projections are needed because every step of the path runs in this library.
  * Workspace (optional): spts_linear_workspace (spts_linear_rope too). */
 spts_status spts_linear(spts_ctx* ctx, const void* a, const int32_t* a_rows, int m, int kdim,
                         const void* w, int n, void* out, const int32_t* out_rows, int accumulate);

@@ -20,7 +20,10 @@ the current candidates, then a weighted sum.  Because a fused score decides
 an integer (which rows are kept), it is evaluated in float32 with a fixed
 operation order, exactly as the kernel evaluates it:
     c = fl(fl(w_a * fl(s_a / max s_a)) + fl(w_b * fl(s_b / max s_b))),
-with a term taken as 0 when its maximum is not positive.
+with a term taken as 0 when its maximum is not positive.  The maxima run
+over every row and skip NaN (a NaN score leaves the other rows' normalised
+values as they are; its own fused value is NaN and ranks lowest); a score
+with no number at all has no positive maximum, so its term is 0.
 
 Table D's "Multiply" (the pages' default fusion, as C^FFN * S^MHA in Table 6)
 is `fuse_multiply`: the product of the two scores, one float32 rounding.  A
@@ -62,7 +65,8 @@ def fuse_maxnorm(s_a, s_b, w_a=0.5, w_b=0.5):
     wb = np.float32(w_b)
 
     def term(w, x):
-        mx = np.float32(x.max()) if x.size else np.float32(0)
+        finite = x[~np.isnan(x)]
+        mx = np.float32(finite.max()) if finite.size else np.float32(0)
         if not (mx > 0):
             return np.zeros_like(x)
         q = (x / mx).astype(np.float32)

@@ -55,7 +55,7 @@ def test_status_names(L):
 
 def test_workspace_queries(L):
     assert L.spts_score_topk_workspace(32768) >= 32768 * 4
-    assert L.spts_reduced_ffn_workspace(11469, 14336) >= 11469 * 14336 * 2
+    assert L.spts_reduced_ffn_workspace(11469, 4096, 14336) >= 11469 * 14336 * 2
     assert L.spts_ltp_probe_workspace(100, 4096, 256) >= 100 * 512 * 2
     assert L.spts_probe_attention_workspace(0, 64, 32) == 0
 
@@ -125,6 +125,13 @@ def test_gemm_family_validation(L, ctx):
     assert L.spts_linear(ctx, FAKE, None, 100, 128, FAKE, 256, FAKE, None, 2) == INVALID
     assert L.spts_linear(ctx, None, None, 100, 128, FAKE, 256, FAKE, None, 0) == INVALID
     assert L.spts_linear(ctx, FAKE, None, 0, 128, FAKE, 256, FAKE, None, 0) == OK             # empty: no-op
+    # a weight of 4 GiB or more is refused (the GEMM forms weight-row offsets in 32 bits)
+    assert L.spts_linear(ctx, FAKE, None, 10, 4096, FAKE, 524288, FAKE, None, 0) == UNSUPPORTED
+    assert L.spts_linear_swiglu(ctx, FAKE, None, 10, 8192, FAKE, FAKE, 262144, FAKE) == UNSUPPORTED
+    assert L.spts_linear_kv(ctx, FAKE, None, 10, 8192, FAKE, 262144, FAKE, 256, FAKE, FAKE, None, None) == UNSUPPORTED
+    assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 10, 8192, 262144, FAKE, None, 0) == UNSUPPORTED
+    assert L.spts_ltp_probe(ctx, FAKE, FAKE, FAKE, 10, 8388608, 256, FAKE) == UNSUPPORTED
+    assert b"4 GiB" in L.spts_last_error(ctx)
     assert L.spts_ltp_probe(ctx, FAKE, FAKE, FAKE, 10, 4096, 100, FAKE) == UNSUPPORTED
     assert L.spts_ltp_probe(ctx, FAKE, FAKE, FAKE, 10, 4096, 256, FAKE) == NOMEM
     assert L.spts_reduced_ffn(ctx, FAKE, None, FAKE, FAKE, FAKE, 10, 4096, 100, FAKE, None, 0) == UNSUPPORTED

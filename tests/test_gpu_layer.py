@@ -256,7 +256,7 @@ def test_msdp_stack_small():
     assert agree > 0.95
     common, ig, io = np.intersect1d(final, pos_ref, return_indices=True)
     err = np.abs(np64(x)[ig] - ref[io]) / np.abs(ref[io]).max(axis=1, keepdims=True)
-    assert np.median(err.max(axis=1)) <= BF16_REL
+    assert err.max() <= BF16_REL, err.max()
 
 
 
@@ -293,7 +293,7 @@ def test_dense_layers_and_schedule_small():
 
 def test_msdp_stack_32k_full_size():
     """The timed workload itself: the 8-layer pre-norm RoPE stack at 32768
-    tokens with the [SPTS] Sec. 3.3 stage schedule, in the configuration the
+    tokens with stages of the kind [SPTS] Table B schedules, in the configuration the
     benchmark runs.  Checked at full size:
       * structure that holds at any size: candidate counts per layer, nested
         ascending candidate sets that keep the probe rows, selection sizes,

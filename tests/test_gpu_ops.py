@@ -118,16 +118,22 @@ def test_select_batched_bit_exact(n, k, nf, batch):
         assert np.array_equal(idx[b], select.select_topk(rows[b].numpy(), k, nf)), f"row {b}"
 
 
-@pytest.mark.parametrize("n,k,nf", [(1000, 350, 64), (32768, 11469, 64)])
-def test_select_fused_bit_exact(n, k, nf):
-    _log(f"fused select n={n}")
+@pytest.mark.parametrize("n,k,nf,nan", [(1000, 350, 64, False), (32768, 11469, 64, False),
+                                         (131072, 32768, 128, False), (1000, 350, 64, True),
+                                         (131072, 32768, 128, True)])
+def test_select_fused_bit_exact(n, k, nf, nan):
+    # n > 32768 keeps the keys in the workspace and takes the maxima in a loop of its own
+    _log(f"fused select n={n} nan={nan}")
     a = W.make_scores(n, seed=7)
     b = W.make_scores(n, seed=8) * 1e-3
     b[5] = b[9]                                            # a tie in the second score
+    if nan:                                                # NaN in each score: the maxima skip it
+        a[3] = float("nan")
+        b[n // 2] = float("nan")
     fused = torch.empty(n, dtype=torch.float32, device=DEV)
     idx = capi.spts_score_topk(_cuda(a), k, nf, s_b=_cuda(b), w_a=0.5, w_b=0.5, fused_out=fused)
     ref_c = select.fuse_maxnorm(a.numpy(), b.numpy(), 0.5, 0.5)
-    assert np.array_equal(fused.cpu().numpy(), ref_c)
+    assert np.array_equal(fused.cpu().numpy(), ref_c, equal_nan=True)
     assert np.array_equal(idx.cpu().numpy().astype(np.int64), select.select_topk(ref_c, k, nf))
 
 
@@ -189,6 +195,29 @@ def test_reduced_attention_bf16(n, kq, Hq, Hkv):
     # also per row: every query row within the bf16 bar of its own scale
     per_row = np.abs(np64(o) - ref).max(axis=(1, 2)) / np.abs(ref).max(axis=(1, 2))
     assert per_row.max() <= BF16_REL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reduced_attention_unsorted_idx(dtype):
+    """Query rows in shuffled order (and one row twice): each query's causal
+    range follows its own row, on both dtypes."""
+    n, kq, Hq, Hkv = 1500, 400, 8, 2
+    _log(f"reduced attention {dtype}, shuffled rows")
+    rows = W.sorted_rows(n, kq, 8, seed=80).numpy().copy()
+    np.random.default_rng(81).shuffle(rows)
+    rows[7] = rows[300]
+    idx = torch.from_numpy(rows.astype(np.int32))
+    bf = dtype == "bf16"
+    dh = 128 if bf else 64
+    q = W.randn((kq, Hq, dh), seed=82, std=1.3, bf16=bf)
+    k = W.randn((n, Hkv, dh), seed=83, std=1.3, bf16=bf)
+    v = W.randn((n, Hkv, dh), seed=84, bf16=bf)
+    o = capi.spts_reduced_attention(_cuda(q), _cuda(idx), _cuda(k), _cuda(v))
+    ref = attention.reduced_attention(W.as_f64(q), rows, W.as_f64(k), W.as_f64(v), dh ** -0.5)
+    got = np64(o)
+    tol = BF16_REL if bf else F32_REL
+    per_row = np.abs(got - ref).max(axis=(1, 2)) / np.abs(ref).max(axis=(1, 2))
+    assert per_row.max() <= tol, per_row.max()
 
 
 def test_reduced_attention_full_32k_sampled():

@@ -179,6 +179,21 @@ def test_fuse_maxnorm_pins():
     assert np.allclose(c, ref, rtol=3e-7, atol=0)
     # a zero maximum contributes nothing
     assert np.array_equal(select.fuse_maxnorm(a, np.zeros_like(a)), (np.float32(0.5) * (a / a.max())).astype(np.float32))
+    # a NaN score: the maxima skip it, so every other row keeps the value it
+    # has without the NaN (the float64 definition over the remaining rows),
+    # and the NaN row's own fused value is NaN, which ranks lowest
+    a3 = a.copy()
+    a3[17] = np.nan
+    c3 = select.fuse_maxnorm(a3, b)
+    rest = np.arange(1000) != 17
+    mx = np.max(a[rest].astype(np.float64))
+    ref3 = 0.5 * a[rest].astype(np.float64) / mx + 0.5 * b[rest].astype(np.float64) / b.max()
+    assert np.allclose(c3[rest], ref3, rtol=3e-7, atol=0) and np.isnan(c3[17])
+    assert 17 not in select.select_topk(c3, 999, 0).tolist()
+    # all-NaN score: no positive maximum, the term is 0
+    nan_all = np.full_like(a, np.nan)
+    assert np.array_equal(select.fuse_maxnorm(nan_all, b, 0.5, 0.5),
+                          (np.float32(0.5) * (b / b.max())).astype(np.float32))
 
 
 def test_fuse_multiply_pins():
