@@ -150,7 +150,7 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
     with tm("pap_probe", 2.0 * Hq * dh * P * n):
         S = capi.spts_probe_attention(Qp.view(P, Hq, dh), K)
     if trace is not None:
-        trace.update(S_pre=S, K_pre=K, V_pre=V)
+        trace.update(S_pre=S, K_pre=K, V_pre=V, xt=xt if cfg.prenorm else None)
     # a14: MSDP boundary -- prune, then compact every per-candidate tensor
     xt_rows, xt_pos = None, pos             # rows of xt (and their positions) behind candidate i
     if prune_to is not None and prune_to < n:
@@ -256,10 +256,18 @@ def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None, tm=NO_TIMER):
 
 def spts_layer(x, pos, w, cfg: LayerConfig, rope_table=None, k_given=None, prune_to=None, fused=True,
                trace=None, tm=NO_TIMER, kv_out=None):
-    """Attention block then (if cfg.keep_ffn is set) FFN block."""
+    """Attention block then (if cfg.keep_ffn is set) FFN block.  A trace
+    dict, if given, also receives copies of the layer's input (x_in, pos_in),
+    of the residual between the blocks (x_mid) and of its output (x_out)."""
+    if trace is not None:
+        trace.update(x_in=x.clone(), pos_in=pos.clone())
     x, pos, S = attention_block(x, pos, w, cfg, rope_table, k_given, prune_to, fused, trace, tm, kv_out)
     if cfg.keep_ffn is not None:
+        if trace is not None:
+            trace["x_mid"] = x.clone()
         x = ffn_block(x, S, w, cfg, fused, trace, tm)
+    if trace is not None:
+        trace["x_out"] = x.clone()
     return x, pos
 
 
@@ -272,7 +280,7 @@ def prune_points(first_skip_layer, stage_end_layers, budgets, final_budget=None)
     return pts
 
 
-def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER, kv_out=None):
+def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER, kv_out=None, trace=None):
     """The same decoder layer with every row computed: no probes, no
     selection.  This is the dense-prefill baseline that SPTS is compared
     against ([SPTS] Table 4 compares TTFT against the full model).  x [n, d]
@@ -281,6 +289,8 @@ def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER, kv_ou
     n, d = x.shape
     Hq, Hkv, dh = cfg.Hq, cfg.Hkv, cfg.dh
     rope = cfg.theta is not None
+    if trace is not None:
+        trace.update(x_in=x.clone(), pos_in=pos.clone(), dense=True)
     if cfg.prenorm:
         with tm("rmsnorm", 4.0 * n * d):
             xt = capi.spts_rmsnorm(x, cfg.eps)
@@ -308,28 +318,34 @@ def dense_layer(x, pos, w, cfg: LayerConfig, rope_table=None, tm=NO_TIMER, kv_ou
             H = capi.spts_linear_swiglu(z, w["wg"], w["wu"])
         with tm("ffn_down_add", 2.0 * n * d * f):
             capi.spts_linear(H, w["wd"], out=x, accumulate=True)
+    if trace is not None:
+        trace["x_out"] = x.clone()
     return x
 
 
 def prefill_schedule(x0, layers, cfg: LayerConfig, n_layers, first_skip_layer, points, dense=False,
-                     tm=NO_TIMER, kv_out=None):
+                     tm=NO_TIMER, kv_out=None, traces=None):
     """Prefill of an n_layers model: layers before first_skip_layer are dense,
     the rest are SPTS layers pruned at `points` ([SPTS] Table B gives such a
     schedule per model).  dense=True runs every layer dense (the full-model
     baseline).  Layer li uses weights layers[li % len(layers)].  Returns the
-    residual over the final candidates and their original positions."""
+    residual over the final candidates and their original positions.
+    traces: if a list, receives one trace dict per layer."""
     N = x0.shape[0]
     x = x0.clone()
     pos = torch.arange(N, dtype=torch.int32, device=x0.device)
     table = capi.spts_rope_table(N, cfg.dh, cfg.theta, x0.device) if cfg.theta is not None else None
     for li in range(n_layers):
         w = layers[li % len(layers)]
+        tr = {} if traces is not None else None
         if dense or li < first_skip_layer:
-            x = dense_layer(x, pos, w, cfg, table, tm=tm, kv_out=kv_out)
+            x = dense_layer(x, pos, w, cfg, table, tm=tm, kv_out=kv_out, trace=tr)
         else:
             budget = points.get(li)
             prune = budget if budget is not None and budget < x.shape[0] else None
-            x, pos = spts_layer(x, pos, w, cfg, table, prune_to=prune, tm=tm, kv_out=kv_out)
+            x, pos = spts_layer(x, pos, w, cfg, table, prune_to=prune, tm=tm, kv_out=kv_out, trace=tr)
+        if traces is not None:
+            traces.append(tr)
     return x, pos
 
 

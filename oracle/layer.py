@@ -40,12 +40,18 @@ from .ffn import swiglu_rows
 from .normrope import rmsnorm, rope
 
 
-def _proj(x, w, heads, dh, pos=None, theta=None):
+def project(x, w, heads, dh, pos=None, theta=None):
+    """One head-shaped projection as the layer stores it: x W^T accumulated
+    to fp32, rotated (RoPE at `pos`) when theta is given, rounded to bf16.
+    x [rows, d], w [heads*dh, d] -> [rows, heads, dh] float64."""
     acc = f32(x @ np.asarray(w, dtype=np.float64).T)
     acc = acc.reshape(x.shape[0], heads, dh)
     if theta is not None:
         acc = rope(acc, pos, theta)
     return bf16(acc)
+
+
+_proj = project
 
 
 def attention_block(x, pos, w, cfg, k_given=None, prune_to=None):

@@ -56,3 +56,24 @@ def window_violations(oracle_scores, idx, k, n_forced, rel=WINDOW_REL):
     bad_in = free[chosen[free] & (s[free] < t * (1 - rel))]
     bad_out = free[~chosen[free] & (s[free] > t * (1 + rel))]
     return len(bad_in) + len(bad_out)
+
+
+def agreeing_rows(final_pos, gpu_layers, ref_layers):
+    """Original positions among final_pos whose every decision agreed in a
+    free run: in each layer, membership in the candidate set, in the
+    attention selection and in the FFN selection is the same on both sides.
+    gpu_layers / ref_layers: per layer (pos, idx, idx_f) with pos the
+    layer's candidates (original positions, after any pruning) and idx /
+    idx_f indices into them (idx_f None for an attention-only layer)."""
+    final_pos = np.asarray(final_pos, dtype=np.int64)
+    ok = np.ones(len(final_pos), bool)
+
+    def members(pos, rows):
+        return np.isin(final_pos, np.asarray(pos, dtype=np.int64)[np.asarray(rows, dtype=np.int64)])
+
+    for (gp, gi, gf), (rp, ri, rf) in zip(gpu_layers, ref_layers):
+        ok &= np.isin(final_pos, gp) == np.isin(final_pos, rp)
+        ok &= members(gp, gi) == members(rp, ri)
+        if gf is not None:
+            ok &= members(gp, gf) == members(rp, rf)
+    return final_pos[ok]
