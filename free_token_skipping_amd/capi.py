@@ -28,7 +28,8 @@ EXPORTS = [
     "spts_ltp_structured_workspace", "spts_ltp_probe_structured",
     "spts_decode_attention_workspace", "spts_decode_linear", "spts_decode_linear_rope", "spts_decode_swiglu",
     "spts_decode_attention", "spts_decode_step_workspace", "spts_decode_step",
-    "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_score_topk_batched", "spts_gather", "spts_scatter",
+    "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_score_topk_batched",
+    "spts_score_topk_noalloc", "spts_gather", "spts_scatter",
     "spts_reduced_attention", "spts_ltp_probe", "spts_reduced_ffn", "spts_msdp_stage",
     "spts_linear", "spts_linear_rope", "spts_linear_kv", "spts_linear_swiglu", "spts_rope_table",
     "spts_rmsnorm",
@@ -64,6 +65,7 @@ _SIGS = {
     "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
     "spts_score_topk_multiply": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "spts_score_topk_noalloc": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
     "spts_score_topk_batched": (_I, [_P, _P, _c.c_int64, _I, _I, _I, _I, _P, _c.c_int64]),
     "spts_gather": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "spts_scatter": (_I, [_P, _I, _P, _P, _I, _I, _P, _I]),
@@ -212,6 +214,21 @@ def spts_score_topk(s_a, k, n_forced, s_b=None, w_a=0.5, w_b=0.5, idx=None, fuse
                                       float(w_a), float(w_b), n, int(k), int(n_forced),
                                       _ptr(idx, torch.int32, "idx"), _ptr(fused_out, torch.float32, "fused_out")),
            "spts_score_topk")
+    return idx
+
+
+def spts_score_topk_noalloc(s_a, k, n_forced, idx, s_b=None, w_a=0.5, w_b=0.5, fused_out=None):
+    """spts_score_topk without a workspace: the library's static per-GPU
+    scratch holds the keys (n <= 1048576); idx (and fused_out) are the
+    caller's.  Calls overlapping on one GPU race on that scratch."""
+    n = s_a.shape[0]
+    ctx = context()
+    h = ctx.bind(0, s_a.device)
+    _check(ctx, lib().spts_score_topk_noalloc(h, _ptr(s_a, torch.float32, "s_a"), _ptr(s_b, torch.float32, "s_b"),
+                                              float(w_a), float(w_b), n, int(k), int(n_forced),
+                                              _ptr(idx, torch.int32, "idx"),
+                                              _ptr(fused_out, torch.float32, "fused_out")),
+           "spts_score_topk_noalloc")
     return idx
 
 

@@ -220,6 +220,22 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
                     "score_topk");
 }
 
+spts_status spts_score_topk_noalloc(spts_ctx* ctx, const float* s_a, const float* s_b, float w_a, float w_b,
+                                    int n, int k, int n_forced, int32_t* idx, float* fused_out) {
+  CHECK_CTX();
+  REQUIRE_PTR(s_a); REQUIRE_PTR(idx);
+  REQUIRE_ALIGN(s_a); REQUIRE_ALIGN(idx);
+  if (s_b) REQUIRE_ALIGN(s_b);
+  if (fused_out) REQUIRE_ALIGN(fused_out);
+  REQUIRE(n >= 1, SPTS_ERR_SHAPE, "n must be >= 1");
+  REQUIRE(n <= kTopkNoallocMaxN, SPTS_ERR_UNSUPPORTED,
+          "score_topk_noalloc holds at most %d scores in its static scratch (n=%d)", kTopkNoallocMaxN, n);
+  REQUIRE(n_forced >= 0 && n_forced <= k && n_forced <= n, SPTS_ERR_SHAPE,
+          "need 0 <= n_forced <= k and n_forced <= n (n=%d k=%d n_forced=%d)", n, k, n_forced);
+  return hip_status(ctx, launch_topk_noalloc(s_a, s_b, w_a, w_b, false, n, k, n_forced, idx, fused_out, ctx->stream),
+                    "score_topk_noalloc");
+}
+
 spts_status spts_score_topk_batched(spts_ctx* ctx, const float* s, int64_t s_stride, int batch, int n, int k,
                                     int n_forced, int32_t* idx, int64_t idx_stride) {
   CHECK_CTX();

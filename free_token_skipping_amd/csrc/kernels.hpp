@@ -80,6 +80,11 @@ size_t topk_workspace(int n);
 // or by their product (multiply == true)
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
                        int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s);
+// launch_topk with the key storage in a static per-GPU device array instead
+// of a workspace: no allocation; n <= kTopkNoallocMaxN (else hipErrorInvalidValue)
+constexpr int kTopkNoallocMaxN = 1 << 20;
+hipError_t launch_topk_noalloc(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
+                               int k, int n_forced, int32_t* idx, float* fused_out, hipStream_t s);
 // one workgroup per score row (rows of at most 1024 * 32 scores, keys in registers)
 hipError_t launch_topk_batched(const float* s, long s_stride, int batch, int n, int k, int n_forced, int32_t* idx,
                                long idx_stride, hipStream_t st);

@@ -17,6 +17,8 @@
 // (the usual case), those keys are copied to LDS and a single wave finishes
 // the remaining digits over them, with no workgroup barrier per digit; a
 // larger bin (many equal scores) continues with 8-bit workgroup passes.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -462,6 +464,42 @@ hipError_t launch_topk_batched(const float* s, long s_stride, int batch, int n, 
 }
 
 size_t topk_workspace(int n) { return (((size_t)n * 4) + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------- allocation-free top-k
+// Key storage of launch_topk_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Its host-side name is not a device
+// address; host code uses only the address hipGetSymbolAddress gives for the
+// current device, resolved once per device.  Every call on one GPU shares it
+// (the kernel writes each key before reading it, so nothing needs clearing),
+// so calls that overlap on one GPU race.
+static __device__ __align__(256) uint32_t scratch[kTopkNoallocMaxN];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+uint32_t* scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t launch_topk_noalloc(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
+                               int k, int n_forced, int32_t* idx, float* fused_out, hipStream_t s) {
+  if (n > kTopkNoallocMaxN) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint32_t* keys;
+  {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      scratch_ptr[dev] = reinterpret_cast<uint32_t*>(p);
+    }
+    keys = scratch_ptr[dev];
+  }
+  return launch_topk(s_a, s_b, w_a, w_b, multiply, n, k, n_forced, idx, fused_out, keys, s);
+}
 
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
                        int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s) {

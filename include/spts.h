@@ -130,6 +130,20 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
                             float w_b, int n, int k, int n_forced, int32_t* idx,
                             float* fused_out);
 
+/* spts_score_topk without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, rules and results as
+ * spts_score_topk; the context's workspace is not used.  The keys of a
+ * selection over more than 32768 scores go to a static device array of the
+ * library (1048576 entries, 4 MiB, one per GPU, held until the process
+ * ends) instead of the workspace; nothing is allocated or freed.  Every call
+ * on one GPU shares that array, so calls that overlap on one GPU (on
+ * different streams or host threads) race; calls in one stream's order do
+ * not.  Requires n <= 1048576 (SPTS_ERR_UNSUPPORTED otherwise). */
+spts_status spts_score_topk_noalloc(spts_ctx* ctx, const float* s_a, const float* s_b, float w_a,
+                                    float w_b, int n, int k, int n_forced, int32_t* idx,
+                                    float* fused_out);
+
 /* spts_score_topk (one score, no fusion) on `batch` independent rows in one
  * launch, one workgroup per row: row b reads s + b * s_stride and writes
  * min(k, n) ascending indices to idx + b * idx_stride (same rule: last

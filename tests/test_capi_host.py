@@ -109,6 +109,11 @@ def test_select_validation(L, ctx):
     assert f(ctx, FAKE, None, 0.5, 0.5, 0, 0, 0, FAKE, None) == SHAPE      # n = 0
     assert f(ctx, FAKE, None, 0.5, 0.5, 10, 4, 1, FAKE, None) == NOMEM
     assert f(ctx, FAKE, MIS, 0.5, 0.5, 10, 4, 1, FAKE, None) == ALIGN
+    na = L.spts_score_topk_noalloc
+    assert na(ctx, None, None, 0.5, 0.5, 10, 4, 1, FAKE, None) == INVALID
+    assert na(ctx, FAKE, None, 0.5, 0.5, 10, 4, 5, FAKE, None) == SHAPE
+    assert na(ctx, FAKE, None, 0.5, 0.5, (1 << 20) + 1, 4, 1, FAKE, None) == UNSUPPORTED   # beyond its scratch
+    assert b"static scratch" in L.spts_last_error(ctx)
     m = L.spts_score_topk_multiply
     assert m(ctx, FAKE, None, 10, 4, 1, FAKE, None) == INVALID            # s_b required
     assert m(ctx, FAKE, FAKE, 10, 4, 5, FAKE, None) == SHAPE
