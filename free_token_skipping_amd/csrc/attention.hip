@@ -33,52 +33,6 @@ __device__ __forceinline__ int vswz(int d, int chunk) { return d * KT + ((chunk 
 // MFMA A-row -> key row within a 32-key tile: swap index bits 2 and 3.
 __device__ __forceinline__ int perm32(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
-// Stage one K tile (and optionally the transposed V tile) of KV head g.
-// Rows >= n are clamped to n-1 (they are always masked).
-struct TileRegs { u32x4 k[4]; u32x4 v[4]; };
-
-__device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* k, const uint16_t* v, int j0,
-                                          int n, int Hkv, int g, int tid, bool with_v) {
-  const long row_stride = (long)Hkv * DH;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {        // K: thread -> row tid/16 + 16 i, chunk tid%16
-    int j = j0 + (tid >> 4) + 16 * i;
-    j = j < n ? j : n - 1;
-    t.k[i] = ld16(k + j * row_stride + g * DH + (tid & 15) * 8);
-  }
-  if (with_v) {                        // V: thread -> keys 4*(tid%16)+q, dh chunk tid/16
-    const int kq4 = tid & 15, dc = tid >> 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int j = j0 + kq4 * 4 + q;
-      j = j < n ? j : n - 1;
-      t.v[q] = ld16(v + j * row_stride + g * DH + dc * 8);
-    }
-  }
-}
-
-__device__ __forceinline__ void store_tile(const TileRegs& t, uint16_t* ks, uint16_t* vts, int tid,
-                                           bool with_v) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st16(ks + kswz((tid >> 4) + 16 * i, tid & 15), t.k[i]);
-  if (with_v) {
-    const int kq4 = tid & 15, dc = tid >> 4;
-    // transpose 4 keys x 8 dh -> 8 rows of 4 keys (8 bytes each)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const bool hiw = e & 1;
-      uint32_t x[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = hiw ? (t.v[q][w] >> 16) : (t.v[q][w] & 0xFFFFu);
-      u32x2 out;
-      out[0] = x[0] | (x[1] << 16);
-      out[1] = x[2] | (x[3] << 16);
-      *reinterpret_cast<u32x2*>(vts + vswz(dc * 8 + e, kq4 >> 1) + (kq4 & 1) * 4) = out;
-    }
-  }
-}
-
 // ============================================================ reduced attention
 // grid: ceil(kq/64) * Hq/4 workgroups, one per (64-query block, group of 4
 // query heads); block 512 = 8 waves: wave w serves query head 4*hg + (w & 3)
@@ -375,97 +329,179 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 }
 
 // =============================================================== PAP probe
-// Pass 1: per key chunk, per head, partial (max, sum) of the probe softmax
-// in log2 units.  grid (ceil(n/chunk), Hq/4), 4 waves = 4 heads.  A chunk is
-// a multiple of the 64-key tile between 128 and 1024 keys: the shortest whose
-// grid still fits in one round of resident workgroups (two per compute unit
-// for P <= 64, one for P = 128, as the kernels' registers allow).  A partly
-// filled second round costs a whole chunk's time, while every workgroup also
-// loads all P probe queries of its 4 heads, so chunks stay as long as that
-// round allows; past 1024 keys the grid runs in several rounds.
+// Two passes over the keys, both on v_mfma_f32_32x32x16_bf16 with 64-key K
+// tiles in LDS shared by the waves of a workgroup.  A workgroup is (key
+// chunk, group of 4 query heads that share one KV head); each of its waves
+// holds the queries of 32*PT probes of one head in registers, and
+// P / (32*PT) waves per head cover all P probes (8 waves at P = 128, so no
+// wave holds more than 64 probes' queries).
+//
+// K tiles stream straight from global memory into a ring of NS LDS stages
+// (global_load_lds, the swizzle applied on the global side), NS-1 tiles
+// ahead of the one being scored: one tile in flight per workgroup left the
+// passes waiting on load latency.
+//
+// Pass 1 (stats): per (chunk, head, probe) the running max and sum of
+// exp2(scale*log2e * logit), logits as S^T = K Q^T so a lane owns a probe.
+// The reference max moves only when a tile's max passes it by 2^8 (exp2
+// units), so a tile costs one max, one fma, one exp and one add per logit.
+// Combine: per (head, probe) the chunk partials merge into
+// M = max + log2(sum).
+// Pass 2 (column sums): logits as S = Q K^T so a lane owns a key, and each
+// logit adds exp2(scale*log2e * logit - M) = its softmax weight to its key's
+// sum: one fma, one exp and one add per logit.  The head quad's sums are
+// added in a fixed order in LDS; a last launch adds the head quads in a
+// fixed order.  Causal masking is applied only to the tiles that reach past
+// the first probe row (the last one or two tiles of the sequence).  No float
+// atomics: the result does not depend on scheduling.
+//
+// A key chunk is a multiple of the 64-key tile between 128 and 1024 keys:
+// the shortest whose grid of chunks x head quads fits one round of resident
+// workgroups.  A partly filled second round costs a whole chunk's time, while
+// every workgroup also loads its probes' queries, so chunks stay as long as
+// that round allows; past 1024 keys the grid runs in several rounds.
 constexpr int MIN_CHUNK = 128;
+constexpr float kProbeLazy = 8.0f;   // exp2 units
+constexpr int NS = 4;                // K tile stages in LDS
 
 int probe_chunk(int n, int Hq, int P) {
-  const long slots = 256L * (P <= 64 ? 2 : 1);
+  const long slots = 256L * (P <= 64 ? 2 : 1);                     // two waves per SIMD: 2 or 1 workgroups per CU
   const long need = ((long)n * (Hq / 4) + slots - 1) / slots;      // keys per chunk for one round
   const int c = (int)(((need + KT - 1) / KT) * KT);
   return c < MIN_CHUNK ? MIN_CHUNK : (c > 1024 ? 1024 : c);
 }
 
-template <int PT>   // probe column tiles of 32 (P = 32*PT)
-__global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __restrict__ q,
-                                                             const uint16_t* __restrict__ k, int n,
-                                                             int chunk_keys,
-                                                             int Hq, int Hkv, float sl2,
-                                                             float* __restrict__ part_m,
-                                                             float* __restrict__ part_l) {
-  constexpr int P = 32 * PT;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * DH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
-  const int h = blockIdx.y * 4 + wave;
-  const int g = (blockIdx.y * 4) / (Hq / Hkv);
-  const int chunk = blockIdx.x;
-  const int nt = min(chunk_keys / KT, (n - chunk * chunk_keys + KT - 1) / KT);   // key tiles of this chunk
+// Issue the global -> LDS copy of the K tile [64 keys][128] of KV head g at
+// key j0 into `stage`, NT threads.  Instruction i of wave w fills the 1 KiB
+// block of keys 4*blk .. 4*blk+3 (blk = w*PER + i): lane L writes physical
+// chunk L%16 of key 4*blk + L/16, so it fetches logical chunk
+// (L%16) ^ (key & 15) -- the kswz swizzle, applied on the global side.  Keys
+// >= n clamp to n-1 (always masked).
+template <int NT>
+__device__ __forceinline__ void issue_k_tile(uint16_t* stage, const uint16_t* k, int j0, int n, int Hkv, int g,
+                                             int tid) {
+  constexpr int PER = 16 / (NT / 64);   // 1 KiB blocks per wave
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int blk = wave * PER + i;
+    const int key = blk * 4 + (lane >> 4);
+    const int lch = (lane & 15) ^ (key & 15);
+    int j = j0 + key;
+    j = j < n ? j : n - 1;
+    const uint16_t* src = k + (long)j * Hkv * DH + g * DH + lch * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(stage + blk * 512), 16, 0, 0);
+  }
+}
 
-  // tile t is read from Ks[t & 1] while tile t+1 is in flight in registers
-  TileRegs tr;
-  load_tile(tr, k, nullptr, chunk * chunk_keys, n, Hkv, g, tid, false);
-  bf16x8 qf[PT][8];
+// Workgroup barrier once at most `tiles` K-tile copies of this thread are
+// still in flight: s_waitcnt on vmcnt (the copies are counted in issue
+// order) and on lgkmcnt (this wave's LDS stores), then s_barrier.  A plain
+// __syncthreads would also wait for every copy still in flight.
+template <int NT>
+__device__ __forceinline__ void barrier_k_tiles(int tiles) {
+  constexpr int PER = 16 / (NT / 64);
+  static_assert(PER * (NS - 2) < 16, "vmcnt field");
+  if (tiles >= 2) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * PER));
+  else if (tiles == 1) __builtin_amdgcn_s_waitcnt(0x0070 | PER);
+  else __builtin_amdgcn_s_waitcnt(0x0070);
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int PT>
+__device__ __forceinline__ void load_probe_q(bf16x8 (&qf)[PT][8], const uint16_t* q, int pbase, int Hq, int h,
+                                             int l32, int half) {
 #pragma unroll
   for (int c = 0; c < PT; ++c)
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)(c * 32 + l32) * Hq + h) * DH + kk * 16 + half * 8);
+      qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)(pbase + c * 32 + l32) * Hq + h) * DH + kk * 16 +
+                                                   half * 8);
+}
+
+template <int PT, int PW>   // each wave: 32*PT probes of one head; PW waves per head; P = 32*PT*PW
+__global__ __launch_bounds__(256 * PW, 2 / PW) void probe_stats_kernel(const uint16_t* __restrict__ q,
+                                                                       const uint16_t* __restrict__ k, int n,
+                                                                       int chunk_keys, int Hq, int Hkv, float sl2,
+                                                                       float* __restrict__ part_m,
+                                                                       float* __restrict__ part_l) {
+  constexpr int P = 32 * PT * PW, NT = 256 * PW;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NS][KT * DH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int h = blockIdx.y * 4 + (wave & 3);
+  const int pbase = (wave >> 2) * 32 * PT;            // this wave's first probe
+  const int g = (blockIdx.y * 4) / (Hq / Hkv);
+  const int chunk = blockIdx.x;
+  const int c0 = chunk * chunk_keys;
+  const int nt = min(chunk_keys / KT, (n - c0 + KT - 1) / KT);   // key tiles of this chunk
+  const int first_probe_row = n - P;
+
+  bf16x8 qf[PT][8];
+  load_probe_q<PT>(qf, q, pbase, Hq, h, l32, half);
+  __builtin_amdgcn_s_waitcnt(0x0F70);                 // the queries land before any K tile is counted
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nt) issue_k_tile<NT>(Ks[s], k, c0 + s * KT, n, Hkv, g, tid);
   float m[PT], l[PT];
 #pragma unroll
   for (int c = 0; c < PT; ++c) { m[c] = -INFINITY; l[c] = 0.f; }
-  store_tile(tr, Ks[0], nullptr, tid, false);
-  __syncthreads();
+
+  // one tile's logits into the running (max, sum) of each probe, 32 keys at a
+  // time (the K fragments of those keys are shared by the PT probe tiles);
+  // MASK: the tile reaches past the first probe row (causal mask per key)
+  auto tile = [&](auto mask, const uint16_t* kt_s, int j0) {
+    constexpr bool MASK = decltype(mask)::value;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      bf16x8 kf[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        kf[kk] = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+#pragma unroll
+      for (int c = 0; c < PT; ++c) {
+        f32x16 s;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) s = mfma32x32x16(kf[kk], qf[c][kk], kk == 0 ? f32x16{} : s);
+        if constexpr (MASK) {
+          // reg r holds key j0 + kt*32 + (r>>3)*16 + half*8 + (r&7)
+          const int prow = first_probe_row + pbase + c * 32 + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7) > prow) s[r] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
+        mx *= sl2;
+        // each lane moves its own reference when its logits pass it by 2^8
+        const float mref = mx > m[c] + kProbeLazy ? mx : m[c];
+        const float alpha = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[c] - mref);
+        m[c] = mref;
+        const float mz = mref == -INFINITY ? 0.f : mref;   // a lane with no visible key yet adds zeros
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -mz));
+          a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2, -mz));
+          a2 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 2], sl2, -mz));
+          a3 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 3], sl2, -mz));
+        }
+        l[c] = l[c] * alpha + ((a0 + a1) + (a2 + a3));
+      }
+    }
+  };
 
   for (int t = 0; t < nt; ++t) {
-    const int j0 = chunk * chunk_keys + t * KT;
-    if (t + 1 < nt) load_tile(tr, k, nullptr, j0 + KT, n, Hkv, g, tid, false);
-    const uint16_t* kt_s = Ks[t & 1];
-#pragma unroll
-    for (int c = 0; c < PT; ++c) {
-      const int prow = n - P + c * 32 + l32;
-      f32x16 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
-          s[kt] = mfma32x32x16(kf, qf[c][kk], s[kt]);
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7);
-          float x = s[kt][r] * sl2;
-          if (key > prow) x = -INFINITY;
-          s[kt][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      const float mnew = fmaxf(m[c], mx);
-      if (mnew == -INFINITY) continue;     // nothing visible yet for this probe
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rs += __builtin_amdgcn_exp2f(s[kt][r] - mnew);
-      l[c] = l[c] * __builtin_amdgcn_exp2f(m[c] - mnew) + rs;
-      m[c] = mnew;
-    }
-    // the next tile goes to the other buffer, read last in step t-1 (before
-    // the barrier that ended it)
-    if (t + 1 < nt) store_tile(tr, Ks[(t + 1) & 1], nullptr, tid, false);
-    __syncthreads();
+    const int j0 = c0 + t * KT;
+    // every thread's copies of tile t have landed; stage (t-1) % NS is free
+    barrier_k_tiles<NT>(min(NS - 2, nt - 1 - t));
+    if (t + NS - 1 < nt) issue_k_tile<NT>(Ks[(t + NS - 1) % NS], k, j0 + (NS - 1) * KT, n, Hkv, g, tid);
+    if (j0 + KT - 1 > first_probe_row)                // uniform: only the last tiles of the sequence
+      tile(std::true_type{}, Ks[t % NS], j0);
+    else
+      tile(std::false_type{}, Ks[t % NS], j0);
   }
   // merge the two half-waves (they hold different keys of the same probes)
 #pragma unroll
@@ -475,19 +511,19 @@ __global__ __launch_bounds__(256, 1) void probe_stats_kernel(const uint16_t* __r
     float lt = 0.f;
     if (mt != -INFINITY) lt = l[c] * exp2f(m[c] - mt) + l2 * exp2f(m2 - mt);
     if (half == 0) {
-      const long o = ((long)chunk * Hq + h) * P + c * 32 + l32;
+      const long o = ((long)chunk * Hq + h) * P + pbase + c * 32 + l32;
       part_m[o] = mt;
       part_l[o] = lt;
     }
   }
 }
 
-// Pass 1b: combine chunk partials -> per (head, probe) max and 1/sum.  One
-// wave per (head, probe); lanes stride over chunks, fixed-order wave tree.
+// Combine chunk partials -> per (head, probe) M = max + log2(sum) in exp2
+// units.  One wave per (head, probe); lanes stride over chunks, fixed-order
+// wave tree.
 __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restrict__ part_m,
                                                             const float* __restrict__ part_l, int nchunks,
-                                                            int HP, float* __restrict__ fin_m,
-                                                            float* __restrict__ fin_il) {
+                                                            int HP, float* __restrict__ fin_M) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= HP) return;
@@ -500,56 +536,44 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restr
     if (mc != -INFINITY) lt += part_l[(long)c * HP + i] * exp2f(mc - mt);
   }
   lt = wave_sum(lt);
-  if (lane == 0) {
-    fin_m[i] = mt;
-    fin_il[i] = 1.0f / lt;
-  }
+  if (lane == 0) fin_M[i] = mt + log2f(lt);
 }
 
 // Pass 2: column sums of the normalised probe softmax for one key chunk and
 // one head quad; logits formed as S = Q K^T so a lane owns one key.
-template <int PT>
-__global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k, int n,
-                                                              int chunk_keys,
-                                                              int Hq, int Hkv, float sl2,
-                                                              const float* __restrict__ fin_m,
-                                                              const float* __restrict__ fin_il,
-                                                              float* __restrict__ quad_sum) {
-  constexpr int P = 32 * PT;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * DH];
-  __shared__ __attribute__((aligned(16))) float st_m[4][P];
-  __shared__ __attribute__((aligned(16))) float st_il[4][P];
-  __shared__ float red[2][4][KT];
+template <int PT, int PW>
+__global__ __launch_bounds__(256 * PW, 2 / PW) void probe_colsum_kernel(const uint16_t* __restrict__ q,
+                                                                        const uint16_t* __restrict__ k, int n,
+                                                                        int chunk_keys, int Hq, int Hkv, float sl2,
+                                                                        const float* __restrict__ fin_M,
+                                                                        float* __restrict__ quad_sum) {
+  constexpr int P = 32 * PT * PW, NT = 256 * PW, NW = 4 * PW;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NS][KT * DH];
+  __shared__ __attribute__((aligned(16))) float st_M[4][P];
+  __shared__ float red[2][NW][KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int h = blockIdx.y * 4 + wave;
+  const int hw = wave & 3;
+  const int h = blockIdx.y * 4 + hw;
+  const int pbase = (wave >> 2) * 32 * PT;
   const int g = (blockIdx.y * 4) / (Hq / Hkv);
   const int chunk = blockIdx.x;
-  const int nt = min(chunk_keys / KT, (n - chunk * chunk_keys + KT - 1) / KT);   // key tiles of this chunk
+  const int c0 = chunk * chunk_keys;
+  const int nt = min(chunk_keys / KT, (n - c0 + KT - 1) / KT);
+  const int first_probe_row = n - P;
 
-  // tile t is read from Ks[t & 1] while tile t+1 is in flight in registers
-  TileRegs tr;
-  load_tile(tr, k, nullptr, chunk * chunk_keys, n, Hkv, g, tid, false);
-  for (int i = tid; i < 4 * P; i += 256) {
-    const int hh = blockIdx.y * 4 + i / P, p = i % P;
-    st_m[i / P][p] = fin_m[hh * P + p];
-    st_il[i / P][p] = fin_il[hh * P + p];
-  }
+  for (int i = tid; i < 4 * P; i += NT) st_M[i / P][i % P] = fin_M[(blockIdx.y * 4 + i / P) * P + i % P];
   bf16x8 qf[PT][8];
+  load_probe_q<PT>(qf, q, pbase, Hq, h, l32, half);
+  __builtin_amdgcn_s_waitcnt(0x0F70);                 // queries and M land before any K tile is counted
 #pragma unroll
-  for (int c = 0; c < PT; ++c)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[c][kk] = *reinterpret_cast<const bf16x8*>(q + ((long)(c * 32 + l32) * Hq + h) * DH + kk * 16 + half * 8);
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nt) issue_k_tile<NT>(Ks[s], k, c0 + s * KT, n, Hkv, g, tid);
 
-  store_tile(tr, Ks[0], nullptr, tid, false);
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const int j0 = chunk * chunk_keys + t * KT;
-    if (t + 1 < nt) load_tile(tr, k, nullptr, j0 + KT, n, Hkv, g, tid, false);
-    const uint16_t* kt_s = Ks[t & 1];
-    float colsum[2] = {0.f, 0.f};
+  // one tile's softmax weights summed per key (lane = key); MASK: the tile
+  // reaches past the first probe row
+  auto tile = [&](auto mask, const uint16_t* kt_s, int j0, float (&cs)[2]) {
+    constexpr bool MASK = decltype(mask)::value;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = j0 + kt * 32 + perm32(l32);          // this lane's key column
@@ -557,39 +581,55 @@ __global__ __launch_bounds__(256, 1) void probe_colsum_kernel(const uint16_t* __
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         kf[kk] = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
       for (int c = 0; c < PT; ++c) {
         f32x16 s;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) s = mfma32x32x16(qf[c][kk], kf[kk], s);
-        // reg r -> probe row p = c*32 + (r>>2)*8 + half*4 + (r&3)
+        for (int kk = 0; kk < 8; ++kk) s = mfma32x32x16(qf[c][kk], kf[kk], kk == 0 ? f32x16{} : s);
+        // reg r -> probe row pbase + c*32 + (r>>2)*8 + half*4 + (r&3)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-          const int pb = c * 32 + qd * 8 + half * 4;
-          const f32x4 mm = *reinterpret_cast<const f32x4*>(&st_m[wave][pb]);
-          const f32x4 il = *reinterpret_cast<const f32x4*>(&st_il[wave][pb]);
+          const int pb = pbase + c * 32 + qd * 8 + half * 4;
+          const f32x4 mm = *reinterpret_cast<const f32x4*>(&st_M[hw][pb]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int prow = n - P + pb + e;
-            if (key <= prow) colsum[kt] += __builtin_amdgcn_exp2f(s[qd * 4 + e] * sl2 - mm[e]) * il[e];
+            float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qd * 4 + e], sl2, -mm[e]));
+            if constexpr (MASK) w = key > first_probe_row + pb + e ? 0.f : w;
+            if (e & 1) a1 += w; else a0 += w;
           }
         }
       }
+      cs[kt] = a0 + a1;
     }
-    // add the other half-wave (other probe rows), then the 4 heads
+  };
+
+  for (int t = 0; t < nt; ++t) {
+    const int j0 = c0 + t * KT;
+    // tile t in LDS; stage (t-1) % NS free; red[(t-1) & 1] read (after last step's barrier)
+    barrier_k_tiles<NT>(min(NS - 2, nt - 1 - t));
+    if (t + NS - 1 < nt) issue_k_tile<NT>(Ks[(t + NS - 1) % NS], k, j0 + (NS - 1) * KT, n, Hkv, g, tid);
+    float cs[2];
+    if (j0 + KT - 1 > first_probe_row)
+      tile(std::true_type{}, Ks[t % NS], j0, cs);
+    else
+      tile(std::false_type{}, Ks[t % NS], j0, cs);
+    // add the other half-wave (other probe rows), then the waves of the quad
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) colsum[kt] += __shfl_xor(colsum[kt], 32);
+    for (int kt = 0; kt < 2; ++kt) cs[kt] += __shfl_xor(cs[kt], 32);
     float(*rd)[KT] = red[t & 1];
     if (half == 0) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) rd[wave][kt * 32 + perm32(l32)] = colsum[kt];
+      for (int kt = 0; kt < 2; ++kt) rd[wave][kt * 32 + perm32(l32)] = cs[kt];
     }
-    if (t + 1 < nt) store_tile(tr, Ks[(t + 1) & 1], nullptr, tid, false);
-    __syncthreads();
-    if (tid < KT && j0 + tid < n)
-      quad_sum[(long)blockIdx.y * n + j0 + tid] = ((rd[0][tid] + rd[1][tid]) + rd[2][tid]) + rd[3][tid];
+    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): the sums are in LDS (vmcnt untouched)
+    __builtin_amdgcn_s_barrier();
+    if (tid < KT && j0 + tid < n) {
+      float tot = rd[0][tid];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) tot += rd[w][tid];
+      quad_sum[(long)blockIdx.y * n + j0 + tid] = tot;
+    }
   }
 }
 
@@ -674,7 +714,7 @@ __global__ void attn_f32_kernel(const float* q, const int32_t* idx, const float*
 size_t probe_workspace(int n, int P, int Hq) {
   const size_t nchunks = (size_t)(n + MIN_CHUNK - 1) / MIN_CHUNK;   // bound for every chunk size
   const size_t HP = (size_t)Hq * P;
-  // part_m, part_l [nchunks*HP]; fin_m, fin_il [HP]; quad_sum [Hq/4 * n]
+  // part_m, part_l [nchunks*HP]; fin_M [HP] (2*HP reserved); quad_sum [Hq/4 * n]
   size_t b = 2 * nchunks * HP * 4 + 2 * HP * 4 + (size_t)((Hq + 3) / 4) * n * 4;
   return (b + 255) & ~(size_t)255;
 }
@@ -686,24 +726,23 @@ hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P,
   const long HP = (long)Hq * P;
   float* part_m = reinterpret_cast<float*>(ws);
   float* part_l = part_m + nchunks * HP;
-  float* fin_m = part_l + nchunks * HP;
-  float* fin_il = fin_m + HP;
-  float* quad = fin_il + HP;
+  float* fin_M = part_l + nchunks * HP;
+  float* quad = fin_M + 2 * HP;
   const float sl2 = scale * kLog2e;
   const dim3 grid(nchunks, Hq / 4);
-  switch (P / 32) {
-#define SPTS_PROBE_CASE(PT)                                                                        \
-  case PT:                                                                                         \
-    hipLaunchKernelGGL(probe_stats_kernel<PT>, grid, dim3(256), 0, s, q, k, n, ck, Hq, Hkv, sl2,  \
-                       part_m, part_l);                                                            \
-    hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_m,         \
-                       part_l, nchunks, (int)HP, fin_m, fin_il);                                   \
-    hipLaunchKernelGGL(probe_colsum_kernel<PT>, grid, dim3(256), 0, s, q, k, n, ck, Hq, Hkv, sl2, \
-                       fin_m, fin_il, quad);                                                       \
+  switch (P) {
+#define SPTS_PROBE_CASE(PP, PT, PW)                                                                     \
+  case PP:                                                                                              \
+    hipLaunchKernelGGL((probe_stats_kernel<PT, PW>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv,  \
+                       sl2, part_m, part_l);                                                            \
+    hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_m, part_l,       \
+                       nchunks, (int)HP, fin_M);                                                        \
+    hipLaunchKernelGGL((probe_colsum_kernel<PT, PW>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv, \
+                       sl2, fin_M, quad);                                                               \
     break;
-    SPTS_PROBE_CASE(1)
-    SPTS_PROBE_CASE(2)
-    SPTS_PROBE_CASE(4)
+    SPTS_PROBE_CASE(32, 1, 1)
+    SPTS_PROBE_CASE(64, 2, 1)
+    SPTS_PROBE_CASE(128, 2, 2)
 #undef SPTS_PROBE_CASE
     default: return hipErrorInvalidValue;
   }

@@ -153,14 +153,16 @@ def test_select_multiply_bit_exact(n, k, nf):
 
 # ------------------------------------------------------------ gather / scatter
 
-@pytest.mark.parametrize("width", [520, 1536])   # 1040-byte rows; 3 KiB rows (1 KiB-segment kernels)
+# 1040-byte, 3 KiB, 8 KiB and 16 KiB rows (1, 1, 2 and 4 units of 16 bytes per
+# thread and row; 4, 4, 2 and 1 rows per workgroup), and 24 KiB rows (grid-stride)
+@pytest.mark.parametrize("width", [520, 1536, 4096, 8192, 12296])
 def test_gather_scatter_bit_exact(width):
     _log(f"gather / scatter width={width}")
     x = W.randn((777, width), seed=9)
-    idx = W.sorted_rows(777, 300, 16, seed=10)
+    idx = W.sorted_rows(777, 301, 16, seed=10)
     g = capi.spts_gather(_cuda(x), _cuda(idx))
     assert torch.equal(g.cpu(), x[idx.long()])
-    src = W.randn((300, width), seed=11)
+    src = W.randn((301, width), seed=11)
     dst = _cuda(x).clone()
     capi.spts_scatter(_cuda(src), _cuda(idx), dst, accumulate=False)
     ref = x.clone()
