@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="standalone gather/scatter kernels")
     ap.add_argument("--cpu-sample", type=float, default=1.0 / 32,
                     help="fraction of row-separable oracle work timed for the CPU baseline")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle's whole 32K layer unsampled (several minutes)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run spts_gather over 1 GiB with identity rows (a plain copy of known size, "
                          "to scale HBM byte counters) and exit")
@@ -163,19 +165,61 @@ def measured_traffic(call):
     return float(m_tr.group(1))
 
 
-def roofline(summary, steps):
+# rocprofv3 kernel names behind a call (main kernel, tail fixup launch), as the
+# committed kernel summary of the 8-layer stack lists them
+ROCPROF_KERNELS = {"ffn_gate_up": ("gemm_tn_kernel<2, true>", "gemm_tail_fixup_kernel<2, true>"),
+                   "reduced_attention": ("attn_bf16_kernel", None),
+                   "kv_proj": ("gemm_tn_kernel<6, false>", "gemm_tail_fixup_kernel<6, false>")}
+STACK_PROFILE = os.path.join(ROOT, "profiles", "msdp_stack_32k_kernel_stats.md")
+
+
+def rocprof_per_call(call):
+    """Average time per call of `call` from the committed rocprofv3 summary of
+    the stack (main kernel plus its tail fixup launches, over the main
+    kernel's launch count), or None."""
+    import re
+    names = ROCPROF_KERNELS.get(call)
+    if not names:
+        return None
+    try:
+        text = open(STACK_PROFILE).read()
+    except OSError:
+        return None
+    rows = {}
+    for m in re.finditer(r"^\|\s*([^|]+?)\s*\|\s*(\d+)\s*\|\s*([0-9.]+)\s*\|", text, re.M):
+        rows[m.group(1)] = (int(m.group(2)), float(m.group(3)))
+    main, fix = names
+    if main not in rows:
+        return None
+    calls, total = rows[main]
+    if fix and fix in rows:
+        total += rows[fix][1]
+    return {"avg_call_ms": round(total / calls, 4), "launches": calls,
+            "source": "profiles/msdp_stack_32k_kernel_stats.md"}
+
+
+def roofline(summary, steps, with_rocprof=False):
     """Dominant single-kernel call by time: achieved = algorithmic FLOPs per
-    launch / average launch time (events on the launching stream)."""
+    launch / average launch time (events on the launching stream).  With
+    with_rocprof, the same figure from the committed rocprofv3 kernel summary
+    of the stack is given beside it."""
     cands = [(ms, name, calls, work) for name, (calls, ms, work) in summary.items() if name in SINGLE_KERNEL_CALLS]
     ms, name, calls, work = max(cands)
     avg_ms = ms / calls
     flops_per_launch = work / calls
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
-            "kernel": KERNEL_OF_CALL.get(name, name), "call": name,
-            "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_ms, 4),
-            "launches_per_step": calls // steps}
+    out = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name),
+           "kernel": KERNEL_OF_CALL.get(name, name), "call": name,
+           "flops_per_launch": flops_per_launch, "avg_launch_ms": round(avg_ms, 4),
+           "launches_per_step": calls // steps}
+    if with_rocprof:
+        rp = rocprof_per_call(name)
+        if rp:
+            a = flops_per_launch / (rp["avg_call_ms"] * 1e-3) / 1e12
+            rp.update(achieved=round(a, 1), frac=round(a / PEAK_BF16_TFLOPS, 4))
+        out["rocprof"] = rp
+    return out
 
 
 # ------------------------------------------------- 32-layer prefill schedule
@@ -295,6 +339,7 @@ def other_workloads(dev, steps, warmup):
       attn_layer_8k     attention-only layer, 8192 tokens, 64 needles, P 64, keep 0.5
       long_128k_score   probe queries -> PAP score -> top-k at 131072 tokens (clustered
                         keys, 512 needles, P 128, keep 0.25)
+      long_layer_128k   the whole 131072-token layer (attention + FFN, keep 0.25 / 0.25)
       long_16k_prefix   the 128K recipe as a full layer on a 16384-token prefix"""
     import torch
     import workloads as W
@@ -304,10 +349,12 @@ def other_workloads(dev, steps, warmup):
     out = {}
 
     def record(name, fn, tokens, extra):
-        total_ms, _, summ, _ = timed(fn, steps, warmup)
+        total_ms, _, summ, summ_dom = timed(fn, steps, warmup)
         ms = total_ms / steps
         out[name] = dict(extra, ms_per_step=round(ms, 4), tokens_per_s=round(tokens / (ms * 1e-3), 1),
                          breakdown=breakdown(summ, steps))
+        if summ_dom and "layer" in name:
+            out[name]["roofline"] = roofline(summ_dom, steps)
         log(f"{name}: {ms:.3f} ms/step, {tokens / (ms * 1e-3):,.0f} tokens/s")
 
     cfg8k = W.CONFIGS["attn_layer_8k"]
@@ -327,7 +374,7 @@ def other_workloads(dev, steps, warmup):
 
     cfg128k = W.CONFIGS["long_layer_128k"]
     sh = cfg128k["shape"]
-    inp = W.make_layer(sh, seed=cfg128k["seed"], with_ffn=False, needles=cfg128k["needles"],
+    inp = W.make_layer(sh, seed=cfg128k["seed"], needles=cfg128k["needles"],
                        clustered_keys=(cfg128k["centroids"], cfg128k["sigma"]))
     xp = inp["x"][-sh.P:].to(dev).contiguous()
     wq = inp["wq"].to(dev)
@@ -343,7 +390,21 @@ def other_workloads(dev, steps, warmup):
             capi.spts_score_topk(S, k, sh.P)
     record("long_128k_score", score128k, sh.n, {"tokens": sh.n, "probes": sh.P, "keep": cfg128k["keep_attn"],
                                                  "needles": cfg128k["needles"], "keys": "clustered"})
-    del inp, xp, wq, kk
+    # the whole 131072-token layer: PAP over the clustered keys, reduced
+    # attention over 32768 selected queries, LTP, fused select, reduced FFN
+    w = {k2: inp[k2].to(dev) for k2 in keys if k2 in inp}     # no Wk: the keys are given
+    x0 = inp["x"].to(dev)
+    pos = torch.arange(sh.n, dtype=torch.int32, device=dev)
+    cfg = LayerConfig(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, keep_attn=cfg128k["keep_attn"],
+                      keep_ffn=cfg128k["keep_ffn"], w_fuse=cfg128k["w_fuse"])
+
+    def layer128k(tm):
+        with tm("layer_setup", 4.0 * x0.numel()):
+            x = x0.clone()
+        pipeline.spts_layer(x, pos, w, cfg, k_given=kk, tm=tm)
+    record("long_layer_128k", layer128k, sh.n, {"tokens": sh.n, "probes": sh.P, "keep": cfg128k["keep_attn"],
+                                                 "needles": cfg128k["needles"], "keys": "clustered, given"})
+    del inp, xp, wq, kk, w, x0
 
     shp = W.LayerShape(n=cfg128k["prefix"], P=sh.P)
     inp = W.make_layer(shp, seed=cfg128k["seed"], needles=64, clustered_keys=(cfg128k["centroids"], cfg128k["sigma"]))
@@ -456,84 +517,133 @@ def hbm_table(x0, reps=5):
 
 # ------------------------------------------------------------ CPU baseline
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        return os.cpu_count()
+
+
+def _oracle_layer_sampled(x, pos, w, cfg, frac, rng):
+    """One oracle layer timed on the host as a CPU baseline (the oracle is
+    test infrastructure; it runs here only to be timed).  Every step that
+    needs all rows runs in full: pre-norm, K/V and probe-query projections,
+    PAP score, selections, LTP score over every row, fused score.  The steps
+    that are independent per selected row (Q projection + reduced attention +
+    O projection + residual add; SwiGLU + residual add) run on about a
+    fraction `frac` of the selected rows (attention: evenly spaced blocks of
+    256 consecutive rows) and are scaled by the ratio of rows.
+    Returns a dict of seconds: measured and estimated for the whole layer,
+    and the projection + probe part (which scales with the candidates)."""
+    import numpy as np
+    from oracle import numerics, normrope, pap, select, attention, ltp, ffn
+    from oracle.layer import project
+    Hq, Hkv, dh, P = cfg["Hq"], cfg["Hkv"], cfg["dh"], cfg["P"]
+    theta, prenorm, scale = cfg.get("theta"), cfg.get("prenorm", False), dh ** -0.5
+    t0 = time.perf_counter()
+    xt = numerics.bf16(normrope.rmsnorm(x)) if prenorm else x
+    K = project(xt, w["wk"], Hkv, dh, pos, theta)
+    V = project(xt, w["wv"], Hkv, dh)
+    Qp = project(xt[-P:], w["wq"], Hq, dh, pos[-P:], theta)
+    S = pap.pap_scores(Qp, K, scale)
+    t_kvp = time.perf_counter() - t0
+    n = x.shape[0]
+    k_a = numerics.keep_count(0.35, n)
+    idx = select.select_topk(numerics.f32(S), k_a, P)
+    t_full = time.perf_counter() - t0
+    # attention rows: evenly spaced blocks of 256 consecutive selected rows,
+    # each one chunk of the oracle's attention loop as in the whole run (a
+    # row's cost grows with its position, so the blocks' mean is the layer's)
+    nb = min(max(2, int(round(k_a * frac / 256))), (k_a + 255) // 256)
+    starts = np.unique(np.linspace(0, max(0, k_a - 256), nb).astype(np.int64))
+    blocks = [idx[b0:b0 + 256] for b0 in starts]
+    m = sum(len(b) for b in blocks)
+    y = x.copy()
+    t1 = time.perf_counter()
+    for qi in blocks:
+        Qs = project(xt[qi], w["wq"], Hq, dh, pos[qi], theta)
+        O = numerics.bf16(attention.reduced_attention(Qs, qi, K, V, scale))
+        y[qi] = numerics.bf16(x[qi] + numerics.bf16(O.reshape(len(qi), -1) @ w["wo"].T))
+    t_rows = (time.perf_counter() - t1) * k_a / m
+    t_meas = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    z = numerics.bf16(normrope.rmsnorm(y)) if prenorm else y
+    L = ltp.ltp_scores(z, w["u_t"], w["v_t"])
+    idx_f = select.select_topk(select.fuse_maxnorm(numerics.f32(S), numerics.f32(L)), k_a, P)
+    t_full += time.perf_counter() - t2
+    mf = max(1, int(round(k_a * frac)))
+    fi = idx_f[np.sort(rng.choice(k_a, mf, replace=False))]
+    t3 = time.perf_counter()
+    _, yv = ffn.swiglu_rows(z[fi], w["wg"], w["wu"], w["wd"])
+    _ = numerics.bf16(y[fi] + yv)
+    t_rows += (time.perf_counter() - t3) * k_a / mf
+    t_meas += t_full + time.perf_counter() - t3
+    return {"est": t_full + t_rows, "measured": t_meas, "kvp": t_kvp, "rows_sampled": m + mf, "rows": 2 * k_a}
+
+
 def cpu_baseline(sh, st, n_layers, points, frac):
     """The CPU oracle timed on a bounded sample of the stack workload.
 
-    For each MSDP stage (2 layers, c_s candidates) one oracle layer is run on
-    c_s rows of the inputs with that stage's first-layer weights: the steps
-    that need every row (norm, K/V projection, probe score, selections) run
-    in full; the row-separable steps (selected-query projection and
-    attention, O projection, LTP, SwiGLU) run on a fraction `frac` of their
-    rows and are scaled by 1/frac.  Stack time = 2 * sum over stages."""
+    Per MSDP stage (2 layers, c_s candidates) one oracle layer runs on c_s
+    rows with that stage's first-layer weights (_oracle_layer_sampled: steps
+    over all rows in full, per-row steps on a fraction of the selected rows,
+    scaled).  The stage's first layer also projects and probes the c_{s-1}
+    outgoing rows before its boundary, so the stage costs twice the layer
+    plus the projection + probe part scaled by c_{s-1}/c_s - 1."""
     import numpy as np
     import workloads as W
-    from oracle import numerics, normrope, pap, select, attention, ltp, ffn
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        cores = os.cpu_count()
-    P, Hq, Hkv, dh, d = sh.P, sh.Hq, sh.Hkv, sh.dh, sh.d
-    scale = dh ** -0.5
-    theta = 500000.0
+    cfg = dict(Hq=sh.Hq, Hkv=sh.Hkv, dh=sh.dh, P=sh.P, prenorm=True, theta=500000.0)
     rng = np.random.default_rng(0)
-    t_stack = 0.0
-    measured = 0.0
-    starts = sorted(points)
+    t_stack = measured = 0.0
     c_prev = sh.n
-    for si, layer_idx in enumerate(starts):
+    for si, layer_idx in enumerate(sorted(points)):
         c = points[layer_idx]
         w = {k: W.as_f64(v) for k, v in st["layers"][layer_idx].items()}
         x = W.as_f64(st["x"][:c])
-        pos = np.arange(c)
-        t_full = 0.0
-        t_rows = 0.0
-        t0 = time.perf_counter()
-        xt = numerics.bf16(normrope.rmsnorm(x))
-        K = numerics.bf16(normrope.rope(numerics.f32(xt @ w["wk"].T).reshape(c, Hkv, dh), pos, theta))
-        V = numerics.bf16(xt @ w["wv"].T).reshape(c, Hkv, dh)
-        Qp = numerics.bf16(normrope.rope(numerics.f32(xt[-P:] @ w["wq"].T).reshape(P, Hq, dh), pos[-P:], theta))
-        S = pap.pap_scores(Qp, K, scale)
-        t_kvp = time.perf_counter() - t0
-        k_a = numerics.keep_count(0.35, c)
-        idx = select.select_topk(numerics.f32(S), k_a, P)
-        t_full += time.perf_counter() - t0
-        m = max(1, int(round(k_a * frac)))
-        rows = np.sort(rng.choice(k_a, m, replace=False))
-        t0 = time.perf_counter()
-        qi = idx[rows]
-        Qs = numerics.bf16(normrope.rope(numerics.f32(xt[qi] @ w["wq"].T).reshape(m, Hq, dh), qi, theta))
-        O = numerics.bf16(attention.reduced_attention(Qs, qi, K, V, scale))
-        delta = numerics.bf16(O.reshape(m, -1) @ w["wo"].T)
-        _ = numerics.bf16(x[qi] + delta)
-        mz = max(1, int(round(c * frac)))
-        zr = np.sort(rng.choice(c, mz, replace=False))
-        z = numerics.bf16(normrope.rmsnorm(x[zr]))
-        _ = ltp.ltp_scores(z, w["u_t"], w["v_t"])
-        _, y = ffn.swiglu_rows(z[: min(mz, m)], w["wg"], w["wu"], w["wd"])
-        t_rows += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        L = np.abs(rng.standard_normal(c))                   # stands in for the full-row LTP score
-        _ = select.select_topk(select.fuse_maxnorm(numerics.f32(S), numerics.f32(L)), k_a, P)
-        t_full += time.perf_counter() - t0
-        # scale: attention/Q/O rows by k_a/m, LTP rows by c/mz, FFN rows by k_f/min(mz, m)
-        t_layer = t_full + t_rows / frac
-        measured += t_full + t_rows
-        # the stage's first layer projects and probes the outgoing c_prev rows
-        t_stack += 2 * t_layer + t_kvp * (c_prev / c - 1.0)
+        r = _oracle_layer_sampled(x, np.arange(c), w, cfg, frac, rng)
+        measured += r["measured"]
+        t_stack += 2 * r["est"] + r["kvp"] * (c_prev / c - 1.0)
         c_prev = c
-        log(f"cpu oracle stage {si}: {c} candidates, measured {t_full + t_rows:.1f}s, layer est {t_layer:.1f}s")
-    value = n_layers * sh.n / t_stack
-    return {"value": round(value, 1), "unit": "tokens/s/layer", "cores": int(cores), "kind": "oracle",
-            "sample": (f"one oracle layer per MSDP stage at its candidate count (19661/14746/11469/8192 of "
-                       f"32768 rows); full-row steps (RMSNorm, K/V projection, probe score, selections) in full, "
-                       f"row-separable steps (Q projection + reduced attention + O projection, LTP, SwiGLU) on "
-                       f"{frac:.4f} of their rows scaled by 1/{frac:.4f}; stack = 2 x sum over stages, the "
-                       f"first layer's K/V + probe scaled to the outgoing row count; "
+        log(f"cpu oracle stage {si}: {c} candidates, measured {r['measured']:.1f}s, layer est {r['est']:.1f}s")
+    cores = _blas_threads()
+    return {"value": round(n_layers * sh.n / t_stack, 1), "unit": "tokens/s/layer", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"the 8-layer 32K stack: one oracle layer per MSDP stage at its candidate count "
+                       f"(19661/14746/11469/8192 of 32768 rows); the steps over all rows (RMSNorm, K/V and "
+                       f"probe-query projections, PAP score, selections, LTP score, fused score) run in full, "
+                       f"the per-row steps (Q projection + reduced attention + O projection, SwiGLU) on about "
+                       f"{frac:.4f} of the selected rows (at least two 256-row blocks), scaled by the row ratio; "
+                       f"stack = 2 x each stage's "
+                       f"layer + the first layer's projections and probe over the outgoing rows; "
                        f"{measured:.1f}s measured on {cores} BLAS threads"),
-            "seconds_per_step_est": round(t_stack, 2),
+            "seconds_per_step_est": round(t_stack, 2), "seconds_measured": round(measured, 2),
             "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
             "numpy": np.__version__}
+
+
+def cpu_baseline_layer(x0, w0, n, frac, full=False):
+    """The CPU oracle on the single 32K layer (attention + FFN, PAP + LTP,
+    keep 0.35 / 0.35): the same sampling as the stack's, or (full=True) the
+    oracle's whole layer run unsampled."""
+    import numpy as np
+    import workloads as W
+    from oracle import layer as olayer
+    w = {k: W.as_f64(v) for k, v in w0.items()}
+    x = W.as_f64(x0)
+    cores = _blas_threads()
+    if full:
+        t0 = time.perf_counter()
+        olayer.spts_layer(x, np.arange(n), w, dict(Hq=32, Hkv=8, dh=128, P=64, keep_attn=0.35, keep_ffn=0.35))
+        sec = time.perf_counter() - t0
+        return {"value": round(n / sec, 1), "unit": "tokens/s/layer", "cores": int(cores), "kind": "oracle",
+                "sample": "the whole 32K layer, unsampled", "seconds_measured": round(sec, 2)}
+    r = _oracle_layer_sampled(x, np.arange(n), w, dict(Hq=32, Hkv=8, dh=128, P=64), frac,
+                              np.random.default_rng(1))
+    return {"value": round(n / r["est"], 1), "unit": "tokens/s/layer", "cores": int(cores), "kind": "oracle",
+            "sample": (f"the 32K layer: steps over all rows in full, per-row steps on {r['rows_sampled']} of "
+                       f"{r['rows']} selected rows, scaled; {r['measured']:.1f}s measured"),
+            "seconds_per_layer_est": round(r["est"], 2), "seconds_measured": round(r["measured"], 2)}
 
 
 # --------------------------------------------------------------------- main
@@ -622,7 +732,8 @@ def main():
         ms = total_ms / args.steps
         results[name] = dict(ms_per_step=ms, wall_ms_per_step=wall_ms / args.steps,
                              tokens_per_s_per_layer=nl * N / (ms * 1e-3),
-                             breakdown=breakdown(summ, args.steps), roofline=roofline(summ_dom, args.steps))
+                             breakdown=breakdown(summ, args.steps),
+                             roofline=roofline(summ_dom, args.steps, with_rocprof=(name == "msdp_stack_32k")))
         log(f"{name}: {ms:.3f} ms/step, {nl * N / (ms * 1e-3):,.0f} tokens/s/layer")
 
     head = results[args.workload]
@@ -671,6 +782,9 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(sh, st, n_layers, points, args.cpu_sample)
+        log("timing the CPU oracle on the single 32K layer" + (" (unsampled)" if args.cpu_full else ""))
+        rec.setdefault("also", {})["cpu_baseline_layer_32k"] = cpu_baseline_layer(
+            st["x"], st["layers"][0], N, args.cpu_sample, full=args.cpu_full)
     print(json.dumps(rec), flush=True)
 
 
