@@ -64,6 +64,9 @@ def parse():
                     help="fraction of row-separable oracle work timed for the CPU baseline")
     ap.add_argument("--cpu-full", action="store_true",
                     help="time the oracle's whole 32K layer unsampled (several minutes)")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="only run the PAP probe on the 32K-stack shape (64 probes, 32768 keys) and the 128K shape "
+                         "(128 probes, 131072 keys), 20 calls each, printing per-call times (for kernel profiles)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run spts_gather over 1 GiB with identity rows (a plain copy of known size, "
                          "to scale HBM byte counters) and exit")
@@ -662,6 +665,26 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fused = not args.unfused
+    if args.probe_only:
+        import workloads as W
+        out = {}
+        for n, P in ((32768, 64), (131072, 128)):
+            q = W.randn((P, 32, 128), seed=1, std=1.28).to(dev)
+            k = W.randn((n, 8, 128), seed=2, std=1.28).to(dev)
+            S = torch.empty(n, dtype=torch.float32, device=dev)
+            for _ in range(3):
+                capi.spts_probe_attention(q, k, scores=S)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(50_000_000)              # the GPU stays busy while the calls are enqueued
+            e0.record()
+            for _ in range(20):
+                capi.spts_probe_attention(q, k, scores=S)
+            e1.record()
+            torch.cuda.synchronize()
+            out[f"n{n}_p{P}_us"] = round(e0.elapsed_time(e1) / 20 * 1e3, 1)
+        print(json.dumps({"pap_probe": out}), flush=True)
+        return
     if args.calibrate_copy:
         rows, width = 131072, 4096                       # 1 GiB of bf16 read + 1 GiB written
         src = torch.ones((rows, width), dtype=torch.bfloat16, device=dev)
