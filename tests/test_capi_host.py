@@ -164,6 +164,8 @@ def test_attention_and_rows_validation(L, ctx):
     assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 10, 5, 32, 8, 128, 0.1, FAKE) == SHAPE   # kq > n
     assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 5, 10, 32, 8, 64, 0.1, FAKE) == UNSUPPORTED
     assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 0, 10, 32, 8, 128, 0.1, FAKE) == OK       # empty
+    # K/V of 2^31 elements or more (32-bit staging offsets): refused before any launch
+    assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 5, 1 << 21, 32, 8, 128, 0.1, FAKE) == UNSUPPORTED
     assert f(ctx, capi.I32, FAKE, FAKE, FAKE, FAKE, 5, 10, 32, 8, 128, 0.1, FAKE) == DTYPE
     assert L.spts_gather(ctx, 9, FAKE, FAKE, 4, 8, FAKE) == DTYPE
     assert L.spts_gather(ctx, capi.BF16, FAKE, FAKE, 0, 8, FAKE) == OK
