@@ -8,10 +8,10 @@
 // Tiling: 256 x 256 x 64 per workgroup, 8 waves in a 4 (M) x 2 (N) grid, each
 // wave owns a 64 x 128 block = 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (128
 // fp32 accumulators per lane), two waves per SIMD.  Operands go straight from
-// global memory into double-buffered LDS (2 x 64 KiB), one barrier per
-// k-step.  Only waves 0-3 (one per SIMD) issue the global->LDS loads: a wave
-// stalled on issuing them cannot issue MFMAs, so each SIMD keeps one wave
-// that only computes.
+// global memory into LDS, A and B each in two 32 KiB slots, copied by all 8
+// waves.  Two barriers per k-step release the A slot and the B slot at
+// different points, so the next steps' copies stay in flight across every
+// barrier (see the pipeline comment in the kernel).
 //
 // The MFMA is issued as (B fragment, A fragment) so each lane's accumulators
 // hold ONE row of C and 4 groups of 4 consecutive columns; every epilogue
@@ -226,23 +226,20 @@ void gemm_tn_kernel(GemmArgs g) {
     // KV: tiles at or past column n0 read b1 and write out2
     const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
 
-    // ---- direct global -> LDS staging by waves 0-3.  Loading wave w,
-    // instruction i writes the 1 KiB block of tile rows rb*8 .. rb*8+7,
-    // rb = 4*i + w; lane L lands at row r = rb*8 + L/8, physical chunk L%8, so
-    // it fetches the logical chunk (L%8) ^ ((r >> 1) & 7) -- the swizzle of
-    // swz() applied on the global side.
-    const bool loader = wave < 4;
-    const int lw = wave & 3;
+    // ---- direct global -> LDS staging by all 8 waves.  Wave w, instruction
+    // i (0..3) of an operand writes the 1 KiB block of tile rows rb*8 ..
+    // rb*8+7, rb = 8*i + w; lane L lands at row r = rb*8 + L/8, physical chunk
+    // L%8, so it fetches the logical chunk (L%8) ^ ((r >> 1) & 7) -- the
+    // swizzle of swz() applied on the global side.
     const int ld_sub = lane >> 3;                       // row within the 8-row block
     // byte offsets of the staged rows: A rows in 64 bits (a gathered source
     // can span more than 4 GiB), B rows in 32 bits (the host rejects weights
     // of 4 GiB or more)
-    uint64_t a_off[8];
-    uint32_t b_off[8];
-    unsigned b_from_up = 0;                             // SWIGLU: instruction i reads Wu
+    uint64_t a_off[4];
+    uint32_t b_off[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rb = 4 * i + lw;
+    for (int i = 0; i < 4; ++i) {
+      const int rb = 8 * i + wave;
       const int r = rb * 8 + ld_sub;                    // row within the 256-row tile
       const int ld_ch = (lane & 7) ^ ((r >> 1) & 7);    // logical 16-byte chunk fetched
       int ar = tile_m * BM + r;
@@ -250,10 +247,11 @@ void gemm_tn_kernel(GemmArgs g) {
       if (GATHER) ar = g.a_rows[ar];
       a_off[i] = ((uint64_t)(uint32_t)ar * (uint32_t)g.lda + ld_ch * 8) * 2u;
       if (kSwiglu) {
-        // wave column block r / 128: rows 0..63 gate, 64..127 up, same 64 outputs
+        // wave column block r / 128: rows 0..63 gate, 64..127 up, same 64
+        // outputs; block rb = 8*i + w covers rows 64..127 of its 128-row block
+        // exactly when i is odd, so odd instructions read Wu
         const int within = r & 127;
         const uint32_t brow = (uint32_t)tile_n * 128 + (r >> 7) * 64 + (within & 63);
-        if (within >= 64) b_from_up |= 1u << i;
         b_off[i] = (brow * (uint32_t)g.ldb + ld_ch * 8) * 2u;
       } else {
         const uint32_t brow = (uint32_t)(tile_n * BN - (part1 ? g.n0 : 0)) + r;
@@ -266,24 +264,42 @@ void gemm_tn_kernel(GemmArgs g) {
     const int KT = k1 - k0;                              // k-steps of this job
     const int kt_base = k0;
 
-    auto issue = [&](int kt_local, int stage) {
-      if (!loader) return;
-      const int kt = kt_base + kt_local;
+    // The operands of k-step s go to slots As[s & 1] and Bs[s & 1]; s past
+    // the job's last step reloads that step (never read), so every wave
+    // issues the same loads and addresses stay in bounds.
+    auto issue_a = [&](int s) {
+      const int kt = kt_base + (s < KT ? s : KT - 1);
       const uint32_t ka = (uint32_t)kt * BK * 2u;
-      const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
-      uint16_t* a_s = As + stage * TILE_ELEMS;
-      uint16_t* b_s = Bs + stage * TILE_ELEMS;
+      uint16_t* a_s = As + (s & 1) * TILE_ELEMS;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rb = 4 * i + lw;
+      for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(abase + a_off[i] + ka),
-            (__attribute__((address_space(3))) void*)(a_s + rb * 512), 16, 0, 0);
-        const char* bb = (kSwiglu && ((b_from_up >> i) & 1u)) ? b1base : b0base;
+            (__attribute__((address_space(3))) void*)(a_s + (8 * i + wave) * 512), 16, 0, 0);
+    };
+    auto issue_b = [&](int s) {
+      const int kt = kt_base + (s < KT ? s : KT - 1);
+      const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
+      uint16_t* b_s = Bs + (s & 1) * TILE_ELEMS;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* bb = (kSwiglu && (i & 1)) ? b1base : b0base;
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)(bb + b_off[i] + kb),
-            (__attribute__((address_space(3))) void*)(b_s + rb * 512), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(b_s + (8 * i + wave) * 512), 16, 0, 0);
       }
+    };
+    auto read_a = [&](bf16x8 (&f)[2], int s, int kk) {
+      const uint16_t* a_s = As + (s & 1) * TILE_ELEMS;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        f[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 64 + i * 32 + l32, kk * 2 + half));
+    };
+    auto read_b = [&](bf16x8 (&f)[4], int s, int kk) {
+      const uint16_t* b_s = Bs + (s & 1) * TILE_ELEMS;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, kk * 2 + half));
     };
 
     f32x16 acc[2][4];
@@ -293,36 +309,93 @@ void gemm_tn_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mma = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[4]) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fb[j], fa[i], acc[i][j]);
+    };
 
-    // k-step kt reads stage kt & 1 while the loads of k-step kt+1 fill the
-    // other stage; the wait + barrier at its end hands both stages over.
-    issue(0, 0);
+    // Pipeline.  A k-step is four 16-deep substeps kk.  A step's A fragments
+    // are all read by the end of its substep 0 and its B fragments by the end
+    // of substep 2, so two barriers per step free the slots at different
+    // times: after barrier M(t) (substep 1 done) the A slot of step t takes
+    // step t+2; after barrier E(t) (substep 2 done, step t+1 landed) the B
+    // slot of step t takes step t+2 in the next step's substep 0.  E waits
+    // only for step t+1's copies, so step t+2's A copies stay in flight
+    // across it and the load pipeline never drains.
+    bf16x8 fa[4][2], fb0[4], fb1[4];
+    issue_a(0);
+    issue_b(0);
+    issue_a(1);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 4);   // vmcnt(4): step 0 landed, A of step 1 in flight
+    __syncthreads();
+    read_a(fa[0], 0, 0);
+    read_a(fa[1], 0, 1);
+    read_b(fb0, 0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      // substep 0: B kk1, A kk2-3 of this step; B of step kt+1 into its slot
+      read_b(fb1, kt, 1);
+      read_a(fa[2], kt, 2);
+      read_a(fa[3], kt, 3);
+      issue_b(kt + 1);
+      mma(fa[0], fb0);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);     // the four copies
+      __builtin_amdgcn_sched_barrier(0);
+      // substep 1: B kk2
+      read_b(fb0, kt, 2);
+      mma(fa[1], fb1);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // M(kt): every A read of step kt is done
+      __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);   // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // substep 2: B kk3; A of step kt+2 into the A slot of step kt
+      read_b(fb1, kt, 3);
+      issue_a(kt + 2);
+      mma(fa[2], fb0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // E(kt): every read of step kt is done; step kt+1 has landed (only the
+      // four A copies of step kt+2 may still be in flight)
+      __builtin_amdgcn_s_waitcnt(0x0070 | 4);   // vmcnt(4) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // substep 3 from registers; A kk0-1 and B kk0 of step kt+1
+      read_a(fa[0], kt + 1, 0);
+      read_a(fa[1], kt + 1, 1);
+      read_b(fb0, kt + 1, 0);
+      mma(fa[3], fb1);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // no copy into LDS outlives the k-loop, and no wave still reads it
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      // the last k-step reloads its own tile into the idle stage (never read)
-      issue(kt + 1 < KT ? kt + 1 : kt, cur ^ 1);
-      const uint16_t* a_s = As + cur * TILE_ELEMS;
-      const uint16_t* b_s = Bs + cur * TILE_ELEMS;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int ch = kk * 2 + half;
-        bf16x8 af[2], bfm[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 64 + i * 32 + l32, ch));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfm[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, ch));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bfm[j], af[i], acc[i][j]);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
 
     if (kTail && slot >= 0) {
       float* ps = piece_base(g, slot, tid);
