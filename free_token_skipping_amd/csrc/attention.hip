@@ -126,26 +126,28 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   const uint16_t* kbase = k + g * DH + (tid & 15) * 8;
   const int kp = tid & 31, dc = tid >> 5;            // V: key pair, dh chunk
   const uint16_t* vbase = v + g * DH + dc * 8;
-  u32x4 kr[2], vr[2];
-  auto load_k = [&](int j0) {
+  // two register sets: a step stores the tiles loaded one step earlier and
+  // loads the next ones, so every load has two steps to land
+  u32x4 kra[2], vra[2], krb[2], vrb[2];
+  auto load_k = [&](u32x4 (&kr)[2], int j0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = min(j0 + (tid >> 4) + 32 * i, n - 1);
       kr[i] = ld16(kbase + j * row_stride);
     }
   };
-  auto load_v = [&](int j0) {
+  auto load_v = [&](u32x4 (&vr)[2], int j0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int j = min(j0 + 2 * kp + e, n - 1);
       vr[e] = ld16(vbase + j * row_stride);
     }
   };
-  auto store_k = [&](int buf) {
+  auto store_k = [&](const u32x4 (&kr)[2], int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) st16(Ks[buf] + ((tid >> 4) + 32 * i) * KROW + (tid & 15) * 8, kr[i]);
   };
-  auto store_v = [&](int buf) {
+  auto store_v = [&](const u32x4 (&vr)[2], int buf) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1;
@@ -234,16 +236,17 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   // set), pp the P of tile t-1.  The matrix core forms the logits of tile t+1
   // and O += P_{t-1} V_{t-1} while the VALU turns tile t's logits into P_t, so
   // all three streams are independent and interleave one MFMA at a time.  V
-  // trails K by two tiles: V_t is staged during step t (into buffer t & 1)
-  // and read at step t+1, K_{t+2} is staged during step t.
+  // trails K by two tiles: step t stores V_t and K_{t+2} (into buffer t & 1)
+  // from the registers kc / vc loaded during step t-1, and loads V_{t+1} and
+  // K_{t+3} into kn / vn; V_t is read at step t+1.
   auto step = [&](auto with_pv, int t, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pp)[4],
-                  bf16x8 (&pc)[4]) {
+                  bf16x8 (&pc)[4], u32x4 (&kc)[2], u32x4 (&vc)[2], u32x4 (&kn)[2], u32x4 (&vn)[2]) {
     constexpr bool kPV = decltype(with_pv)::value;
     // K/V staging is unconditional (rows clamp to n-1; past the last tile the
     // K store lands in buffer t & 1, whose tile was read in step t-1), so no
     // branch splits the MFMA / VALU block
-    load_k((t + 2) * KT);
-    load_v(t * KT);
+    load_k(kn, (t + 3) * KT);
+    load_v(vn, (t + 1) * KT);
     logits((t + 1) & 1, sn);             // stale data past the last tile; unused
     if constexpr (kPV) pv_mma((t - 1) & 1, pp);
     softmax(sc, pc);
@@ -276,19 +279,22 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     // P_t is only read in the next step; without this anchor the compiler
     // sinks the softmax below the masking of tile t+1, away from the MFMAs
     asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(pc[2]), "+v"(pc[3]), "+v"(l_part));
-    store_k(t & 1);
-    store_v(t & 1);
+    store_k(kc, t & 1);
+    store_v(vc, t & 1);
     if (t + 1 < ntiles) prepare(t + 1, sn, pc);
     __syncthreads();
   };
 
-  // prologue: K_0, K_1 staged; logits of tile 0
-  load_k(0);
-  store_k(0);
+  // prologue: K_0, K_1 staged; K_2 and V_0 in registers (set a) for step 0
+  // to store; logits of tile 0
+  load_k(kra, 0);
+  store_k(kra, 0);
   if (ntiles > 1) {
-    load_k(KT);
-    store_k(1);
+    load_k(kra, KT);
+    store_k(kra, 1);
   }
+  load_k(kra, 2 * KT);
+  load_v(vra, 0);
   __syncthreads();
   f32x16 sa[2], sb[2];
   bf16x8 pa[4], pb[4];
@@ -301,13 +307,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   prepare(0, sa, pb);                     // nothing pending yet (pb is zero)
   // step 0 stages K_2 into Ks[0]: every wave must have read K_0 from it first
   __syncthreads();
-  step(std::false_type{}, 0, sa, sb, pb, pa);
+  step(std::false_type{}, 0, sa, sb, pb, pa, kra, vra, krb, vrb);
   int t = 1;
   for (; t + 1 < ntiles; t += 2) {
-    step(std::true_type{}, t, sb, sa, pa, pb);
-    step(std::true_type{}, t + 1, sa, sb, pb, pa);
+    step(std::true_type{}, t, sb, sa, pa, pb, krb, vrb, kra, vra);
+    step(std::true_type{}, t + 1, sa, sb, pb, pa, kra, vra, krb, vrb);
   }
-  if (t < ntiles) step(std::true_type{}, t, sb, sa, pa, pb);
+  if (t < ntiles) step(std::true_type{}, t, sb, sa, pa, pb, krb, vrb, kra, vra);
   // the last tile's P: step t leaves P_t in pb for odd t, in pa for even t
   if ((ntiles - 1) & 1) pv_mma((ntiles - 1) & 1, pb);
   else pv_mma((ntiles - 1) & 1, pa);
