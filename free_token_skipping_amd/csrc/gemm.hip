@@ -6,16 +6,18 @@
 // each MFMA fragment as one 16-byte LDS load.
 //
 // Tiling: 256 x 256 x 64 per workgroup, 8 waves in a 4 (M) x 2 (N) grid, each
-// wave owns a 64 x 128 block = 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (128
-// fp32 accumulators per lane), two waves per SIMD.  Operands go straight from
+// wave owns a 64 x 128 block = 4 x 8 tiles of v_mfma_f32_16x16x32_bf16 (128
+// fp32 accumulators per lane), two waves per SIMD.  On gfx950 the 16x16x32
+// form kept the matrix cores busier than 32x32x16 with the same data flow.  Operands go straight from
 // global memory into LDS, A and B each in two 32 KiB slots, copied by all 8
 // waves.  Two barriers per k-step release the A slot and the B slot at
 // different points, so the next steps' copies stay in flight across every
 // barrier (see the pipeline comment in the kernel).
 //
 // The MFMA is issued as (B fragment, A fragment) so each lane's accumulators
-// hold ONE row of C and 4 groups of 4 consecutive columns; every epilogue
-// (row scatter, RoPE pairs, SwiGLU pairs, row norms) is then lane-local.
+// hold, per 16-row tile, ONE row of C and 4 consecutive columns of each
+// 16-column tile; every epilogue (row scatter, RoPE pairs, SwiGLU pairs, row
+// norms) is then lane-local.
 #include <atomic>
 #include <cmath>
 
@@ -39,77 +41,75 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 // Epilogue of one finished 256 x 256 tile (STORE, ROPE, KV, SWIGLU,
 // SWIGLU_SPLIT, SPLIT).  Lane holds C[row][col] for row = tile_m*BM + wm*64 +
-// i*32 + l32 and col = (tile base) + wn*128 + j*32 + q*8 + half*4 + e, with
-// accumulator register r = q*4 + e.
+// i*16 + r16 and col = (tile base) + wn*128 + j*16 + q4*4 + e (i < 4, j < 8,
+// e < 4).  The wave's 128 columns are one RoPE head (column c pairs with
+// c + 64: tile j with tile j + 4) or, for SwiGLU, 64 gate rows then the 64 up
+// rows of the same outputs (again tile j with tile j + 4).
 template <int EPI, bool GATHER>
-__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16 (&acc)[2][4], int tile_m, int tile_n,
-                                           bool part1, int wm, int wn, int l32, int half) {
+__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x4 (&acc)[4][8], int tile_m, int tile_n,
+                                           bool part1, int wm, int wn, int r16, int q4) {
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = tile_m * BM + wm * 64 + i * 32 + l32;
+  for (int i = 0; i < 4; ++i) {
+    const int row = tile_m * BM + wm * 64 + i * 16 + r16;
     if (row >= g.m) continue;
     if (kSwiglu) {
       uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)row * g.ldc;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j) {
+        float hv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float hv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float gt = acc[i][j][q * 4 + e];
-            const float up = acc[i][j + 2][q * 4 + e];
-            hv[e] = (gt / (1.0f + __expf(-gt))) * up;
-          }
-          const int col = tile_n * 128 + wn * 64 + j * 32 + q * 8 + half * 4;
-          u32x2 w;
-          w[0] = pack2bf(hv[0], hv[1]);
-          w[1] = pack2bf(hv[2], hv[3]);
-          *reinterpret_cast<u32x2*>(out + col) = w;
-          if (EPI == EPI_SWIGLU_SPLIT) {
-            u32x2 wl;
-            wl[0] = pack2bf(hv[0] - lo_bf(w[0]), hv[1] - hi_bf(w[0]));
-            wl[1] = pack2bf(hv[2] - lo_bf(w[1]), hv[3] - hi_bf(w[1]));
-            *reinterpret_cast<u32x2*>(out + g.n / 2 + col) = wl;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float gt = acc[i][j][e];
+          const float up = acc[i][j + 4][e];
+          hv[e] = (gt / (1.0f + __expf(-gt))) * up;
         }
+        const int col = tile_n * 128 + wn * 64 + j * 16 + q4 * 4;
+        u32x2 w;
+        w[0] = pack2bf(hv[0], hv[1]);
+        w[1] = pack2bf(hv[2], hv[3]);
+        *reinterpret_cast<u32x2*>(out + col) = w;
+        if (EPI == EPI_SWIGLU_SPLIT) {
+          u32x2 wl;
+          wl[0] = pack2bf(hv[0] - lo_bf(w[0]), hv[1] - hi_bf(w[0]));
+          wl[1] = pack2bf(hv[2] - lo_bf(w[1]), hv[3] - hi_bf(w[1]));
+          *reinterpret_cast<u32x2*>(out + g.n / 2 + col) = wl;
+        }
+      }
       continue;
     }
     if (EPI == EPI_SPLIT) {
       uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)row * g.ldc;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j) {
+        float hi[4], lo[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float hi[4], lo[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float t = acc[i][j][q * 4 + e];
-            hi[e] = bf2f(f2bf(t));
-            lo[e] = t - hi[e];
-          }
-          const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4;
-          u32x2 wh, wl;
-          wh[0] = pack2bf(hi[0], hi[1]); wh[1] = pack2bf(hi[2], hi[3]);
-          wl[0] = pack2bf(lo[0], lo[1]); wl[1] = pack2bf(lo[2], lo[3]);
-          *reinterpret_cast<u32x2*>(out + col) = wh;
-          *reinterpret_cast<u32x2*>(out + g.n + col) = wl;
+        for (int e = 0; e < 4; ++e) {
+          const float t = acc[i][j][e];
+          hi[e] = bf2f(f2bf(t));
+          lo[e] = t - hi[e];
         }
+        const int col = tile_n * BN + wn * 128 + j * 16 + q4 * 4;
+        u32x2 wh, wl;
+        wh[0] = pack2bf(hi[0], hi[1]); wh[1] = pack2bf(hi[2], hi[3]);
+        wl[0] = pack2bf(lo[0], lo[1]); wl[1] = pack2bf(lo[2], lo[3]);
+        *reinterpret_cast<u32x2*>(out + col) = wh;
+        *reinterpret_cast<u32x2*>(out + g.n + col) = wl;
+      }
       continue;
     }
     if (EPI == EPI_ROPE || (EPI == EPI_KV && !part1 && g.rope_table)) {
       const int arow = GATHER ? g.a_rows[row] : row;
       const float* tab = g.rope_table + (long)g.pos[arow] * 128;   // 64 (cos, sin) pairs
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = j * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+        for (int e = 0; e < 4; ++e) {
+          const int c = j * 16 + q4 * 4 + e;
           const float cs = tab[2 * c], sn = tab[2 * c + 1];
-          const float x1 = acc[i][j][r], x2 = acc[i][j + 2][r];
-          acc[i][j][r] = x1 * cs - x2 * sn;
-          acc[i][j + 2][r] = x2 * cs + x1 * sn;
+          const float x1 = acc[i][j][e], x2 = acc[i][j + 4][e];
+          acc[i][j][e] = x1 * cs - x2 * sn;
+          acc[i][j + 4][e] = x2 * cs + x1 * sn;
         }
     }
     // EPI_STORE / EPI_ROPE / EPI_KV
@@ -118,25 +118,21 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16 (&acc)[2][4
                           : reinterpret_cast<uint16_t*>(g.out) + (long)orow * g.ldc;
     const int cshift = part1 ? g.n0 : 0;                  // KV: b1 columns restart at 0
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4 - cshift;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
-        u32x2 w;
-        if (g.accumulate) {
-          const u32x2 old = *reinterpret_cast<const u32x2*>(out + col);
-          // the projection result is rounded to bf16 before the residual add
-          w[0] = pack2bf(lo_bf(old[0]) + bf2f(f2bf(v[0])), hi_bf(old[0]) + bf2f(f2bf(v[1])));
-          w[1] = pack2bf(lo_bf(old[1]) + bf2f(f2bf(v[2])), hi_bf(old[1]) + bf2f(f2bf(v[3])));
-        } else {
-          w[0] = pack2bf(v[0], v[1]);
-          w[1] = pack2bf(v[2], v[3]);
-        }
-        *reinterpret_cast<u32x2*>(out + col) = w;
+    for (int j = 0; j < 8; ++j) {
+      const int col = tile_n * BN + wn * 128 + j * 16 + q4 * 4 - cshift;
+      const f32x4 v = acc[i][j];
+      u32x2 w;
+      if (g.accumulate) {
+        const u32x2 old = *reinterpret_cast<const u32x2*>(out + col);
+        // the projection result is rounded to bf16 before the residual add
+        w[0] = pack2bf(lo_bf(old[0]) + bf2f(f2bf(v[0])), hi_bf(old[0]) + bf2f(f2bf(v[1])));
+        w[1] = pack2bf(lo_bf(old[1]) + bf2f(f2bf(v[2])), hi_bf(old[1]) + bf2f(f2bf(v[3])));
+      } else {
+        w[0] = pack2bf(v[0], v[1]);
+        w[1] = pack2bf(v[2], v[3]);
       }
+      *reinterpret_cast<u32x2*>(out + col) = w;
+    }
   }
 }
 
@@ -152,11 +148,15 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, i
 }
 
 // One fp32 tail piece of a tile, in the lanes' own register order: 32 groups
-// of 16 bytes per thread, group-major, so each store covers 8 KiB contiguously.
+// of 16 bytes per thread (accumulator tile (i, j)), group-major, so each store
+// covers 8 KiB contiguously.
 __device__ __forceinline__ float* piece_base(const GemmArgs& g, int slot, int tid) {
   return g.partial + (size_t)slot * (BM * BN) + tid * 4;
 }
-__device__ __forceinline__ int piece_group(int i, int j, int q) { return ((i * 4 + j) * 4 + q) * (NTHREADS * 4); }
+__device__ __forceinline__ int piece_group(int i, int j) { return (i * 8 + j) * (NTHREADS * 4); }
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 template <int EPI, bool GATHER>
 __global__ __launch_bounds__(NTHREADS, 1)
@@ -169,7 +169,7 @@ void gemm_tn_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS addresses in SGPRs
   const int wm = wave >> 1, wn = wave & 1;          // 4 x 2 waves
-  const int l32 = lane & 31, half = lane >> 5;
+  const int r16 = lane & 15, q4 = lane >> 4;   // fragment row, 8-element k group
 
   // ---- work of this workgroup.  Workgroups are dealt round-robin to the 8
   // XCDs, so workgroup b runs on XCD b % 8.  Each XCD gets a contiguous run of
@@ -289,108 +289,106 @@ void gemm_tn_kernel(GemmArgs g) {
             (__attribute__((address_space(3))) void*)(b_s + (8 * i + wave) * 512), 16, 0, 0);
       }
     };
-    auto read_a = [&](bf16x8 (&f)[2], int s, int kk) {
+    // fragments of 16 rows x 32 k (lane: row r16, elements 8*q4 .. 8*q4+7 of
+    // the 32) for substep kk2 (k 32*kk2 .. 32*kk2+31 of the step)
+    auto read_a = [&](bf16x8 (&f)[4], int s, int kk2) {
       const uint16_t* a_s = As + (s & 1) * TILE_ELEMS;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        f[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 64 + i * 32 + l32, kk * 2 + half));
+      for (int i = 0; i < 4; ++i)
+        f[i] = *reinterpret_cast<const bf16x8*>(a_s + swz(wm * 64 + i * 16 + r16, kk2 * 4 + q4));
     };
-    auto read_b = [&](bf16x8 (&f)[4], int s, int kk) {
+    auto read_b = [&](bf16x8 (&f)[8], int s, int kk2) {
       const uint16_t* b_s = Bs + (s & 1) * TILE_ELEMS;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        f[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 32 + l32, kk * 2 + half));
+      for (int j = 0; j < 8; ++j)
+        f[j] = *reinterpret_cast<const bf16x8*>(b_s + swz(wn * 128 + j * 16 + r16, kk2 * 4 + q4));
     };
 
-    f32x16 acc[2][4];
+    f32x4 acc[4][8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    auto mma = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[4]) {
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+    // the MFMAs of column tiles j0 .. j0+3
+    auto mma = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[8], int j0) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fb[j], fa[i], acc[i][j]);
+        for (int j = j0; j < j0 + 4; ++j) acc[i][j] = mfma16x16x32(fb[j], fa[i], acc[i][j]);
     };
 
-    // Pipeline.  A k-step is four 16-deep substeps kk.  A step's A fragments
-    // are all read by the end of its substep 0 and its B fragments by the end
-    // of substep 2, so two barriers per step free the slots at different
-    // times: after barrier M(t) (substep 1 done) the A slot of step t takes
-    // step t+2; after barrier E(t) (substep 2 done, step t+1 landed) the B
-    // slot of step t takes step t+2 in the next step's substep 0.  E waits
-    // only for step t+1's copies, so step t+2's A copies stay in flight
-    // across it and the load pipeline never drains.
-    bf16x8 fa[4][2], fb0[4], fb1[4];
+    // Pipeline.  A k-step is two 32-deep substeps, each issued as two phases
+    // of 16 MFMAs (column tiles 0-3, then 4-7).  A step's A fragments are all
+    // read by the end of its phase 1 and its B fragments by the end of phase
+    // 0, so two barriers per step free the slots at different times: after
+    // barrier M(t) (phase 1 done) the A slot of step t takes step t+2; after
+    // barrier E(t) (phase 2 done, step t+1 landed) the B slot of step t takes
+    // step t+2.  E waits only for step t+1's copies, so step t+2's A copies
+    // stay in flight across it and the load pipeline never drains.
+    bf16x8 fa0[4], fa1[4], fb0[8], fb1[8];
     issue_a(0);
     issue_b(0);
     issue_a(1);
-    __builtin_amdgcn_s_waitcnt(0x0070 | 4);   // vmcnt(4): step 0 landed, A of step 1 in flight
+    issue_b(1);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 8);   // vmcnt(8): step 0 landed, step 1 in flight
     __syncthreads();
-    read_a(fa[0], 0, 0);
-    read_a(fa[1], 0, 1);
+    read_a(fa0, 0, 0);
     read_b(fb0, 0, 0);
     for (int kt = 0; kt < KT; ++kt) {
-      // substep 0: B kk1, A kk2-3 of this step; B of step kt+1 into its slot
+      // phase 0: substep 0, columns 0-3; B of substep 1
       read_b(fb1, kt, 1);
-      read_a(fa[2], kt, 2);
-      read_a(fa[3], kt, 3);
-      issue_b(kt + 1);
-      mma(fa[0], fb0);
+      mma(fa0, fb0, 0);
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);     // the four copies
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
-      // substep 1: B kk2
-      read_b(fb0, kt, 2);
-      mma(fa[1], fb1);
+      // phase 1: substep 0, columns 4-7; A of substep 1
+      read_a(fa1, kt, 1);
+      mma(fa0, fb0, 4);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       __builtin_amdgcn_sched_barrier(0);
       // M(kt): every A read of step kt is done
       __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);   // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // substep 2: B kk3; A of step kt+2 into the A slot of step kt
-      read_b(fb1, kt, 3);
+      // phase 2: substep 1, columns 0-3; A of step kt+2 into the A slot of step kt
       issue_a(kt + 2);
-      mma(fa[2], fb0);
+      mma(fa1, fb1, 0);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one copy
       }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       __builtin_amdgcn_sched_barrier(0);
       // E(kt): every read of step kt is done; step kt+1 has landed (only the
       // four A copies of step kt+2 may still be in flight)
       __builtin_amdgcn_s_waitcnt(0x0070 | 4);   // vmcnt(4) lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // substep 3 from registers; A kk0-1 and B kk0 of step kt+1
-      read_a(fa[0], kt + 1, 0);
-      read_a(fa[1], kt + 1, 1);
+      // phase 3: substep 1, columns 4-7; substep 0 of step kt+1; B of step
+      // kt+2 into the B slot of step kt
+      read_a(fa0, kt + 1, 0);
       read_b(fb0, kt + 1, 0);
-      mma(fa[3], fb1);
+      issue_b(kt + 2);
+      mma(fa1, fb1, 4);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < 12; ++p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // no copy into LDS outlives the k-loop, and no wave still reads it
@@ -400,16 +398,9 @@ void gemm_tn_kernel(GemmArgs g) {
     if (kTail && slot >= 0) {
       float* ps = piece_base(g, slot, tid);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
-            *reinterpret_cast<f32x4*>(ps + piece_group(i, j, q)) = v;
-          }
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4*>(ps + piece_group(i, j)) = acc[i][j];
       if (step == 0) return;
       logical += step;
       slot += step;
@@ -418,58 +409,54 @@ void gemm_tn_kernel(GemmArgs g) {
     }
 
     // ------------------------------------------------------------ epilogues
-    // lane holds C[row][col] for row = tile_m*BM + wm*64 + i*32 + l32 and
-    // col = (tile base) + wn*128 + j*32 + q*8 + half*4 + e, r = q*4 + e.
+    // lane holds C[row][col] for row = tile_m*BM + wm*64 + i*16 + r16 and
+    // col = (tile base) + wn*128 + j*16 + q4*4 + e.
     if (EPI == EPI_PARTIAL) {
       float* part = g.partial + (long)kslice * g.m * g.n;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = tile_m * BM + wm * 64 + i * 32 + l32;
+      for (int i = 0; i < 4; ++i) {
+        const int row = tile_m * BM + wm * 64 + i * 16 + r16;
         if (row >= g.m) continue;
         float* prow = part + (long)row * g.n;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = tile_n * BN + wn * 128 + j * 32 + q * 8 + half * 4;
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][q * 4 + e];
-            *reinterpret_cast<f32x4*>(prow + col) = v;
-          }
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<f32x4*>(prow + tile_n * BN + wn * 128 + j * 16 + q4 * 4) = acc[i][j];
       }
       return;
     }
     if (EPI == EPI_SUMSQ) {
-      float* red = reinterpret_cast<float*>(smem);   // [4 wm][2 i][32 rows] from wn == 1
-      float ss[2];
+      // row sums of squares over the tile's 256 columns: a lane's 32 columns,
+      // then the 4 lanes of the row (q4), then the two column waves (LDS)
+      float* red = reinterpret_cast<float*>(smem);   // [4 wm][4 i][16 rows] from wn == 1
+      float ss[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         float t = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t += acc[i][j][r] * acc[i][j][r];
+          for (int e = 0; e < 4; ++e) t += acc[i][j][e] * acc[i][j][e];
+        t += __shfl_xor(t, 16);
         t += __shfl_xor(t, 32);
         ss[i] = t;
       }
-      if (wn == 1 && half == 0) {
+      if (wn == 1 && q4 == 0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) red[(wm * 2 + i) * 32 + l32] = ss[i];
+        for (int i = 0; i < 4; ++i) red[(wm * 4 + i) * 16 + r16] = ss[i];
       }
       __syncthreads();
-      if (wn == 0 && half == 0) {
+      if (wn == 0 && q4 == 0) {
         float* out = reinterpret_cast<float*>(g.out);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = tile_m * BM + wm * 64 + i * 32 + l32;
-          if (row < g.m) out[(long)row * tiles_n + tile_n] = ss[i] + red[(wm * 2 + i) * 32 + l32];
+        for (int i = 0; i < 4; ++i) {
+          const int row = tile_m * BM + wm * 64 + i * 16 + r16;
+          if (row < g.m) out[(long)row * tiles_n + tile_n] = ss[i] + red[(wm * 4 + i) * 16 + r16];
         }
       }
       return;
     }
 
-    store_tile<EPI, GATHER>(g, acc, tile_m, tile_n, part1, wm, wn, l32, half);
+    store_tile<EPI, GATHER>(g, acc, tile_m, tile_n, part1, wm, wn, r16, q4);
     return;
   }
 }
@@ -482,7 +469,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_fixup_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, half = lane >> 5;
+  const int r16 = lane & 15, q4 = lane >> 4;   // fragment row, 8-element k group
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU);
   const int tiles_m = (g.m + BM - 1) / BM;
   const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
@@ -490,27 +477,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tail_fixup_kernel(GemmArgs g) {
   int tile_m, tile_n;
   tile_of(g.tail_full + tt, tiles_m, tiles_n, tile_m, tile_n);
   const bool part1 = (EPI == EPI_KV) && tile_n * BN >= g.n0;
-  f32x16 acc[2][4];
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
   for (int p = 0; p < g.tail_np; ++p) {
     const float* ps = piece_base(g, p * g.tail_tiles + tt, tid);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ps + piece_group(i, j, q));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][q * 4 + e] += v[e];
-        }
+      for (int j = 0; j < 8; ++j) acc[i][j] += *reinterpret_cast<const f32x4*>(ps + piece_group(i, j));
   }
-  store_tile<EPI, GATHER>(g, acc, tile_m, tile_n, part1, wm, wn, l32, half);
+  store_tile<EPI, GATHER>(g, acc, tile_m, tile_n, part1, wm, wn, r16, q4);
 }
 
 // Split-K finish: sum the fp32 slices in slice order and apply the epilogue.
