@@ -224,9 +224,21 @@ def test_msdp_stack_small():
 
 
 def _compare_final_rows(x, final, ref, pos_ref, traces, hist, min_frac=0.9):
-    """Final residual of a free run against the free-running oracle, by max
-    error, on the rows whose every decision (candidate, attention and FFN
-    membership in every layer) agreed on both sides."""
+    """Final residual of a free run against the free-running oracle.
+
+    Both sides start from the same inputs and take every selection on their
+    own scores, so a near-threshold decision can go either way.  A row whose
+    own decisions all agree can still see a different context: a row earlier
+    in the sequence that one side kept (or sent through the FFN) and the
+    other did not changes that row's keys and values, and an FFN delta is
+    larger than the residual itself with these weights.  So:
+      * at least min_frac of the final rows must have agreed on every
+        decision (candidate, attention and FFN membership in every layer);
+      * every row before the first position where any decision differed in
+        any layer has the same causal history on both sides, and its final
+        residual must meet the bf16 bar by its maximum error.
+    The other agreeing rows' errors are reported, not asserted; per-layer
+    parity is the teacher-forced check."""
     g_layers = [(t["pos"].cpu().numpy(), t["idx"].cpu().numpy(), t["idx_f"].cpu().numpy()) for t in traces]
     r_layers = [(h["pos"], h["attn"]["idx"], h["ffn"]["idx_f"]) for h in hist]
     rows = agreeing_rows(final, g_layers, r_layers)
@@ -235,16 +247,30 @@ def _compare_final_rows(x, final, ref, pos_ref, traces, hist, min_frac=0.9):
     io = np.searchsorted(pos_ref, rows)
     got, exp = np64(x)[ig], ref[io]
     err = np.abs(got - exp).max(axis=1) / np.abs(exp).max(axis=1)
-    _log(f"final residual: {len(rows)} of {len(pos_ref)} rows agreed on every decision, worst row {err.max():.3e}")
-    assert err.max() <= BF16_REL, err.max()
+    diff = set()
+    for li, ((gp, gi, gf), (rp, ri, rf)) in enumerate(zip(g_layers, r_layers)):
+        rp = np.asarray(rp)
+        d_c = set(gp.tolist()) ^ set(rp.tolist())
+        d_a = set(gp[gi].tolist()) ^ set(rp[np.asarray(ri)].tolist())
+        d_f = set(gp[gf].tolist()) ^ set(rp[np.asarray(rf)].tolist())
+        _log(f"  layer {li}: candidates differ in {len(d_c)} rows, attention selections in {len(d_a)}, "
+             f"FFN selections in {len(d_f)}")
+        diff |= d_c | d_a | d_f
+    p_first = min(diff) if diff else int(1 << 30)
+    early = rows < p_first
+    worst_early = float(err[early].max()) if early.any() else 0.0
+    _log(f"final residual: {len(rows)} of {len(pos_ref)} rows agreed on every decision (worst {err.max():.3e}); "
+         f"first differing decision at position {p_first}: {int(early.sum())} rows before it, worst {worst_early:.3e}")
+    assert worst_early <= BF16_REL, worst_early
 
 
 def test_msdp_stack_8_layers_4k_free_running():
     """The 32K stack's exact recipe (8 LLaMA-shaped pre-norm RoPE layers,
     budgets 0.6 / 0.45 / 0.35 / 0.25 of N, keep 0.35 / 0.35) at 4096 tokens,
     run free on both sides from the same seeded inputs: candidate sets within
-    the chain window at the first boundary, the final residual by max error
-    on the rows whose decisions all agreed."""
+    the chain window at the first boundary, every layer teacher-forced on the
+    GPU's own inputs, and the final residual by max error on the rows whose
+    causal history matched (see _compare_final_rows)."""
     cfgd = W.CONFIGS["msdp_stack_32k"]
     sh = W.LayerShape(n=4096, P=64)
     _log("generate 8-layer stack at 4096 tokens")
@@ -264,6 +290,10 @@ def test_msdp_stack_8_layers_4k_free_running():
                              rel=CHAIN_WINDOW) == 0
     final = pos.cpu().numpy()
     assert len(np.intersect1d(final, pos_ref)) / len(pos_ref) > 0.95
+    for li, tr in enumerate(traces):
+        _log(f"teacher-forced steps, layer {li}")
+        check_layer(tr, {k: st["layers"][li][k] for k in WKEYS}, ocfg, prune_to=pts.get(li), n_sample=128,
+                    seed=li, log=_log)
     # 24 decisions per row over 8 layers, each near-threshold row free to go
     # either way in a free run: 0.88 of the final rows agreed on all of them
     _compare_final_rows(x, final, ref, pos_ref, traces, hist, min_frac=0.8)
