@@ -19,7 +19,8 @@ by its maximum error, at full size:
   FFN pre-norm z              residual after attention              bf16, every row
   LTP score L                 z                                     fp32 (1e-4), 2e-5 per row
   fused score                 the GPU's S and L                     bit-exact (same fp32 operations)
-  FFN selection idx_f         oracle S and L, fused in fp32         1e-5 window
+  FFN selection idx_f         oracle S and L, fused in fp32, and    1e-5 window
+                              fused by the float64 definition
   layer output                z, residual after attention           bf16, sampled rows; the rest bit-identical
 
 "Sampled rows" are at least 64 rows per check, including the first and last
@@ -179,6 +180,14 @@ def check_layer(tr, w, cfg, prune_to=None, n_sample=64, seed=0, log=print, k_giv
     idx_f = tr["idx_f"].cpu().numpy().astype(np.int64)
     assert window_violations(fused_ref.astype(np.float64), idx_f, k_f, P) == 0, \
         "FFN selection outside the 1e-5 window"
+    # and against the fusion's plain float64 definition on the oracle's scores,
+    # which does not depend on any fp32 operation order
+    S64, L64 = np.asarray(S_c, dtype=np.float64), np.asarray(L_ref, dtype=np.float64)
+    if cfg.get("fusion", "maxnorm_add") == "multiply":
+        fused64 = S64 * L64
+    else:
+        fused64 = wa * S64 / S64.max() + wb * L64 / L64.max()
+    assert window_violations(fused64, idx_f, k_f, P) == 0, "FFN selection outside the 1e-5 window (float64 fusion)"
     fsel = _sample(len(idx_f), n_sample, rng, must=(0, len(idx_f) - 1))
     fi = idx_f[fsel]
     _, y = ffn.swiglu_rows(z[fi], w64["wg"], w64["wu"], w64["wd"])
