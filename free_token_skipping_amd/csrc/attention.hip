@@ -347,10 +347,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 // ahead of the one being scored: one tile in flight per workgroup left the
 // passes waiting on load latency.
 //
-// Pass 1 (stats): per (chunk, head, probe) the running max and sum of
-// exp2(scale*log2e * logit), logits as S^T = K Q^T so a lane owns a probe.
-// The reference max moves only when a tile's max passes it by 2^8 (exp2
-// units), so a tile costs one max, one fma, one exp and one add per logit.
+// Pass 1 (stats): per (chunk, head, probe) a reference and the sum of
+// exp2(scale*log2e * logit - reference), logits as S^T = K Q^T so a lane owns
+// a probe.  The reference is set from the exact max only when a 16-logit
+// chain's sum of weights leaves [0, 2^64], so a logit costs one fma, one exp
+// and one add, with no max.
 // Combine: per (head, probe) the chunk partials merge into
 // M = max + log2(sum).
 // Pass 2 (column sums): logits as S = Q K^T so a lane owns a key, and each
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 // every workgroup also loads its probes' queries, so chunks stay as long as
 // that round allows; past 1024 keys the grid runs in several rounds.
 constexpr int MIN_CHUNK = 128;
-constexpr float kProbeLazy = 8.0f;   // exp2 units
+constexpr float kProbeGuard = 18446744073709551616.0f;   // 2^64: largest accepted sum of 16 weights
 constexpr int NS = 4;                // K tile stages in LDS
 
 int probe_chunk(int n, int Hq, int P) {
@@ -454,9 +455,15 @@ __global__ __launch_bounds__(256 * PW, 2 / PW) void probe_stats_kernel(const uin
 #pragma unroll
   for (int c = 0; c < PT; ++c) { m[c] = -INFINITY; l[c] = 0.f; }
 
-  // one tile's logits into the running (max, sum) of each probe, 32 keys at a
-  // time (the K fragments of those keys are shared by the PT probe tiles);
-  // MASK: the tile reaches past the first probe row (causal mask per key)
+  // one tile's logits added to each probe's running sum against the lane's
+  // reference m[c] (exp2 units), 32 keys at a time (the K fragments of those
+  // keys are shared by the PT probe tiles).  There is no per-logit max: the
+  // sum of a chain's 16 weights is tested instead, and a wave in which some
+  // lane's sum leaves [0, 2^64] (no reference yet, a logit 64 units above
+  // the reference, or a NaN) redoes that chain against the exact running max,
+  // which becomes the reference.  A sum below 2^64 keeps l far from overflow,
+  // and any reference gives the same M = ref + log2(l) up to rounding.
+  // MASK: the tile reaches past the first probe row (causal mask per key).
   auto tile = [&](auto mask, const uint16_t* kt_s, int j0) {
     constexpr bool MASK = decltype(mask)::value;
 #pragma unroll
@@ -477,38 +484,133 @@ __global__ __launch_bounds__(256 * PW, 2 / PW) void probe_stats_kernel(const uin
           for (int r = 0; r < 16; ++r)
             if (j0 + kt * 32 + (r >> 3) * 16 + half * 8 + (r & 7) > prow) s[r] = -INFINITY;
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
-        mx *= sl2;
-        // each lane moves its own reference when its logits pass it by 2^8
-        const float mref = mx > m[c] + kProbeLazy ? mx : m[c];
-        const float alpha = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[c] - mref);
-        m[c] = mref;
-        const float mz = mref == -INFINITY ? 0.f : mref;   // a lane with no visible key yet adds zeros
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        const float nm = -m[c];
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
-          a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -mz));
-          a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2, -mz));
-          a2 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 2], sl2, -mz));
-          a3 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 3], sl2, -mz));
+          a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, nm));
+          a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2, nm));
+          a2 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 2], sl2, nm));
+          a3 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 3], sl2, nm));
         }
-        l[c] = l[c] * alpha + ((a0 + a1) + (a2 + a3));
+        const float ts = (a0 + a1) + (a2 + a3);
+        if (__builtin_expect(__any(!(ts <= kProbeGuard)), 0)) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[r]);
+          const float mref = __builtin_fmaxf(m[c], mx * sl2);
+          const float alpha = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[c] - mref);
+          const float mz = mref == -INFINITY ? 0.f : mref;   // a lane with no visible key yet adds zeros
+          float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            b0 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -mz));
+            b1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2, -mz));
+          }
+          l[c] = l[c] * alpha + (b0 + b1);
+          m[c] = mref;
+        } else {
+          l[c] += ts;
+        }
       }
     }
   };
 
+  // Tiles entirely below the first probe row (all but the sequence's last one
+  // or two) run software-pipelined across the ring barriers: the weights of
+  // each 16-logit chain are formed while the matrix core computes the next
+  // chain, and a tile's last chain is finished under the next tile's first.
+  auto chain = [&](const bf16x8 (&kf)[8], int c) {
+    f32x16 s;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = mfma32x32x16(kf[kk], qf[c][kk], kk == 0 ? f32x16{} : s);
+    return s;
+  };
+  auto wsum = [&](const f32x16& s, int c) {
+    const float nm = -m[c];
+    float a[4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, nm));
+      a[r & 3] = r < 4 ? w : a[r & 3] + w;
+    }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  };
+  // accept a chain's sum, or redo the chain against the exact running max
+  auto settle = [&](const f32x16& s, int c, float ts) {
+    if (__builtin_expect(__any(!(ts <= kProbeGuard)), 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[r]);
+      const float mref = __builtin_fmaxf(m[c], mx * sl2);
+      const float alpha = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[c] - mref);
+      const float mz = mref == -INFINITY ? 0.f : mref;
+      float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        b0 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -mz));
+        b1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2, -mz));
+      }
+      l[c] = l[c] * alpha + (b0 + b1);
+      m[c] = mref;
+    } else {
+      l[c] += ts;
+    }
+  };
+  // one MFMA, then six VALU instructions, eight times: a chain's MFMAs
+  // interleaved with the previous chain's weights
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+  };
+  // chains of a tile in the order i = kt*PT + c; sp carries the last one
+  auto tile_pipe = [&](auto first, const uint16_t* kt_s, f32x16& sp) {
+    constexpr bool FIRST = decltype(first)::value;
+    bf16x8 kf[2][8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        kf[kt][kk] = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+    f32x16 sc[2 * PT];
+#pragma unroll
+    for (int i = 0; i < 2 * PT; ++i) {
+      sc[i] = chain(kf[i / PT], i % PT);
+      if (i == 0) {
+        if constexpr (!FIRST) {
+          const float ts = wsum(sp, PT - 1);
+          interleave();
+          settle(sp, PT - 1, ts);
+        }
+      } else {
+        const float ts = wsum(sc[i - 1], (i - 1) % PT);
+        interleave();
+        settle(sc[i - 1], (i - 1) % PT, ts);
+      }
+    }
+    sp = sc[2 * PT - 1];
+  };
+
+  int nt_fast = first_probe_row + 1 - c0;            // keys of the chunk at or below the first probe row
+  nt_fast = nt_fast <= 0 ? 0 : min(nt, nt_fast / KT);
+  f32x16 sp;
   for (int t = 0; t < nt; ++t) {
     const int j0 = c0 + t * KT;
     // every thread's copies of tile t have landed; stage (t-1) % NS is free
     barrier_k_tiles<NT>(min(NS - 2, nt - 1 - t));
     if (t + NS - 1 < nt) issue_k_tile<NT>(Ks[(t + NS - 1) % NS], k, j0 + (NS - 1) * KT, n, Hkv, g, tid);
-    if (j0 + KT - 1 > first_probe_row)                // uniform: only the last tiles of the sequence
-      tile(std::true_type{}, Ks[t % NS], j0);
-    else
-      tile(std::false_type{}, Ks[t % NS], j0);
+    if (t < nt_fast) {
+      if (t == 0) tile_pipe(std::true_type{}, Ks[t % NS], sp);
+      else tile_pipe(std::false_type{}, Ks[t % NS], sp);
+    } else {
+      if (t == nt_fast && t > 0) settle(sp, PT - 1, wsum(sp, PT - 1));
+      tile(std::true_type{}, Ks[t % NS], j0);        // reaches past the first probe row
+    }
   }
+  if (nt_fast == nt && nt > 0) settle(sp, PT - 1, wsum(sp, PT - 1));
   // merge the two half-waves (they hold different keys of the same probes)
 #pragma unroll
   for (int c = 0; c < PT; ++c) {
@@ -546,7 +648,12 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restr
 }
 
 // Pass 2: column sums of the normalised probe softmax for one key chunk and
-// one head quad; logits formed as S = Q K^T so a lane owns one key.
+// one head quad; logits formed as S = Q K^T so a lane owns one key, and each
+// lane keeps -M of its 16*PT probe rows in registers.  Per tile, each wave
+// adds its two half-waves and leaves its 64 key sums in LDS; after the next
+// tile's ring barrier one wave adds the waves' sums in a fixed order into the
+// chunk's column sums, also in LDS, which are written out once at the end.
+constexpr int MAX_CHUNK = 1024;
 template <int PT, int PW>
 __global__ __launch_bounds__(256 * PW, 2 / PW) void probe_colsum_kernel(const uint16_t* __restrict__ q,
                                                                         const uint16_t* __restrict__ k, int n,
@@ -555,12 +662,11 @@ __global__ __launch_bounds__(256 * PW, 2 / PW) void probe_colsum_kernel(const ui
                                                                         float* __restrict__ quad_sum) {
   constexpr int P = 32 * PT * PW, NT = 256 * PW, NW = 4 * PW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NS][KT * DH];
-  __shared__ __attribute__((aligned(16))) float st_M[4][P];
-  __shared__ float red[2][NW][KT];
+  __shared__ __attribute__((aligned(16))) float red[2][KT][NW];     // [key][wave]
+  __shared__ __attribute__((aligned(16))) float csum[MAX_CHUNK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int hw = wave & 3;
-  const int h = blockIdx.y * 4 + hw;
+  const int h = blockIdx.y * 4 + (wave & 3);
   const int pbase = (wave >> 2) * 32 * PT;
   const int g = (blockIdx.y * 4) / (Hq / Hkv);
   const int chunk = blockIdx.x;
@@ -568,7 +674,16 @@ __global__ __launch_bounds__(256 * PW, 2 / PW) void probe_colsum_kernel(const ui
   const int nt = min(chunk_keys / KT, (n - c0 + KT - 1) / KT);
   const int first_probe_row = n - P;
 
-  for (int i = tid; i < 4 * P; i += NT) st_M[i / P][i % P] = fin_M[(blockIdx.y * 4 + i / P) * P + i % P];
+  // -M of this lane's rows: reg r of probe tile c is probe pbase + c*32 + (r>>2)*8 + half*4 + (r&3)
+  float nM[PT][16];
+#pragma unroll
+  for (int c = 0; c < PT; ++c)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const f32x4 mm = *reinterpret_cast<const f32x4*>(fin_M + (long)h * P + pbase + c * 32 + qd * 8 + half * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nM[c][qd * 4 + e] = -mm[e];
+    }
   bf16x8 qf[PT][8];
   load_probe_q<PT>(qf, q, pbase, Hq, h, l32, half);
   __builtin_amdgcn_s_waitcnt(0x0F70);                 // queries and M land before any K tile is counted
@@ -587,56 +702,150 @@ __global__ __launch_bounds__(256 * PW, 2 / PW) void probe_colsum_kernel(const ui
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         kf[kk] = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
-      float a0 = 0.f, a1 = 0.f;
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < PT; ++c) {
         f32x16 s;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) s = mfma32x32x16(qf[c][kk], kf[kk], kk == 0 ? f32x16{} : s);
-        // reg r -> probe row pbase + c*32 + (r>>2)*8 + half*4 + (r&3)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int pb = pbase + c * 32 + qd * 8 + half * 4;
-          const f32x4 mm = *reinterpret_cast<const f32x4*>(&st_M[hw][pb]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qd * 4 + e], sl2, -mm[e]));
-            if constexpr (MASK) w = key > first_probe_row + pb + e ? 0.f : w;
-            if (e & 1) a1 += w; else a0 += w;
+        for (int r = 0; r < 16; ++r) {
+          float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, nM[c][r]));
+          if constexpr (MASK) {
+            const int row = pbase + c * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+            w = key > first_probe_row + row ? 0.f : w;
           }
+          a[r & 3] += w;
         }
       }
-      cs[kt] = a0 + a1;
+      cs[kt] = (a[0] + a[1]) + (a[2] + a[3]);
     }
   };
+  // the waves' sums of tile u, added in wave order, into the chunk's sums
+  auto reduce = [&](int u) {
+    if (tid < KT) {
+      const float* rr = red[u & 1][tid];
+      float tot = rr[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) tot += rr[w];
+      csum[u * KT + tid] = tot;
+    }
+  };
+  // this wave's sums of tile u (both half-waves added) into red[u & 1]
+  auto put = [&](int u, float cs0, float cs1) {
+    cs0 += __shfl_xor(cs0, 32);
+    cs1 += __shfl_xor(cs1, 32);
+    if (half == 0) {
+      red[u & 1][perm32(l32)][wave] = cs0;
+      red[u & 1][32 + perm32(l32)][wave] = cs1;
+    }
+  };
+  auto raw_barrier = []() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): LDS traffic done (vmcnt untouched)
+    __builtin_amdgcn_s_barrier();
+  };
 
-  for (int t = 0; t < nt; ++t) {
+  // Tiles entirely below the first probe row run software-pipelined across
+  // the ring barriers, as in the stats pass: a chain's weights are formed
+  // while the matrix core computes the next chain.  A tile's last chain is
+  // finished under the next tile's first, so its sums reach red one tile
+  // later and are reduced two tiles later.
+  auto chain = [&](const bf16x8 (&kf)[8], int c) {
+    f32x16 s;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = mfma32x32x16(qf[c][kk], kf[kk], kk == 0 ? f32x16{} : s);
+    return s;
+  };
+  auto wadd = [&](const f32x16& s, int c, float (&a)[4], bool init) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, nM[c][r]));
+      a[r & 3] = (init && r < 4) ? w : a[r & 3] + w;
+    }
+  };
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+  };
+  // sl: last chain of the previous tile; a1p: that tile's kt = 1 partial
+  // sums (its chains before the last); cs0p: its finished kt = 0 sum
+  auto tile_pipe = [&](auto first, int t, const uint16_t* kt_s, f32x16& sl, float (&a1p)[4], float& cs0p) {
+    constexpr bool FIRST = decltype(first)::value;
+    // the kt = 1 fragments are read after the first chain is issued (fewer live registers)
+    bf16x8 kf[2][8];
+    auto frags = [&](int kt) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        kf[kt][kk] = *reinterpret_cast<const bf16x8*>(kt_s + kswz(kt * 32 + perm32(l32), kk * 2 + half));
+    };
+    frags(0);
+    float a0[4], a1[4];
+    f32x16 sc[2 * PT];
+#pragma unroll
+    for (int i = 0; i < 2 * PT; ++i) {
+      sc[i] = chain(kf[i / PT], i % PT);
+      if (i == 0) frags(1);
+      if (i == 0) {
+        if constexpr (!FIRST) {
+          wadd(sl, PT - 1, a1p, PT == 1);
+          interleave();
+          put(t - 1, cs0p, (a1p[0] + a1p[1]) + (a1p[2] + a1p[3]));
+        }
+      } else {
+        const int j = i - 1;                       // chain j = kt*PT + c
+        if (j / PT == 0) wadd(sc[j], j % PT, a0, j % PT == 0);
+        else wadd(sc[j], j % PT, a1, j % PT == 0);
+        interleave();
+      }
+    }
+    cs0p = (a0[0] + a0[1]) + (a0[2] + a0[3]);
+    if constexpr (PT > 1) {                        // with one probe tile, the next wadd starts a1p
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a1p[e] = a1[e];
+    }
+    sl = sc[2 * PT - 1];
+  };
+
+  int nt_fast = first_probe_row + 1 - c0;
+  nt_fast = nt_fast <= 0 ? 0 : min(nt, nt_fast / KT);
+  if (nt_fast > 0) {
+    f32x16 sl;
+    float a1p[4] = {0.f, 0.f, 0.f, 0.f}, cs0p = 0.f;
+    for (int t = 0; t < nt_fast; ++t) {
+      // tile t in LDS; stage (t-1) % NS free; every wave's sums of tile t-2 in red[t & 1]
+      barrier_k_tiles<NT>(min(NS - 2, nt - 1 - t));
+      if (t >= 2) reduce(t - 2);
+      if (t + NS - 1 < nt) issue_k_tile<NT>(Ks[(t + NS - 1) % NS], k, c0 + (t + NS - 1) * KT, n, Hkv, g, tid);
+      if (t == 0) tile_pipe(std::true_type{}, t, Ks[t % NS], sl, a1p, cs0p);
+      else tile_pipe(std::false_type{}, t, Ks[t % NS], sl, a1p, cs0p);
+    }
+    wadd(sl, PT - 1, a1p, PT == 1);
+    put(nt_fast - 1, cs0p, (a1p[0] + a1p[1]) + (a1p[2] + a1p[3]));
+    raw_barrier();
+    if (nt_fast >= 2) reduce(nt_fast - 2);
+    reduce(nt_fast - 1);
+    raw_barrier();
+  }
+  // tiles that reach past the first probe row: no pipelining, sums reduced one tile later
+  for (int t = nt_fast; t < nt; ++t) {
     const int j0 = c0 + t * KT;
-    // tile t in LDS; stage (t-1) % NS free; red[(t-1) & 1] read (after last step's barrier)
     barrier_k_tiles<NT>(min(NS - 2, nt - 1 - t));
+    if (t > nt_fast) reduce(t - 1);
     if (t + NS - 1 < nt) issue_k_tile<NT>(Ks[(t + NS - 1) % NS], k, j0 + (NS - 1) * KT, n, Hkv, g, tid);
     float cs[2];
-    if (j0 + KT - 1 > first_probe_row)
-      tile(std::true_type{}, Ks[t % NS], j0, cs);
-    else
-      tile(std::false_type{}, Ks[t % NS], j0, cs);
-    // add the other half-wave (other probe rows), then the waves of the quad
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) cs[kt] += __shfl_xor(cs[kt], 32);
-    float(*rd)[KT] = red[t & 1];
-    if (half == 0) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) rd[wave][kt * 32 + perm32(l32)] = cs[kt];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): the sums are in LDS (vmcnt untouched)
-    __builtin_amdgcn_s_barrier();
-    if (tid < KT && j0 + tid < n) {
-      float tot = rd[0][tid];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) tot += rd[w][tid];
-      quad_sum[(long)blockIdx.y * n + j0 + tid] = tot;
-    }
+    tile(std::true_type{}, Ks[t % NS], j0, cs);
+    put(t, cs[0], cs[1]);
   }
+  if (nt_fast < nt) {
+    raw_barrier();
+    reduce(nt - 1);
+  }
+  __syncthreads();
+  const int nk = min(nt * KT, n - c0);
+  for (int i = tid; i < nk; i += NT) quad_sum[(long)blockIdx.y * n + c0 + i] = csum[i];
 }
 
 // Final: S[j] = sum over head quads, fixed order.

@@ -43,6 +43,22 @@ def test_probe_bf16_small(n, P, Hq, Hkv):
     assert abs(got.sum() - Hq * P) < 1e-3 * Hq * P
 
 
+def test_probe_bf16_growing_logits():
+    """Keys whose norm grows 30x along the sequence: the late logits pass an
+    early reference by far more than 64 exp2 units (their weights overflow
+    against it), so the kernel's reference has to move many times per chunk."""
+    n, P, Hq, Hkv = 3000, 64, 8, 2
+    _log(f"probe bf16 growing logits n={n}")
+    q = W.randn((P, Hq, 128), seed=7, std=1.3)
+    k = W.randn((n, Hkv, 128), seed=8, std=1.3)
+    ramp = (1.0 + 30.0 * torch.arange(n, dtype=torch.float32) / n).view(n, 1, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    S = capi.spts_probe_attention(_cuda(q), _cuda(k))
+    ref = pap.pap_scores(W.as_f64(q), W.as_f64(k), 128 ** -0.5)
+    assert np.isfinite(np64(S)).all()
+    assert_close(np64(S), ref, F32_REL, "probe scores, growing logits")
+
+
 def test_probe_bf16_full_32k_and_select_window():
     n, P, Hq, Hkv = 32768, 64, 32, 8
     _log("probe bf16 full 32K")
