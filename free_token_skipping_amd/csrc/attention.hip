@@ -43,19 +43,22 @@ __device__ __forceinline__ int perm32(int i) { return (i & ~12) | ((i & 4) << 1)
 // the logits of tile t+1 and accumulates O += V_{t-1} P_{t-1} (the P of the
 // previous step).  The three streams share no data, so they interleave one
 // MFMA at a time; the exp2 stream hides almost entirely behind the matrix
-// core.  Masking of tile t+1 and the reference-max update follow in the same
-// step, after the overlapped block.
+// core.  The check of tile t's weights and the masking of tile t+1 follow
+// in the same step, after the overlapped block.
 //
-// The reference max is updated lazily: only when a lane's logits exceed it
-// by more than 2^8 (exp2 units), so the O rescale is rare; p = exp2(s*scale*
-// log2e - m) then stays <= 256 and O / l is exact whatever reference was used.
+// No running max is taken per logit: p = exp2(s*scale*log2e - m) is formed
+// against the current reference m, and only when a lane's 32 weights of a
+// tile sum to more than 2^16 (or to inf or NaN) is the tile redone against
+// the exact max, which becomes the reference (a rare O rescale).  The first
+// tile's exact max sets the initial reference.  Every p then stays <= 2^16, and O / l
+// is exact whatever reference was used.
 //
 // LDS rows are padded by 16 bytes instead of XOR-swizzled: gfx950 serves a
 // 16-byte-per-lane read 16 lanes at a time over a 256-byte bank window, and a
 // row stride of 17 (K) or 9 (V^T) 16-byte slots puts the 16 rows read together
 // in 16 distinct slots, while every fragment sits at a constant offset from
 // one per-lane base address.
-constexpr float kLazyMax = 8.0f;
+constexpr float kGuardP = 65536.0f;   // 2^16: largest accepted sum of a lane's 32 weights of a tile
 constexpr int KROW = DH + 8;     // K tile row: 128 dh + 8 pad elements (272 B)
 constexpr int VROW = KT + 8;     // V^T tile row: 64 keys + 8 pad elements (144 B)
 
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ v, int kq,
                                                            int n, int Hq, int Hkv, float sl2,
                                                            uint16_t* __restrict__ o) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[3][KT * KROW];   // K_t stays for its whole step t
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][DH * VROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -167,11 +170,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
         sd[kt] = mfma32x32x16(kf, qf[kk], kk == 0 ? zero16 : sd[kt]);
       }
   };
-  // mask tile t's keys beyond each query, then move the reference max if
-  // needed; key of reg r = t*64 + kt*32 + (r>>3)*16 + half*8 + (r&7).  `pend`
-  // is the P of the previous tile, already formed against the old reference
-  // but not yet multiplied into O: a move rescales it together with O and l.
-  auto prepare = [&](int t, f32x16 (&sd)[2], bf16x8 (&pend)[4]) {
+  // mask tile t's keys beyond each query; key of reg r = t*64 + kt*32 +
+  // (r>>3)*16 + half*8 + (r&7)
+  auto mask = [&](int t, f32x16 (&sd)[2]) {
     if (t >= nfull) {
       const int j0 = t * KT;
 #pragma unroll
@@ -182,31 +183,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
           if (key > qpos) sd[kt][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sd[kt][r]), sd[kt][r + 1]);
-    mx *= sl2;
-    if (__any(mx > m_ref + kLazyMax)) {
-      const float m_new = fmaxf(m_ref, fmaxf(mx, __shfl_xor(mx, 32)));
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        f32x8 pv = __builtin_convertvector(pend[c], f32x8);
-        pv *= alpha;
-        pend[c] = __builtin_convertvector(pv, bf16x8);
-      }
-      m_ref = m_new;
-    }
   };
-  // P_t = exp2(logit * scale * log2e - m_ref) as bf16 MFMA operands; l += P_t
+  // P_t = exp2(logit * scale * log2e - m_ref) as bf16 MFMA operands; returns
+  // this half-wave's sum of the tile's weights (not yet added to l)
   auto softmax = [&](f32x16 (&sc)[2], bf16x8 (&pc)[4]) {
+    float a[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -215,10 +196,42 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][sub * 8 + e], sl2, -m_ref));
-          l_part += pv[e];
+          const int i = kt * 16 + sub * 8 + e;
+          a[i & 3] = i < 4 ? pv[e] : a[i & 3] + pv[e];
         }
         pc[kt * 2 + sub] = __builtin_convertvector(pv, bf16x8);
       }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  };
+  // Accept tile t's weights, or, when some lane's sum left [0, 2^16] (no
+  // reference yet, a logit 16 units above the reference, or a NaN), move the
+  // reference to the exact running max (shared by the two half-waves of a
+  // query), rescale O and l, and form the tile's P again.  O already holds
+  // P_{t-1} V_{t-1} at the old reference, so nothing else is pending.
+  // The logits of tile t are formed again from K_t, still in Ks[t % 3]
+  // during step t, so they need not stay in registers past the softmax.
+  auto settle = [&](int t, bf16x8 (&pc)[4], float ts) {
+    if (__builtin_expect(__any(!(ts <= kGuardP)), 0)) {
+      f32x16 sc[2];
+      logits(t % 3, sc);
+      mask(t, sc);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[kt][r]);
+      mx *= sl2;
+      const float m_new = fmaxf(m_ref, fmaxf(mx, __shfl_xor(mx, 32)));
+      const float alpha = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      m_ref = m_new;
+      ts = softmax(sc, pc);
+    }
+    l_part += ts;
   };
   // O^T += V_u^T P_u^T, V_u in buffer vb
   auto pv_mma = [&](int vb, bf16x8 (&pp)[4]) {
@@ -236,20 +249,21 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   // set), pp the P of tile t-1.  The matrix core forms the logits of tile t+1
   // and O += P_{t-1} V_{t-1} while the VALU turns tile t's logits into P_t, so
   // all three streams are independent and interleave one MFMA at a time.  V
-  // trails K by two tiles: step t stores V_t and K_{t+2} (into buffer t & 1)
-  // from the registers kc / vc loaded during step t-1, and loads V_{t+1} and
-  // K_{t+3} into kn / vn; V_t is read at step t+1.
+  // trails K by two tiles: step t stores K_{t+2} (into K buffer (t+2) % 3)
+  // and V_t (into V buffer t & 1) from the registers kc / vc loaded during
+  // step t-1, and loads V_{t+1} and K_{t+3} into kn / vn; V_t is read at step
+  // t+1.
   auto step = [&](auto with_pv, int t, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pp)[4],
                   bf16x8 (&pc)[4], u32x4 (&kc)[2], u32x4 (&vc)[2], u32x4 (&kn)[2], u32x4 (&vn)[2]) {
     constexpr bool kPV = decltype(with_pv)::value;
     // K/V staging is unconditional (rows clamp to n-1; past the last tile the
-    // K store lands in buffer t & 1, whose tile was read in step t-1), so no
-    // branch splits the MFMA / VALU block
+    // K store lands in buffer (t+2) % 3, whose tile was read in step t-2), so
+    // no branch splits the MFMA / VALU block
     load_k(kn, (t + 3) * KT);
     load_v(vn, (t + 1) * KT);
-    logits((t + 1) & 1, sn);             // stale data past the last tile; unused
+    logits((t + 1) % 3, sn);             // stale data past the last tile; unused
     if constexpr (kPV) pv_mma((t - 1) & 1, pp);
-    softmax(sc, pc);
+    float ts = softmax(sc, pc);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);          // first K fragments
     if constexpr (kPV) {
 #pragma unroll
@@ -278,10 +292,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     }
     // P_t is only read in the next step; without this anchor the compiler
     // sinks the softmax below the masking of tile t+1, away from the MFMAs
-    asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(pc[2]), "+v"(pc[3]), "+v"(l_part));
-    store_k(kc, t & 1);
+    asm volatile("" : "+v"(pc[0]), "+v"(pc[1]), "+v"(pc[2]), "+v"(pc[3]), "+v"(ts));
+    settle(t, pc, ts);
+    store_k(kc, (t + 2) % 3);
     store_v(vc, t & 1);
-    if (t + 1 < ntiles) prepare(t + 1, sn, pc);
+    if (t + 1 < ntiles) mask(t + 1, sn);
     __syncthreads();
   };
 
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   }
   load_k(kra, 2 * KT);
   load_v(vra, 0);
-  __syncthreads();
+  __syncthreads();                        // K_0, K_1 in LDS
   f32x16 sa[2], sb[2];
   bf16x8 pa[4], pb[4];
 #pragma unroll
@@ -304,9 +319,17 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     pb[c] = bf16x8{};
   }
   logits(0, sa);
-  prepare(0, sa, pb);                     // nothing pending yet (pb is zero)
-  // step 0 stages K_2 into Ks[0]: every wave must have read K_0 from it first
-  __syncthreads();
+  mask(0, sa);
+  // tile 0's reference: its exact max (key 0 is visible to every query), so
+  // the first tile is not formed twice
+  {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sa[kt][r]);
+    m_ref = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  }
   step(std::false_type{}, 0, sa, sb, pb, pa, kra, vra, krb, vrb);
   int t = 1;
   for (; t + 1 < ntiles; t += 2) {
@@ -371,8 +394,8 @@ constexpr int MIN_CHUNK = 128;
 constexpr float kProbeGuard = 18446744073709551616.0f;   // 2^64: largest accepted sum of 16 weights
 constexpr int NS = 4;                // K tile stages in LDS
 
-int probe_chunk(int n, int Hq, int P) {
-  const long slots = 256L * (P <= 64 ? 2 : 1);                     // two waves per SIMD: 2 or 1 workgroups per CU
+int probe_chunk(int n, int Hq, int occ) {
+  const long slots = 256L * occ;                                   // resident workgroups
   const long need = ((long)n * (Hq / 4) + slots - 1) / slots;      // keys per chunk for one round
   const int c = (int)(((need + KT - 1) / KT) * KT);
   return c < MIN_CHUNK ? MIN_CHUNK : (c > 1024 ? 1024 : c);
@@ -427,8 +450,9 @@ __device__ __forceinline__ void load_probe_q(bf16x8 (&qf)[PT][8], const uint16_t
                                                    half * 8);
 }
 
-template <int PT, int PW>   // each wave: 32*PT probes of one head; PW waves per head; P = 32*PT*PW
-__global__ __launch_bounds__(256 * PW, 2 / PW) void probe_stats_kernel(const uint16_t* __restrict__ q,
+// each wave: 32*PT probes of one head; PW waves per head; P = 32*PT*PW; OCC workgroups per CU
+template <int PT, int PW, int OCC>
+__global__ __launch_bounds__(256 * PW, OCC) void probe_stats_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ k, int n,
                                                                        int chunk_keys, int Hq, int Hkv, float sl2,
                                                                        float* __restrict__ part_m,
@@ -654,8 +678,8 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restr
 // tile's ring barrier one wave adds the waves' sums in a fixed order into the
 // chunk's column sums, also in LDS, which are written out once at the end.
 constexpr int MAX_CHUNK = 1024;
-template <int PT, int PW>
-__global__ __launch_bounds__(256 * PW, 2 / PW) void probe_colsum_kernel(const uint16_t* __restrict__ q,
+template <int PT, int PW, int OCC>
+__global__ __launch_bounds__(256 * PW, OCC) void probe_colsum_kernel(const uint16_t* __restrict__ q,
                                                                         const uint16_t* __restrict__ k, int n,
                                                                         int chunk_keys, int Hq, int Hkv, float sl2,
                                                                         const float* __restrict__ fin_M,
@@ -934,34 +958,41 @@ size_t probe_workspace(int n, int P, int Hq) {
   return (b + 255) & ~(size_t)255;
 }
 
-hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P, int Hq, int Hkv,
-                             float scale, float* scores, void* ws, hipStream_t s) {
-  const int ck = probe_chunk(n, Hq, P);
+// The two passes and the chunk combine for P = 32*PT*PW probes.
+template <int PT, int PW, int OCC>
+void probe_passes(const uint16_t* q, const uint16_t* k, int n, int Hq, int Hkv, float sl2, void* ws,
+                  float* scores, hipStream_t s) {
+  constexpr int P = 32 * PT * PW;
+  const int ck = probe_chunk(n, Hq, OCC);
   const int nchunks = (n + ck - 1) / ck;
   const long HP = (long)Hq * P;
   float* part_m = reinterpret_cast<float*>(ws);
   float* part_l = part_m + nchunks * HP;
   float* fin_M = part_l + nchunks * HP;
   float* quad = fin_M + 2 * HP;
-  const float sl2 = scale * kLog2e;
   const dim3 grid(nchunks, Hq / 4);
+  hipLaunchKernelGGL((probe_stats_kernel<PT, PW, OCC>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv, sl2,
+                     part_m, part_l);
+  hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_m, part_l, nchunks,
+                     (int)HP, fin_M);
+  hipLaunchKernelGGL((probe_colsum_kernel<PT, PW, OCC>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv, sl2,
+                     fin_M, quad);
+  hipLaunchKernelGGL(quad_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, quad, Hq / 4, n, scores);
+}
+
+hipError_t launch_probe_bf16(const uint16_t* q, const uint16_t* k, int n, int P, int Hq, int Hkv,
+                             float scale, float* scores, void* ws, hipStream_t s) {
+  const float sl2 = scale * kLog2e;
+  // Two waves per SIMD, 64 probes per wave: at 64 probes two 4-wave
+  // workgroups per CU (one wave per head), at 128 one 8-wave workgroup (two
+  // waves per head).  One 128-probe wave per SIMD and four 32-probe waves
+  // per SIMD both measured slower.
   switch (P) {
-#define SPTS_PROBE_CASE(PP, PT, PW)                                                                     \
-  case PP:                                                                                              \
-    hipLaunchKernelGGL((probe_stats_kernel<PT, PW>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv,  \
-                       sl2, part_m, part_l);                                                            \
-    hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_m, part_l,       \
-                       nchunks, (int)HP, fin_M);                                                        \
-    hipLaunchKernelGGL((probe_colsum_kernel<PT, PW>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv, \
-                       sl2, fin_M, quad);                                                               \
-    break;
-    SPTS_PROBE_CASE(32, 1, 1)
-    SPTS_PROBE_CASE(64, 2, 1)
-    SPTS_PROBE_CASE(128, 2, 2)
-#undef SPTS_PROBE_CASE
+    case 32: probe_passes<1, 1, 2>(q, k, n, Hq, Hkv, sl2, ws, scores, s); break;
+    case 64: probe_passes<2, 1, 2>(q, k, n, Hq, Hkv, sl2, ws, scores, s); break;
+    case 128: probe_passes<2, 2, 1>(q, k, n, Hq, Hkv, sl2, ws, scores, s); break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(quad_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, quad, Hq / 4, n, scores);
   return hipGetLastError();
 }
 

@@ -215,6 +215,26 @@ def test_reduced_attention_bf16(n, kq, Hq, Hkv):
     assert per_row.max() <= BF16_REL
 
 
+def test_reduced_attention_growing_logits():
+    """Keys whose norm grows 30x along the sequence: later tiles' logits pass
+    the softmax reference by far more than 16 exp2 units (their weights
+    overflow against it), so the kernel moves its reference many times."""
+    n, kq, Hq, Hkv = 3000, 700, 8, 2
+    _log(f"reduced attention bf16 growing logits n={n} kq={kq}")
+    q = W.randn((kq, Hq, 128), seed=17, std=1.3)
+    k = W.randn((n, Hkv, 128), seed=18, std=1.3)
+    ramp = (1.0 + 30.0 * torch.arange(n, dtype=torch.float32) / n).view(n, 1, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    v = W.randn((n, Hkv, 128), seed=19)
+    idx = W.sorted_rows(n, kq, 64, seed=20)
+    o = capi.spts_reduced_attention(_cuda(q), _cuda(idx), _cuda(k), _cuda(v))
+    ref = attention.reduced_attention(W.as_f64(q), idx.numpy(), W.as_f64(k), W.as_f64(v), 128 ** -0.5)
+    got = np64(o)
+    assert np.isfinite(got).all()
+    per_row = np.abs(got - ref).max(axis=(1, 2)) / np.abs(ref).max(axis=(1, 2))
+    assert per_row.max() <= BF16_REL, per_row.max()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_reduced_attention_unsorted_idx(dtype):
     """Query rows in shuffled order (and one row twice): each query's causal
