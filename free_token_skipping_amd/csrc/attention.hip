@@ -48,17 +48,19 @@ __device__ __forceinline__ int perm32(int i) { return (i & ~12) | ((i & 4) << 1)
 //
 // No running max is taken per logit: p = exp2(s*scale*log2e - m) is formed
 // against the current reference m, and only when a lane's 32 weights of a
-// tile sum to more than 2^16 (or to inf or NaN) is the tile redone against
+// tile sum to more than 2^64 (or to inf or NaN) is the tile redone against
 // the exact max, which becomes the reference (a rare O rescale).  The first
-// tile's exact max sets the initial reference.  Every p then stays <= 2^16, and O / l
-// is exact whatever reference was used.
+// tile's exact max sets the initial reference.  Every p then stays <= 2^64
+// (a bf16 holds it; O stays far inside fp32 range), so a key tens of exp2
+// units above the reference costs nothing extra, and O / l is exact
+// whatever reference was used.
 //
 // LDS rows are padded by 16 bytes instead of XOR-swizzled: gfx950 serves a
 // 16-byte-per-lane read 16 lanes at a time over a 256-byte bank window, and a
 // row stride of 17 (K) or 9 (V^T) 16-byte slots puts the 16 rows read together
 // in 16 distinct slots, while every fragment sits at a constant offset from
 // one per-lane base address.
-constexpr float kGuardP = 65536.0f;   // 2^16: largest accepted sum of a lane's 32 weights of a tile
+constexpr float kGuardP = 18446744073709551616.0f;   // 2^64: largest accepted sum of a lane's 32 weights of a tile
 constexpr int KROW = DH + 8;     // K tile row: 128 dh + 8 pad elements (272 B)
 constexpr int VROW = KT + 8;     // V^T tile row: 64 keys + 8 pad elements (144 B)
 
@@ -203,8 +205,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
       }
     return (a[0] + a[1]) + (a[2] + a[3]);
   };
-  // Accept tile t's weights, or, when some lane's sum left [0, 2^16] (no
-  // reference yet, a logit 16 units above the reference, or a NaN), move the
+  // Accept tile t's weights, or, when some lane's sum left [0, 2^64] (a
+  // logit 64 units above the reference, or a NaN), move the
   // reference to the exact running max (shared by the two half-waves of a
   // query), rescale O and l, and form the tile's P again.  O already holds
   // P_{t-1} V_{t-1} at the old reference, so nothing else is pending.
