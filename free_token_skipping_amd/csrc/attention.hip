@@ -473,7 +473,8 @@ __global__ __launch_bounds__(256 * PW, OCC) void probe_stats_kernel(const uint16
 
   bf16x8 qf[PT][8];
   load_probe_q<PT>(qf, q, pbase, Hq, h, l32, half);
-  __builtin_amdgcn_s_waitcnt(0x0F70);                 // the queries land before any K tile is counted
+  // no wait here: the queries are older than every K copy, so the first
+  // ring barrier's in-order count also covers them
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nt) issue_k_tile<NT>(Ks[s], k, c0 + s * KT, n, Hkv, g, tid);
@@ -712,7 +713,8 @@ __global__ __launch_bounds__(256 * PW, OCC) void probe_colsum_kernel(const uint1
     }
   bf16x8 qf[PT][8];
   load_probe_q<PT>(qf, q, pbase, Hq, h, l32, half);
-  __builtin_amdgcn_s_waitcnt(0x0F70);                 // queries and M land before any K tile is counted
+  // no wait here: the queries and M are older than every K copy, so the
+  // first ring barrier's in-order count also covers them
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nt) issue_k_tile<NT>(Ks[s], k, c0 + s * KT, n, Hkv, g, tid);
