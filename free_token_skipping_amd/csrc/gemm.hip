@@ -263,6 +263,11 @@ void gemm_tn_kernel(GemmArgs g) {
     const char* b1base = reinterpret_cast<const char*>(g.b1);
     const int KT = k1 - k0;                              // k-steps of this job
     const int kt_base = k0;
+    // B's k offset wraps at kwrap when it is set; otherwise the modulus is
+    // larger than any offset.  Kept free of a branch: a branch inside the
+    // k-loop splits the last phase into two blocks and undoes its
+    // MFMA / LDS-read interleave.
+    const uint32_t kwr = g.kwrap > 0 ? (uint32_t)g.kwrap : 0x7fffffffu;
 
     // The operands of k-step s go to slots As[s & 1] and Bs[s & 1]; s past
     // the job's last step reloads that step (never read), so every wave
@@ -279,7 +284,7 @@ void gemm_tn_kernel(GemmArgs g) {
     };
     auto issue_b = [&](int s) {
       const int kt = kt_base + (s < KT ? s : KT - 1);
-      const uint32_t kb = (g.kwrap > 0 ? (uint32_t)((kt * BK) % g.kwrap) : (uint32_t)kt * BK) * 2u;
+      const uint32_t kb = ((uint32_t)(kt * BK) % kwr) * 2u;
       uint16_t* b_s = Bs + (s & 1) * TILE_ELEMS;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
