@@ -457,8 +457,7 @@ template <int PT, int PW, int OCC>
 __global__ __launch_bounds__(256 * PW, OCC) void probe_stats_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ k, int n,
                                                                        int chunk_keys, int Hq, int Hkv, float sl2,
-                                                                       float* __restrict__ part_m,
-                                                                       float* __restrict__ part_l) {
+                                                                       float* __restrict__ part_lse, int nchunks) {
   constexpr int P = 32 * PT * PW, NT = 256 * PW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NS][KT * DH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -639,36 +638,36 @@ __global__ __launch_bounds__(256 * PW, OCC) void probe_stats_kernel(const uint16
   }
   if (nt_fast == nt && nt > 0) settle(sp, PT - 1, wsum(sp, PT - 1));
   // merge the two half-waves (they hold different keys of the same probes)
+  // and store the chunk's log-sum-exp ref + log2(sum) (exp2 units; -inf when
+  // no key of the chunk is visible to the probe), the chunks of one (head,
+  // probe) row side by side
 #pragma unroll
   for (int c = 0; c < PT; ++c) {
     const float m2 = __shfl_xor(m[c], 32), l2 = __shfl_xor(l[c], 32);
     const float mt = fmaxf(m[c], m2);
-    float lt = 0.f;
-    if (mt != -INFINITY) lt = l[c] * exp2f(m[c] - mt) + l2 * exp2f(m2 - mt);
-    if (half == 0) {
-      const long o = ((long)chunk * Hq + h) * P + pbase + c * 32 + l32;
-      part_m[o] = mt;
-      part_l[o] = lt;
-    }
+    float lse = -INFINITY;
+    if (mt != -INFINITY) lse = mt + log2f(l[c] * exp2f(m[c] - mt) + l2 * exp2f(m2 - mt));
+    if (half == 0) part_lse[((long)h * P + pbase + c * 32 + l32) * nchunks + chunk] = lse;
   }
 }
 
-// Combine chunk partials -> per (head, probe) M = max + log2(sum) in exp2
-// units.  One wave per (head, probe); lanes stride over chunks, fixed-order
-// wave tree.
-__global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restrict__ part_m,
-                                                            const float* __restrict__ part_l, int nchunks,
+// Combine the chunks' log-sum-exps -> per (head, probe) M = log2 of the sum
+// over chunks of 2^lse (exp2 units), taken against the largest.  One wave per
+// (head, probe), whose chunks lie side by side; lanes stride over chunks,
+// fixed-order wave tree.
+__global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restrict__ part_lse, int nchunks,
                                                             int HP, float* __restrict__ fin_M) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= HP) return;
+  const float* row = part_lse + (long)i * nchunks;
   float mt = -INFINITY;
-  for (int c = lane; c < nchunks; c += 64) mt = fmaxf(mt, part_m[(long)c * HP + i]);
+  for (int c = lane; c < nchunks; c += 64) mt = fmaxf(mt, row[c]);
   mt = wave_max(mt);
   float lt = 0.f;
   for (int c = lane; c < nchunks; c += 64) {
-    const float mc = part_m[(long)c * HP + i];
-    if (mc != -INFINITY) lt += part_l[(long)c * HP + i] * exp2f(mc - mt);
+    const float v = row[c];
+    if (v != -INFINITY) lt += exp2f(v - mt);
   }
   lt = wave_sum(lt);
   if (lane == 0) fin_M[i] = mt + log2f(lt);
@@ -957,8 +956,8 @@ __global__ void attn_f32_kernel(const float* q, const int32_t* idx, const float*
 size_t probe_workspace(int n, int P, int Hq) {
   const size_t nchunks = (size_t)(n + MIN_CHUNK - 1) / MIN_CHUNK;   // bound for every chunk size
   const size_t HP = (size_t)Hq * P;
-  // part_m, part_l [nchunks*HP]; fin_M [HP] (2*HP reserved); quad_sum [Hq/4 * n]
-  size_t b = 2 * nchunks * HP * 4 + 2 * HP * 4 + (size_t)((Hq + 3) / 4) * n * 4;
+  // part_lse [HP][nchunks]; fin_M [HP] (2*HP reserved); quad_sum [Hq/4 * n]
+  size_t b = HP * nchunks * 4 + 2 * HP * 4 + (size_t)((Hq + 3) / 4) * n * 4;
   return (b + 255) & ~(size_t)255;
 }
 
@@ -970,15 +969,13 @@ void probe_passes(const uint16_t* q, const uint16_t* k, int n, int Hq, int Hkv, 
   const int ck = probe_chunk(n, Hq, OCC);
   const int nchunks = (n + ck - 1) / ck;
   const long HP = (long)Hq * P;
-  float* part_m = reinterpret_cast<float*>(ws);
-  float* part_l = part_m + nchunks * HP;
-  float* fin_M = part_l + nchunks * HP;
+  float* part_lse = reinterpret_cast<float*>(ws);
+  float* fin_M = part_lse + HP * nchunks;
   float* quad = fin_M + 2 * HP;
   const dim3 grid(nchunks, Hq / 4);
   hipLaunchKernelGGL((probe_stats_kernel<PT, PW, OCC>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv, sl2,
-                     part_m, part_l);
-  hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_m, part_l, nchunks,
-                     (int)HP, fin_M);
+                     part_lse, nchunks);
+  hipLaunchKernelGGL(probe_combine_kernel, dim3((HP + 3) / 4), dim3(256), 0, s, part_lse, nchunks, (int)HP, fin_M);
   hipLaunchKernelGGL((probe_colsum_kernel<PT, PW, OCC>), grid, dim3(256 * PW), 0, s, q, k, n, ck, Hq, Hkv, sl2,
                      fin_M, quad);
   hipLaunchKernelGGL(quad_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, quad, Hq / 4, n, scores);
