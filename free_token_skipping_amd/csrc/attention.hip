@@ -387,20 +387,28 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 // the first probe row (the last one or two tiles of the sequence).  No float
 // atomics: the result does not depend on scheduling.
 //
-// A key chunk is a multiple of the 64-key tile between 128 and 1024 keys:
-// the shortest whose grid of chunks x head quads fits one round of resident
+// A key chunk is a multiple of the 64-key tile of at least 128 keys: the
+// shortest whose grid of chunks x head quads fits one round of resident
 // workgroups.  A partly filled second round costs a whole chunk's time, while
 // every workgroup also loads its probes' queries, so chunks stay as long as
-// that round allows; past 1024 keys the grid runs in several rounds.
+// that round allows; past max_chunk keys the grid runs in several rounds.
 constexpr int MIN_CHUNK = 128;
 constexpr float kProbeGuard = 18446744073709551616.0f;   // 2^64: largest accepted sum of 16 weights
 constexpr int NS = 4;                // K tile stages in LDS
 
+// Longest key chunk of pass 2 (its column sums sit in LDS): 32 KiB of sums
+// beside the 64 KiB K ring at one workgroup per CU, 8 KiB at two.
+constexpr int max_chunk(int occ) { return occ == 1 ? 8192 : 2048; }
+
+// Keys per chunk: the shortest multiple of 64 whose grid fits one round of
+// resident workgroups, so each workgroup loads its probe queries and fills its
+// K ring once per CU (4096-key chunks at 131072 keys and 128 probes: 333 us
+// per call against 373 us with 1024-key chunks in four rounds).
 int probe_chunk(int n, int Hq, int occ) {
   const long slots = 256L * occ;                                   // resident workgroups
   const long need = ((long)n * (Hq / 4) + slots - 1) / slots;      // keys per chunk for one round
-  const int c = (int)(((need + KT - 1) / KT) * KT);
-  return c < MIN_CHUNK ? MIN_CHUNK : (c > 1024 ? 1024 : c);
+  const long c = ((need + KT - 1) / KT) * KT;
+  return c < MIN_CHUNK ? MIN_CHUNK : (int)(c > max_chunk(occ) ? max_chunk(occ) : c);
 }
 
 // Issue the global -> LDS copy of the K tile [64 keys][128] of KV head g at
@@ -679,7 +687,6 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restr
 // adds its two half-waves and leaves its 64 key sums in LDS; after the next
 // tile's ring barrier one wave adds the waves' sums in a fixed order into the
 // chunk's column sums, also in LDS, which are written out once at the end.
-constexpr int MAX_CHUNK = 1024;
 template <int PT, int PW, int OCC>
 __global__ __launch_bounds__(256 * PW, OCC) void probe_colsum_kernel(const uint16_t* __restrict__ q,
                                                                         const uint16_t* __restrict__ k, int n,
@@ -689,7 +696,7 @@ __global__ __launch_bounds__(256 * PW, OCC) void probe_colsum_kernel(const uint1
   constexpr int P = 32 * PT * PW, NT = 256 * PW, NW = 4 * PW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NS][KT * DH];
   __shared__ __attribute__((aligned(16))) float red[2][KT][NW];     // [key][wave]
-  __shared__ __attribute__((aligned(16))) float csum[MAX_CHUNK];
+  __shared__ __attribute__((aligned(16))) float csum[max_chunk(OCC)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int h = blockIdx.y * 4 + (wave & 3);

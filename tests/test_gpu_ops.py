@@ -85,6 +85,21 @@ def test_probe_bf16_full_128k_clustered_and_select_window():
     assert window_violations(ref, idx.cpu().numpy(), k_a, P) == 0
 
 
+@pytest.mark.parametrize("n,P", [(131072, 64), (100000, 128)])
+def test_probe_bf16_long_chunks(n, P):
+    """Chunks longer than 1024 keys: 131072 keys at 64 probes run 2048-key
+    chunks (the limit at two workgroups per CU); 100000 keys at 128 probes run
+    3136-key chunks, the last one partly filled."""
+    Hq, Hkv = 32, 8
+    _log(f"probe bf16 long chunks n={n} P={P}")
+    q = W.randn((P, Hq, 128), seed=11, std=1.28)
+    k = W.randn((n, Hkv, 128), seed=12, std=1.28)
+    S = capi.spts_probe_attention(_cuda(q), _cuda(k))
+    ref = pap.pap_scores(W.as_f64(q), W.as_f64(k), 128 ** -0.5)
+    assert_close(np64(S), ref, F32_REL, "probe scores, long chunks")
+    assert abs(float(np64(S).sum()) - Hq * P) < 1e-3 * Hq * P
+
+
 def test_probe_f32_tiny_config():
     _log("probe fp32 tiny (N=256, 4 heads, d_head 64, P=16)")
     t = W.make_pap_tiny()
