@@ -26,6 +26,7 @@ EXPORTS = [
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
     "spts_linear_kv_workspace", "spts_linear_swiglu_workspace",
     "spts_ltp_structured_workspace", "spts_ltp_probe_structured",
+    "spts_ltp_gram_workspace", "spts_ltp_gram", "spts_ltp_probe_gram",
     "spts_decode_attention_workspace", "spts_decode_linear", "spts_decode_linear_rope", "spts_decode_swiglu",
     "spts_decode_attention", "spts_decode_step_workspace", "spts_decode_step",
     "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_score_topk_batched",
@@ -48,6 +49,9 @@ _SIGS = {
     "spts_probe_attention_workspace": (_SZ, [_I, _I, _I]),
     "spts_score_topk_workspace": (_SZ, [_I]),
     "spts_ltp_probe_workspace": (_SZ, [_I, _I, _I]),
+    "spts_ltp_gram_workspace": (_SZ, [_I, _I, _I]),
+    "spts_ltp_gram": (_I, [_P, _P, _I, _I, _P]),
+    "spts_ltp_probe_gram": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "spts_reduced_ffn_workspace": (_SZ, [_I, _I, _I]),
     "spts_msdp_stage_workspace": (_SZ, [_I]),
     "spts_linear_workspace": (_SZ, [_I, _I, _I]),
@@ -308,6 +312,34 @@ def spts_ltp_probe(z, u_t, v_t, score=None):
     bf = torch.bfloat16
     _check(ctx, lib().spts_ltp_probe(h, _ptr(z, bf, "z"), _ptr(u_t, bf, "u_t"), _ptr(v_t, bf, "v_t"), n, d, r,
                                      _ptr(score, torch.float32, "score")), "spts_ltp_probe")
+    return score
+
+
+def spts_ltp_gram(v_t, gram=None):
+    """Offline Gram operand of the proxy's second factor: v_t [d, r] ->
+    gram [r, 3r] bf16, rows [hi(G) | hi(G) | lo(G)] of G = V V^T."""
+    d, r = v_t.shape
+    if gram is None:
+        gram = torch.empty(r, 3 * r, dtype=torch.bfloat16, device=v_t.device)
+    ctx = context()
+    h = ctx.bind(0, v_t.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_ltp_gram(h, _ptr(v_t, bf, "v_t"), d, r, _ptr(gram, bf, "gram")), "spts_ltp_gram")
+    return gram
+
+
+def spts_ltp_probe_gram(z, u_t, gram, score=None):
+    """LTP score ||(z U) V|| per row as sqrt(t G t^T), t = z U, with the gram
+    operand from spts_ltp_gram."""
+    n, d = z.shape
+    r = u_t.shape[0]
+    if score is None:
+        score = torch.empty(n, dtype=torch.float32, device=z.device)
+    ctx = context()
+    h = ctx.bind(lib().spts_ltp_gram_workspace(n, d, r), z.device)
+    bf = torch.bfloat16
+    _check(ctx, lib().spts_ltp_probe_gram(h, _ptr(z, bf, "z"), _ptr(u_t, bf, "u_t"), _ptr(gram, bf, "gram"), n, d,
+                                          r, _ptr(score, torch.float32, "score")), "spts_ltp_probe_gram")
     return score
 
 

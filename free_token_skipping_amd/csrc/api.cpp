@@ -135,6 +135,13 @@ size_t spts_ltp_probe_workspace(int n, int d, int r) {
   const size_t part = round256((size_t)n * (d / 256) * 4);        // row sums of squares
   return t2 + part + gemm_split_workspace(n, d, r, EPI_SPLIT);    // split-K partials of z U
 }
+// T3 [n, 3r] = [hi | lo | hi] of z U | partial quadratic forms [n, (r/256) * k-slices] | split-K partials
+size_t spts_ltp_gram_workspace(int n, int d, int r) {
+  if (n <= 0 || d <= 0 || r <= 0) return 0;
+  const size_t t3 = round256((size_t)n * 3 * r * 2);
+  const size_t part = round256((size_t)n * (r / 256) * gemm_quad_ksplit(n, 3 * r, r) * 4);
+  return t3 + part + gemm_split_workspace(n, d, r, EPI_SPLIT);
+}
 // T2 [n, 4r] | H2 [n, 2 d_low] | Td2 [n, 2r] (bf16 hi/lo pairs) | row sums [n, d/256] | split-K partials
 static void ltp_structured_layout(int n, int d, int r, int d_low, size_t off[5]) {
   off[0] = 0;
@@ -498,6 +505,60 @@ spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const 
   e = launch_gemm(g2, EPI_SUMSQ, ctx->stream);
   if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe (T V)");
   return hip_status(ctx, launch_rowsum_sqrt(part, n, d / 256, score, ctx->stream), "ltp_probe (norm)");
+}
+
+spts_status spts_ltp_gram(spts_ctx* ctx, const void* v_t, int d, int r, void* gram) {
+  CHECK_CTX();
+  REQUIRE(d > 0 && r > 0, SPTS_ERR_SHAPE, "bad LTP Gram sizes");
+  REQUIRE(r % 256 == 0 && d <= 65536, SPTS_ERR_UNSUPPORTED, "LTP Gram needs r %% 256 == 0 and d <= 65536");
+  {
+    const spts_status st = weight_size_ok(ctx, d, r);
+    if (st != SPTS_OK) return st;
+  }
+  REQUIRE_PTR(v_t); REQUIRE_PTR(gram);
+  REQUIRE_ALIGN(v_t); REQUIRE_ALIGN(gram);
+  return hip_status(ctx, launch_ltp_gram(reinterpret_cast<const uint16_t*>(v_t), d, r,
+                                         reinterpret_cast<uint16_t*>(gram), ctx->stream), "ltp_gram");
+}
+
+spts_status spts_ltp_probe_gram(spts_ctx* ctx, const void* z, const void* u_t, const void* gram, int n, int d,
+                                int r, float* score) {
+  CHECK_CTX();
+  REQUIRE(n >= 0 && d > 0 && r > 0, SPTS_ERR_SHAPE, "bad LTP sizes");
+  REQUIRE(d % 256 == 0 && r % 256 == 0, SPTS_ERR_UNSUPPORTED, "LTP needs d %% 256 == 0 and r %% 256 == 0");
+  {
+    spts_status st = weight_size_ok(ctx, r, d);
+    if (st == SPTS_OK) st = weight_size_ok(ctx, r, 3L * r);
+    if (st != SPTS_OK) return st;
+  }
+  if (n == 0) return SPTS_OK;
+  REQUIRE_PTR(z); REQUIRE_PTR(u_t); REQUIRE_PTR(gram); REQUIRE_PTR(score);
+  REQUIRE_ALIGN(z); REQUIRE_ALIGN(u_t); REQUIRE_ALIGN(gram); REQUIRE_ALIGN(score);
+  const size_t need = spts_ltp_gram_workspace(n, d, r);
+  REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
+  const int ks = gemm_quad_ksplit(n, 3 * r, r);
+  uint16_t* t3 = reinterpret_cast<uint16_t*>(ctx->ws);
+  const size_t t3_bytes = round256((size_t)n * 3 * r * 2);
+  const size_t part_bytes = round256((size_t)n * (r / 256) * ks * 4);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + t3_bytes);
+  float* split_ws = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + t3_bytes + part_bytes);
+  // T = z U as bf16 [hi | lo | hi] [n, 3r]
+  GemmArgs g1{};
+  g1.a = reinterpret_cast<const uint16_t*>(z); g1.m = n; g1.k = d; g1.lda = d;
+  g1.b0 = reinterpret_cast<const uint16_t*>(u_t); g1.ldb = d; g1.n = r;
+  g1.out = t3; g1.ldc = 3 * r; g1.split3 = 1;
+  g1.partial = split_ws; g1.partial_bytes = ctx->ws_bytes - t3_bytes - part_bytes;
+  hipError_t e = launch_gemm(g1, EPI_SPLIT, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_gram (z U)");
+  // Y = [hi|lo|hi](T) [hi|hi|lo](G)^T = T G less lo(T) lo(G); each k-slice
+  // adds its part of sum_c Y[m, c] T[m, c] per row
+  GemmArgs g2{};
+  g2.a = t3; g2.m = n; g2.k = 3 * r; g2.lda = 3 * r;
+  g2.b0 = reinterpret_cast<const uint16_t*>(gram); g2.ldb = 3 * r; g2.n = r;
+  g2.out = part;
+  e = launch_gemm(g2, EPI_QUAD, ctx->stream);
+  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_gram (T G T^T)");
+  return hip_status(ctx, launch_rowsum_sqrt(part, n, (r / 256) * ks, score, ctx->stream), "ltp_probe_gram (norm)");
 }
 
 spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* a_gu_t, const void* b_gate,

@@ -95,6 +95,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x4 (&acc)[4][8]
         wl[0] = pack2bf(lo[0], lo[1]); wl[1] = pack2bf(lo[2], lo[3]);
         *reinterpret_cast<u32x2*>(out + col) = wh;
         *reinterpret_cast<u32x2*>(out + g.n + col) = wl;
+        if (g.split3) *reinterpret_cast<u32x2*>(out + 2 * g.n + col) = wh;
       }
       continue;
     }
@@ -179,7 +180,7 @@ void gemm_tn_kernel(GemmArgs g) {
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT);
   constexpr bool kTail = (EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_KV || EPI == EPI_SWIGLU);
   const int tiles_n = kSwiglu ? (g.n / 2) / 128 : g.n / BN;
-  const int ksplit = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
+  const int ksplit = (EPI == EPI_PARTIAL || EPI == EPI_QUAD) ? g.ksplit : 1;
   const int b = (int)blockIdx.x;
   int logical, kslice = 0, k0, k1;
   int slot = -1, step = 0;             // tail piece slot; ends workgroups: tail tiles between jobs
@@ -429,6 +430,49 @@ void gemm_tn_kernel(GemmArgs g) {
       }
       return;
     }
+    if (EPI == EPI_QUAD) {
+      // this k-slice's row sums of C[i, c] * t[i, c] over the tile's 256
+      // columns, t = hi + lo read from A's columns c and n + c (exact in
+      // fp32): a lane's 32 columns, then the 4 lanes of the row (q4), then
+      // the two column waves (LDS)
+      float* red = reinterpret_cast<float*>(smem);   // [4 wm][4 i][16 rows] from wn == 1
+      float ss[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int row = tile_m * BM + wm * 64 + i * 16 + r16;
+        row = row < g.m ? row : g.m - 1;             // rows past m: summed, never stored
+        const uint16_t* trow = g.a + (size_t)row * g.lda;
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = tile_n * BN + wn * 128 + j * 16 + q4 * 4;
+          const u32x2 th = *reinterpret_cast<const u32x2*>(trow + col);
+          const u32x2 tl = *reinterpret_cast<const u32x2*>(trow + g.n + col);
+          t += acc[i][j][0] * (lo_bf(th[0]) + lo_bf(tl[0]));
+          t += acc[i][j][1] * (hi_bf(th[0]) + hi_bf(tl[0]));
+          t += acc[i][j][2] * (lo_bf(th[1]) + lo_bf(tl[1]));
+          t += acc[i][j][3] * (hi_bf(th[1]) + hi_bf(tl[1]));
+        }
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        ss[i] = t;
+      }
+      if (wn == 1 && q4 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(wm * 4 + i) * 16 + r16] = ss[i];
+      }
+      __syncthreads();
+      if (wn == 0 && q4 == 0) {
+        float* out = reinterpret_cast<float*>(g.out);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = tile_m * BM + wm * 64 + i * 16 + r16;
+          if (row < g.m)
+            out[((long)row * tiles_n + tile_n) * ksplit + kslice] = ss[i] + red[(wm * 4 + i) * 16 + r16];
+        }
+      }
+      return;
+    }
     if (EPI == EPI_SUMSQ) {
       // row sums of squares over the tile's 256 columns: a lane's 32 columns,
       // then the 4 lanes of the row (q4), then the two column waves (LDS)
@@ -545,6 +589,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
       wl[0] = pack2bf(lo[0], lo[1]); wl[1] = pack2bf(lo[2], lo[3]);
       *reinterpret_cast<u32x2*>(out + col) = wh;
       *reinterpret_cast<u32x2*>(out + g.n + col) = wl;
+      if (g.split3) *reinterpret_cast<u32x2*>(out + 2 * g.n + col) = wh;
     } else {   // EPI_STORE
       const int orow = g.out_rows ? g.out_rows[row] : row;
       uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)orow * g.ldc;
@@ -581,7 +626,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_devices.fetch_or(bit, std::memory_order_release);
   }
-  const int ks = (EPI == EPI_PARTIAL) ? g.ksplit : 1;
+  const int ks = (EPI == EPI_PARTIAL || EPI == EPI_QUAD) ? g.ksplit : 1;
   int grid = ((tiles_m * tiles_n * ks + 7) / 8) * 8;           // a multiple of the 8 XCDs
   if (g.tail_tiles > 0) {
     const int units = g.tail_ends ? g.tail_tiles + (g.tail_tiles + g.tail_ends - 1) / g.tail_ends
@@ -664,6 +709,21 @@ Plan choose_plan(int m, int k, int n, int epi) {
 
 int gemm_ksplit(int m, int k, int n, int epi) { return choose_plan(m, k, n, epi).ksplit; }
 
+// EPI_QUAD: the smallest k-split that gives every CU a workgroup, keeping at
+// least two k-steps per slice (the row sums are linear in C, so each slice
+// finishes its own part and no fp32 tile goes through memory).
+int gemm_quad_ksplit(int m, int k, int n) {
+  const int tiles = ((m + BM - 1) / BM) * (n / BN);
+  const int KT = k / BK;
+  int best = 1;
+  for (int ks = 1; ks <= KT / 2; ++ks) {
+    if (KT % ks != 0) continue;
+    best = ks;
+    if ((long)tiles * ks >= kCUs) break;
+  }
+  return best;
+}
+
 size_t gemm_split_workspace(int m, int k, int n, int epi) { return choose_plan(m, k, n, epi).ws; }
 
 hipError_t launch_gemm(const GemmArgs& g0, int epi, hipStream_t s) {
@@ -676,6 +736,10 @@ hipError_t launch_gemm(const GemmArgs& g0, int epi, hipStream_t s) {
   if (room && plan.tiles > 0) {
     g.tail_full = plan.full; g.tail_tiles = plan.tiles; g.tail_np = plan.np;
     g.tail_ends = plan.ends; g.tail_kx = plan.kx;
+  }
+  if (epi == EPI_QUAD) {
+    g.ksplit = gemm_quad_ksplit(g.m, g.k, g.n);
+    return launch_one<EPI_QUAD, false>(g, s);
   }
   if (room && plan.ksplit > 1) {
     g.ksplit = plan.ksplit;

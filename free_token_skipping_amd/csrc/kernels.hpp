@@ -21,6 +21,9 @@ enum GemmEpilogue : int {
                    // the rest from b1 into out2 (ldc2 columns), both bf16
   EPI_SWIGLU_SPLIT = 7,  // as SWIGLU, the fp32 result h written as bf16 pair: hi = bf16(h)
                          // at column c, lo = bf16(h - hi) at column f + c (f = n / 2)
+  EPI_QUAD = 8,    // fp32 out[(i * tiles_n + tile_n) * ksplit + kslice] = sum over the tile's
+                   // columns c of C[i, c] * (A[i, c] + A[i, n + c]) for this k-slice's part of C
+                   // (A holds a bf16 hi/lo pair per column; no gather, no tail split)
 };
 
 struct GemmArgs {
@@ -51,6 +54,7 @@ struct GemmArgs {
   // a head [0, tail_kx) per workgroup, and each remaining workgroup takes the
   // ends [tail_kx, KT) of up to tail_ends tiles.
   int tail_full, tail_tiles, tail_np, tail_ends, tail_kx;
+  int split3;               // EPI_SPLIT: also write the hi half again at column 2n + c
 };
 
 // Split count the launcher would use for this problem (1 = no split) and the
@@ -58,6 +62,8 @@ struct GemmArgs {
 // launcher picks; 0 when it runs the problem unsplit).
 int gemm_ksplit(int m, int k, int n, int epilogue);
 size_t gemm_split_workspace(int m, int k, int n, int epilogue);
+// k-slices of an EPI_QUAD launch: each writes its own partial row sums
+int gemm_quad_ksplit(int m, int k, int n);
 hipError_t launch_gemm(const GemmArgs& g, int epilogue, hipStream_t s);
 
 // ------------------------------------------------------------ attention
@@ -123,5 +129,9 @@ hipError_t launch_scatter_add_i32(const int32_t* src, const int32_t* idx, int k,
 hipError_t launch_rmsnorm(const uint16_t* x, int n, int d, float eps, uint16_t* out, hipStream_t s);
 hipError_t launch_rope_table(int max_pos, int dh, double theta, float* table, hipStream_t s);
 hipError_t launch_rowsum_sqrt(const float* partial, int n, int parts, float* out, hipStream_t s);
+// Gram operand of the LTP proxy's second factor: G = V V^T (r x r) from
+// v_t = V^T [d, r] bf16, accumulated in fp64, written as bf16 rows
+// [hi(G) | hi(G) | lo(G)] of width 3r (gcat [r, 3r])
+hipError_t launch_ltp_gram(const uint16_t* v_t, int d, int r, uint16_t* gcat, hipStream_t s);
 
 }  // namespace spts

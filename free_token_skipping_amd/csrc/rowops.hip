@@ -135,7 +135,29 @@ __global__ void rowsum_sqrt_kernel(const float* __restrict__ partial, int n, int
   if (i >= n) return;
   float t = 0.f;
   for (int b = 0; b < parts; ++b) t += partial[(long)i * parts + b];
-  out[i] = sqrtf(t);
+  // a quadratic form with a positive semi-definite matrix can round to just
+  // below zero when its value is ~0; NaN stays NaN
+  out[i] = sqrtf(t < 0.f ? 0.f : t);
+}
+
+// G = V V^T for v_t = V^T [d, r]: workgroup i computes row i, threads stride
+// over the columns j (coalesced loads of v_t's rows, the column-i element is
+// a broadcast).  Products of bf16 values are exact in fp64 and the sum runs in
+// k order in fp64, so G is symmetric bit for bit.  Row i of gcat is
+// [hi | hi | lo] with hi = bf16(G[i, :]) and lo = bf16(G[i, :] - hi).
+__global__ void ltp_gram_kernel(const uint16_t* __restrict__ v_t, int d, int r, uint16_t* __restrict__ gcat) {
+  const int i = blockIdx.x;
+  for (int j = threadIdx.x; j < r; j += blockDim.x) {
+    double acc = 0.0;
+    for (int k = 0; k < d; ++k)
+      acc = fma((double)bf2f(v_t[(long)k * r + i]), (double)bf2f(v_t[(long)k * r + j]), acc);
+    const uint16_t hi = f2bf((float)acc);
+    const uint16_t lo = f2bf((float)(acc - (double)bf2f(hi)));
+    uint16_t* row = gcat + (long)i * 3 * r;
+    row[j] = hi;
+    row[r + j] = hi;
+    row[2 * r + j] = lo;
+  }
 }
 
 inline dim3 grid_for(long work, int tpb = 256) {
@@ -208,6 +230,11 @@ hipError_t launch_rope_table(int max_pos, int dh, double theta, float* table, hi
 
 hipError_t launch_rowsum_sqrt(const float* partial, int n, int parts, float* out, hipStream_t s) {
   hipLaunchKernelGGL(rowsum_sqrt_kernel, dim3((n + 255) / 256), dim3(256), 0, s, partial, n, parts, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ltp_gram(const uint16_t* v_t, int d, int r, uint16_t* gcat, hipStream_t s) {
+  hipLaunchKernelGGL(ltp_gram_kernel, dim3(r), dim3(256), 0, s, v_t, d, r, gcat);
   return hipGetLastError();
 }
 

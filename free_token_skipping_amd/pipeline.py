@@ -101,9 +101,23 @@ class LayerConfig:
     w_fuse: Tuple[float, float] = (0.5, 0.5)
     fusion: str = "maxnorm_add"           # FFN score fusion: "maxnorm_add" or "multiply"
     proxy: str = "linear"                 # LTP proxy: "linear" (u_t, v_t) or "structured" (proxy_packed)
+    ltp_form: str = "gram"                # linear proxy score: "gram" (sqrt(t G t^T)) or "direct" (||t V||)
     prenorm: bool = False
     eps: float = 1e-5
     theta: Optional[float] = None         # None: no rotary embedding
+
+
+def ltp_gram(w):
+    """Gram operand of the linear proxy in weights dict w (spts_ltp_gram),
+    prepared on first use and kept in w; prepared again when v_t is replaced
+    or written in place (its version counter moves)."""
+    v = w["v_t"]
+    key = (v.data_ptr(), v._version, tuple(v.shape))
+    cached = w.get("_ltp_gram")
+    if cached is None or cached[0] != key:
+        cached = (key, capi.spts_ltp_gram(v))
+        w["_ltp_gram"] = cached
+    return cached[1]
 
 
 def _attn_flops(idx, Hq, dh):
@@ -222,6 +236,11 @@ def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None, tm=NO_TIMER):
         r, d_low = pk["c_t"].shape
         with tm("ltp_probe", 2.0 * n * 3 * r * (d + d_low)):
             L = capi.spts_ltp_probe_structured(z, pk)
+    elif cfg.ltp_form == "gram":
+        r = w["u_t"].shape[0]
+        gram = ltp_gram(w)                  # offline: once per proxy
+        with tm("ltp_probe", 2.0 * n * r * (d + r)):
+            L = capi.spts_ltp_probe_gram(z, w["u_t"], gram)
     else:
         r = w["u_t"].shape[0]
         with tm("ltp_probe", 4.0 * n * d * r):

@@ -80,6 +80,7 @@ size_t spts_probe_attention_workspace(int n, int P, int Hq);
 size_t spts_score_topk_workspace(int n);
 size_t spts_ltp_probe_workspace(int n, int d, int r);
 size_t spts_ltp_structured_workspace(int n, int d, int r, int d_low);
+size_t spts_ltp_gram_workspace(int n, int d, int r);
 size_t spts_decode_attention_workspace(int L, int Hq);
 size_t spts_decode_step_workspace(int max_len, int Hq, int f);
 size_t spts_reduced_ffn_workspace(int k, int d, int f);
@@ -202,6 +203,28 @@ spts_status spts_reduced_attention(spts_ctx* ctx, spts_dtype dtype, const void* 
  * Requires d % 256 == 0, r % 256 == 0.  Workspace: spts_ltp_probe_workspace. */
 spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const void* v_t,
                            int n, int d, int r, float* score);
+
+/* The same score through the Gram matrix of the proxy's second factor:
+ *     score[m]^2 = t G t^T,   t = z[m,:] U (1 x r),   G = V V^T (r x r),
+ * which equals ||t V||^2 exactly, so the (n x r) x (r x d) product becomes an
+ * (n x r) x (r x r) one.  G depends only on the proxy, which the method builds
+ * offline ([SPTS] abstract, Fig. 2(b)), so it is prepared once per proxy by
+ * spts_ltp_gram and passed in here.  t is kept near fp32 precision (two bf16
+ * terms); G as two bf16 terms (hi, lo); the product t G drops only the
+ * lo(t) lo(G) term (~2^-18 relative).  For a positive semi-definite G that
+ * rounds to a value just below 0 the score is 0.
+ *   z [n, d] bf16, u_t [r, d] bf16, gram [r, 3r] bf16 from spts_ltp_gram,
+ *   score [n] float32.
+ * Requires d % 256 == 0, r % 256 == 0.  Workspace: spts_ltp_gram_workspace. */
+spts_status spts_ltp_probe_gram(spts_ctx* ctx, const void* z, const void* u_t, const void* gram,
+                                int n, int d, int r, float* score);
+
+/* Offline preparation for spts_ltp_probe_gram: G = V V^T from v_t = V^T
+ * [d, r] bf16, accumulated in fp64 (G is symmetric bit for bit), written to
+ * gram [r, 3r] bf16 as rows [hi(G) | hi(G) | lo(G)], hi = bf16(G),
+ * lo = bf16(G - hi).  The buffer belongs to the caller and stays valid while
+ * v_t is unchanged.  Requires r % 256 == 0 and 0 < d <= 65536.  No workspace. */
+spts_status spts_ltp_gram(spts_ctx* ctx, const void* v_t, int d, int r, void* gram);
 
 /* The structured proxy form of [SPTS] Table A: the feed-forward restricted to
  * d_low of its hidden channels, each projection factored at rank r

@@ -434,6 +434,81 @@ def test_ltp_full_size_sampled(n):
     assert (np.abs(got - ref) / ref).max() < 2e-5
 
 
+def test_ltp_gram_operand():
+    """spts_ltp_gram: rows [hi | hi | lo] of G = V V^T, hi + lo within the
+    two-term bf16 bound of G, G symmetric bit for bit."""
+    d, r = 4096, 256
+    v_t = W.randn((d, r), seed=41, std=0.06)
+    g = capi.spts_ltp_gram(_cuda(v_t))
+    torch.cuda.synchronize()
+    gb = g.cpu()
+    hi = gb[:, :r].float().numpy().astype(np.float64)
+    assert torch.equal(gb[:, :r], gb[:, r:2 * r])
+    lo = gb[:, 2 * r:].float().numpy().astype(np.float64)
+    v = W.as_f64(v_t)
+    ref = v.T @ v
+    assert np.array_equal(hi, hi.T) and np.array_equal(lo, lo.T)
+    scale = np.abs(ref).max()
+    assert np.abs(hi + lo - ref).max() <= 2.0 ** -16 * scale
+    assert np.all(np.abs(lo) <= 2.0 ** -8 * np.abs(hi) + 1e-30)
+
+
+@pytest.mark.parametrize("n,d,r", [(1000, 512, 256), (300, 1024, 512), (1, 512, 256), (257, 768, 256)])
+def test_ltp_probe_gram(n, d, r):
+    """sqrt(t G t^T) against the oracle's ||(z U) V|| (ragged row tails, one
+    row, two 256-column tiles of G at r = 512)."""
+    _log(f"ltp gram n={n} d={d} r={r}")
+    z = W.randn((n, d), seed=36)
+    m = np.random.default_rng(37).standard_normal((d, d)) * 0.02
+    u_t, v_t = W.proxy_factors(m, r)
+    u_t, v_t = W.to_bf16(u_t), W.to_bf16(v_t)
+    gram = capi.spts_ltp_gram(_cuda(v_t))
+    L = capi.spts_ltp_probe_gram(_cuda(z), _cuda(u_t), gram)
+    ref = ltp.ltp_scores(W.as_f64(z), W.as_f64(u_t), W.as_f64(v_t))
+    got = np64(L)
+    assert (np.abs(got - ref) / ref).max() < 2e-5
+
+
+def test_ltp_probe_gram_zero_rows():
+    """A zero row scores exactly 0 (no NaN from a form rounding below 0); an
+    empty input is a no-op."""
+    n, d, r = 600, 512, 256
+    z = W.randn((n, d), seed=42)
+    z[::7] = 0
+    u_t = W.randn((r, d), seed=43, std=0.3)
+    v_t = W.randn((d, r), seed=44, std=0.06)
+    gram = capi.spts_ltp_gram(_cuda(v_t))
+    got = np64(capi.spts_ltp_probe_gram(_cuda(z), _cuda(u_t), gram))
+    assert np.all(got[::7] == 0.0)
+    ref = ltp.ltp_scores(W.as_f64(z), W.as_f64(u_t), W.as_f64(v_t))
+    keep = np.ones(n, bool)
+    keep[::7] = False
+    assert (np.abs(got[keep] - ref[keep]) / ref[keep]).max() < 2e-5
+    e = capi.spts_ltp_probe_gram(_cuda(z[:0]), _cuda(u_t), gram)
+    assert e.shape == (0,)
+
+
+@pytest.mark.parametrize("n,factors", [(32768, "random"), (19661, "random"), (32768, "svd")])
+def test_ltp_gram_full_size_sampled(n, factors):
+    """The Gram form at the 32K input and the first MSDP stage, on random
+    factors (G far from diagonal) and on the truncated-SVD proxy."""
+    d, r = 4096, 256
+    _log(f"ltp gram full size n={n} {factors} (sampled rows)")
+    z = W.randn((n, d), seed=38)
+    if factors == "random":
+        u_t = W.randn((r, d), seed=39, std=0.3)
+        v_t = W.randn((d, r), seed=40, std=0.06)
+    else:
+        m = np.random.default_rng(45).standard_normal((d, d)) * 0.02
+        u_t, v_t = (W.to_bf16(a) for a in W.proxy_factors(m, r))
+    gram = capi.spts_ltp_gram(_cuda(v_t))
+    L = capi.spts_ltp_probe_gram(_cuda(z), _cuda(u_t), gram)
+    pick = np.concatenate([np.random.default_rng(3).choice(n, 256, replace=False), [0, n - 1]])
+    ref = ltp.ltp_scores(W.as_f64(z[pick]), W.as_f64(u_t), W.as_f64(v_t))
+    got = np64(L)[pick]
+    assert (np.abs(got - ref) / ref).max() < 2e-5
+
+
 def _structured_case(n, d, f, d_low, r, seed):
     z = W.randn((n, d), seed=seed)
     wg = W.randn((f, d), seed=seed + 1, std=0.05)
