@@ -26,7 +26,7 @@ EXPORTS = [
     "spts_reduced_ffn_workspace", "spts_msdp_stage_workspace", "spts_linear_workspace",
     "spts_linear_kv_workspace", "spts_linear_swiglu_workspace",
     "spts_ltp_structured_workspace", "spts_ltp_probe_structured",
-    "spts_ltp_gram_workspace", "spts_ltp_gram", "spts_ltp_probe_gram",
+    "spts_ltp_gram_workspace", "spts_ltp_gram", "spts_ltp_probe_gram", "spts_ltp_probe_structured_gram",
     "spts_decode_attention_workspace", "spts_decode_linear", "spts_decode_linear_rope", "spts_decode_swiglu",
     "spts_decode_attention", "spts_decode_step_workspace", "spts_decode_step",
     "spts_probe_attention", "spts_score_topk", "spts_score_topk_multiply", "spts_score_topk_batched",
@@ -66,6 +66,7 @@ _SIGS = {
     "spts_decode_step_workspace": (_SZ, [_I, _I, _I]),
     "spts_decode_step": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _I, _F]),
     "spts_ltp_probe_structured": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "spts_ltp_probe_structured_gram": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "spts_probe_attention": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "spts_score_topk": (_I, [_P, _P, _P, _F, _F, _I, _I, _I, _P, _P]),
     "spts_score_topk_multiply": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
@@ -355,8 +356,10 @@ def pack_structured_proxy(a_g_t, b_g_t, a_u_t, b_u_t, c_t, d_t):
             "c_t": c_t.contiguous(), "d_t": d_t.contiguous()}
 
 
-def spts_ltp_probe_structured(z, packed, score=None):
-    """Structured LTP score ||(silu((zA_g)B_g) * ((zA_u)B_u)) C D|| per row."""
+def spts_ltp_probe_structured(z, packed, score=None, gram=None):
+    """Structured LTP score ||(silu((zA_g)B_g) * ((zA_u)B_u)) C D|| per row;
+    with gram (spts_ltp_gram of packed["d_t"]) the last factor enters through
+    its Gram matrix (spts_ltp_probe_structured_gram)."""
     n, d = z.shape
     r = packed["c_t"].shape[0]
     d_low = packed["c_t"].shape[1]
@@ -365,11 +368,12 @@ def spts_ltp_probe_structured(z, packed, score=None):
     ctx = context()
     h = ctx.bind(lib().spts_ltp_structured_workspace(n, d, r, d_low), z.device)
     bf = torch.bfloat16
-    _check(ctx, lib().spts_ltp_probe_structured(h, _ptr(z, bf, "z"), _ptr(packed["a_gu_t"], bf, "a_gu_t"),
-                                                _ptr(packed["b_gate"], bf, "b_gate"), _ptr(packed["b_up"], bf, "b_up"),
-                                                _ptr(packed["c_t"], bf, "c_t"), _ptr(packed["d_t"], bf, "d_t"),
-                                                n, d, r, d_low, _ptr(score, torch.float32, "score")),
-           "spts_ltp_probe_structured")
+    fn, name = ((lib().spts_ltp_probe_structured_gram, "spts_ltp_probe_structured_gram") if gram is not None
+                else (lib().spts_ltp_probe_structured, "spts_ltp_probe_structured"))
+    last = _ptr(gram, bf, "gram") if gram is not None else _ptr(packed["d_t"], bf, "d_t")
+    _check(ctx, fn(h, _ptr(z, bf, "z"), _ptr(packed["a_gu_t"], bf, "a_gu_t"), _ptr(packed["b_gate"], bf, "b_gate"),
+                   _ptr(packed["b_up"], bf, "b_up"), _ptr(packed["c_t"], bf, "c_t"), last, n, d, r, d_low,
+                   _ptr(score, torch.float32, "score")), name)
     return score
 
 

@@ -135,28 +135,34 @@ size_t spts_ltp_probe_workspace(int n, int d, int r) {
   const size_t part = round256((size_t)n * (d / 256) * 4);        // row sums of squares
   return t2 + part + gemm_split_workspace(n, d, r, EPI_SPLIT);    // split-K partials of z U
 }
-// T3 [n, 3r] = [hi | lo | hi] of z U | partial quadratic forms [n, (r/256) * k-slices] | split-K partials
+// fp32 t in the QUAD lanes' order: rows padded to whole 256-row tiles
+static size_t tperm_bytes(int n, int r) { return round256((size_t)((n + 255) / 256) * 256 * r * 4); }
+// T3 [n, 3r] = [hi | lo | hi] of z U | t (quad_perm order) | partial quadratic
+// forms [n, (r/256) * k-slices] | split-K partials
 size_t spts_ltp_gram_workspace(int n, int d, int r) {
   if (n <= 0 || d <= 0 || r <= 0) return 0;
   const size_t t3 = round256((size_t)n * 3 * r * 2);
   const size_t part = round256((size_t)n * (r / 256) * gemm_quad_ksplit(n, 3 * r, r) * 4);
-  return t3 + part + gemm_split_workspace(n, d, r, EPI_SPLIT);
+  return t3 + tperm_bytes(n, r) + part + gemm_split_workspace(n, d, r, EPI_SPLIT);
 }
-// T2 [n, 4r] | H2 [n, 2 d_low] | Td2 [n, 2r] (bf16 hi/lo pairs) | row sums [n, d/256] | split-K partials
-static void ltp_structured_layout(int n, int d, int r, int d_low, size_t off[5]) {
+// T2 [n, 4r] | H2 [n, 2 d_low] | Td3 [n, 3r] (bf16 hi/lo pairs) | row sums | h C (quad_perm order) | split-K partials
+// (Td3 holds h C as [hi | lo | hi]; the direct form reads its first 2r columns.)
+static void ltp_structured_layout(int n, int d, int r, int d_low, size_t off[6]) {
+  const int parts_direct = d / 256, parts_gram = (r / 256) * gemm_quad_ksplit(n, 3 * r, r);
   off[0] = 0;
   off[1] = off[0] + round256((size_t)n * 4 * r * 2);
   off[2] = off[1] + round256((size_t)n * 2 * d_low * 2);
-  off[3] = off[2] + round256((size_t)n * 2 * r * 2);
-  off[4] = off[3] + round256((size_t)n * (d / 256) * 4);
+  off[3] = off[2] + round256((size_t)n * 3 * r * 2);
+  off[4] = off[3] + round256((size_t)n * (parts_direct > parts_gram ? parts_direct : parts_gram) * 4);
+  off[5] = off[4] + tperm_bytes(n, r);
 }
 size_t spts_ltp_structured_workspace(int n, int d, int r, int d_low) {
   if (n <= 0 || d <= 0 || r <= 0 || d_low <= 0) return 0;
-  size_t off[5];
+  size_t off[6];
   ltp_structured_layout(n, d, r, d_low, off);
   const size_t s1 = gemm_split_workspace(n, d, 2 * r, EPI_SPLIT);
   const size_t s3 = gemm_split_workspace(n, 2 * d_low, r, EPI_SPLIT);
-  return off[4] + (s1 > s3 ? s1 : s3);
+  return off[5] + (s1 > s3 ? s1 : s3);
 }
 size_t spts_linear_workspace(int m, int kdim, int n) {
   if (m <= 0 || kdim <= 0 || n <= 0) return 0;
@@ -537,17 +543,21 @@ spts_status spts_ltp_probe_gram(spts_ctx* ctx, const void* z, const void* u_t, c
   const size_t need = spts_ltp_gram_workspace(n, d, r);
   REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
   const int ks = gemm_quad_ksplit(n, 3 * r, r);
-  uint16_t* t3 = reinterpret_cast<uint16_t*>(ctx->ws);
+  char* ws = reinterpret_cast<char*>(ctx->ws);
+  uint16_t* t3 = reinterpret_cast<uint16_t*>(ws);
   const size_t t3_bytes = round256((size_t)n * 3 * r * 2);
+  float* tperm = reinterpret_cast<float*>(ws + t3_bytes);
+  const size_t tp_bytes = tperm_bytes(n, r);
   const size_t part_bytes = round256((size_t)n * (r / 256) * ks * 4);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + t3_bytes);
-  float* split_ws = reinterpret_cast<float*>(reinterpret_cast<char*>(ctx->ws) + t3_bytes + part_bytes);
+  float* part = reinterpret_cast<float*>(ws + t3_bytes + tp_bytes);
+  const size_t pre = t3_bytes + tp_bytes + part_bytes;
+  float* split_ws = reinterpret_cast<float*>(ws + pre);
   // T = z U as bf16 [hi | lo | hi] [n, 3r]
   GemmArgs g1{};
   g1.a = reinterpret_cast<const uint16_t*>(z); g1.m = n; g1.k = d; g1.lda = d;
   g1.b0 = reinterpret_cast<const uint16_t*>(u_t); g1.ldb = d; g1.n = r;
-  g1.out = t3; g1.ldc = 3 * r; g1.split3 = 1;
-  g1.partial = split_ws; g1.partial_bytes = ctx->ws_bytes - t3_bytes - part_bytes;
+  g1.out = t3; g1.ldc = 3 * r; g1.split3 = 1; g1.tperm = tperm;
+  g1.partial = split_ws; g1.partial_bytes = ctx->ws_bytes - pre;
   hipError_t e = launch_gemm(g1, EPI_SPLIT, ctx->stream);
   if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_gram (z U)");
   // Y = [hi|lo|hi](T) [hi|hi|lo](G)^T = T G less lo(T) lo(G); each k-slice
@@ -555,15 +565,18 @@ spts_status spts_ltp_probe_gram(spts_ctx* ctx, const void* z, const void* u_t, c
   GemmArgs g2{};
   g2.a = t3; g2.m = n; g2.k = 3 * r; g2.lda = 3 * r;
   g2.b0 = reinterpret_cast<const uint16_t*>(gram); g2.ldb = 3 * r; g2.n = r;
-  g2.out = part;
+  g2.out = part; g2.tperm = tperm;
   e = launch_gemm(g2, EPI_QUAD, ctx->stream);
   if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_gram (T G T^T)");
   return hip_status(ctx, launch_rowsum_sqrt(part, n, (r / 256) * ks, score, ctx->stream), "ltp_probe_gram (norm)");
 }
 
-spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* a_gu_t, const void* b_gate,
-                                      const void* b_up, const void* c_t, const void* d_t, int n, int d, int r,
-                                      int d_low, float* score) {
+// The structured proxy's score; the last factor D enters either directly
+// (last = d_t, the norm of (h C) D from row sums of squares) or through its
+// Gram operand (last = [hi | hi | lo](D D^T), the quadratic form of h C).
+static spts_status ltp_structured(spts_ctx* ctx, const void* z, const void* a_gu_t, const void* b_gate,
+                                  const void* b_up, const void* c_t, const void* last, bool gram, int n, int d,
+                                  int r, int d_low, float* score, const char* name) {
   CHECK_CTX();
   REQUIRE(n >= 0 && d > 0 && r > 0 && d_low > 0, SPTS_ERR_SHAPE, "bad structured LTP sizes");
   REQUIRE(d % 256 == 0 && r % 256 == 0 && d_low % 256 == 0, SPTS_ERR_UNSUPPORTED,
@@ -571,26 +584,27 @@ spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* 
   {
     spts_status st = weight_size_ok(ctx, 2L * r, d);
     if (st == SPTS_OK) st = weight_size_ok(ctx, d_low, 4L * r);
-    if (st == SPTS_OK) st = weight_size_ok(ctx, d, r);
+    if (st == SPTS_OK) st = gram ? weight_size_ok(ctx, r, 3L * r) : weight_size_ok(ctx, d, r);
     if (st == SPTS_OK) st = weight_size_ok(ctx, r, d_low);
     if (st != SPTS_OK) return st;
   }
   if (n == 0) return SPTS_OK;
   REQUIRE_PTR(z); REQUIRE_PTR(a_gu_t); REQUIRE_PTR(b_gate); REQUIRE_PTR(b_up); REQUIRE_PTR(c_t);
-  REQUIRE_PTR(d_t); REQUIRE_PTR(score);
+  REQUIRE_PTR(last); REQUIRE_PTR(score);
   REQUIRE_ALIGN(z); REQUIRE_ALIGN(a_gu_t); REQUIRE_ALIGN(b_gate); REQUIRE_ALIGN(b_up); REQUIRE_ALIGN(c_t);
-  REQUIRE_ALIGN(d_t); REQUIRE_ALIGN(score);
+  REQUIRE_ALIGN(last); REQUIRE_ALIGN(score);
   const size_t need = spts_ltp_structured_workspace(n, d, r, d_low);
   REQUIRE(ctx->ws_bytes >= need, SPTS_ERR_NOMEM, "workspace %zu < %zu bytes", ctx->ws_bytes, need);
-  size_t off[5];
+  size_t off[6];
   ltp_structured_layout(n, d, r, d_low, off);
   char* ws = reinterpret_cast<char*>(ctx->ws);
   uint16_t* t2 = reinterpret_cast<uint16_t*>(ws + off[0]);
   uint16_t* h2 = reinterpret_cast<uint16_t*>(ws + off[1]);
-  uint16_t* td2 = reinterpret_cast<uint16_t*>(ws + off[2]);
+  uint16_t* td3 = reinterpret_cast<uint16_t*>(ws + off[2]);
   float* part = reinterpret_cast<float*>(ws + off[3]);
-  float* split_ws = reinterpret_cast<float*>(ws + off[4]);
-  const size_t split_bytes = ctx->ws_bytes - off[4];
+  float* tperm = reinterpret_cast<float*>(ws + off[4]);
+  float* split_ws = reinterpret_cast<float*>(ws + off[5]);
+  const size_t split_bytes = ctx->ws_bytes - off[5];
   // [z A_g | z A_u] as hi/lo pairs: T2 row = [Tg_hi | Tu_hi | Tg_lo | Tu_lo]
   GemmArgs g1{};
   g1.a = reinterpret_cast<const uint16_t*>(z); g1.m = n; g1.k = d; g1.lda = d;
@@ -598,7 +612,7 @@ spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* 
   g1.out = t2; g1.ldc = 4 * r;
   g1.partial = split_ws; g1.partial_bytes = split_bytes;
   hipError_t e = launch_gemm(g1, EPI_SPLIT, ctx->stream);
-  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (z A)");
+  if (e != hipSuccess) return hip_status(ctx, e, name);
   // h = silu(T_g B_g) * (T_u B_u) over the hi/lo pairs (the packed B blocks pick
   // the gate or up columns of T2), written as hi/lo pairs
   GemmArgs g2{};
@@ -606,23 +620,45 @@ spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* 
   g2.b0 = reinterpret_cast<const uint16_t*>(b_gate); g2.b1 = reinterpret_cast<const uint16_t*>(b_up);
   g2.ldb = 4 * r; g2.n = 2 * d_low; g2.out = h2; g2.ldc = 2 * d_low;
   e = launch_gemm(g2, EPI_SWIGLU_SPLIT, ctx->stream);
-  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (swiglu)");
-  // h C over the hi/lo pairs (C's columns read modulo d_low), as hi/lo pairs
+  if (e != hipSuccess) return hip_status(ctx, e, name);
+  // h C over the hi/lo pairs (C's columns read modulo d_low), as [hi | lo | hi]
   GemmArgs g3{};
   g3.a = h2; g3.m = n; g3.k = 2 * d_low; g3.lda = 2 * d_low;
   g3.b0 = reinterpret_cast<const uint16_t*>(c_t); g3.ldb = d_low; g3.kwrap = d_low; g3.n = r;
-  g3.out = td2; g3.ldc = 2 * r;
+  g3.out = td3; g3.ldc = 3 * r; g3.split3 = 1; g3.tperm = gram ? tperm : nullptr;
   g3.partial = split_ws; g3.partial_bytes = split_bytes;
   e = launch_gemm(g3, EPI_SPLIT, ctx->stream);
-  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (h C)");
-  // ||(h C) D||: row sums of squares per 256 columns, then the root
+  if (e != hipSuccess) return hip_status(ctx, e, name);
   GemmArgs g4{};
-  g4.a = td2; g4.m = n; g4.k = 2 * r; g4.lda = 2 * r;
-  g4.b0 = reinterpret_cast<const uint16_t*>(d_t); g4.ldb = r; g4.kwrap = r; g4.n = d;
-  g4.out = part; g4.ldc = d / 256;
-  e = launch_gemm(g4, EPI_SUMSQ, ctx->stream);
-  if (e != hipSuccess) return hip_status(ctx, e, "ltp_probe_structured (T D)");
-  return hip_status(ctx, launch_rowsum_sqrt(part, n, d / 256, score, ctx->stream), "ltp_probe_structured (norm)");
+  g4.a = td3; g4.m = n; g4.lda = 3 * r; g4.out = part;
+  int parts;
+  if (gram) {
+    // (h C) G (h C)^T, G = D D^T: each k-slice adds its part per row
+    g4.k = 3 * r; g4.b0 = reinterpret_cast<const uint16_t*>(last); g4.ldb = 3 * r; g4.n = r; g4.tperm = tperm;
+    e = launch_gemm(g4, EPI_QUAD, ctx->stream);
+    parts = (r / 256) * gemm_quad_ksplit(n, 3 * r, r);
+  } else {
+    // ||(h C) D||: row sums of squares per 256 columns
+    g4.k = 2 * r; g4.b0 = reinterpret_cast<const uint16_t*>(last); g4.ldb = r; g4.kwrap = r; g4.n = d;
+    e = launch_gemm(g4, EPI_SUMSQ, ctx->stream);
+    parts = d / 256;
+  }
+  if (e != hipSuccess) return hip_status(ctx, e, name);
+  return hip_status(ctx, launch_rowsum_sqrt(part, n, parts, score, ctx->stream), name);
+}
+
+spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* a_gu_t, const void* b_gate,
+                                      const void* b_up, const void* c_t, const void* d_t, int n, int d, int r,
+                                      int d_low, float* score) {
+  return ltp_structured(ctx, z, a_gu_t, b_gate, b_up, c_t, d_t, false, n, d, r, d_low, score,
+                        "ltp_probe_structured");
+}
+
+spts_status spts_ltp_probe_structured_gram(spts_ctx* ctx, const void* z, const void* a_gu_t, const void* b_gate,
+                                           const void* b_up, const void* c_t, const void* gram, int n, int d,
+                                           int r, int d_low, float* score) {
+  return ltp_structured(ctx, z, a_gu_t, b_gate, b_up, c_t, gram, true, n, d, r, d_low, score,
+                        "ltp_probe_structured_gram");
 }
 
 // --------------------------------------------------------------------- decode

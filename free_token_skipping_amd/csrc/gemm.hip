@@ -96,6 +96,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x4 (&acc)[4][8]
         *reinterpret_cast<u32x2*>(out + col) = wh;
         *reinterpret_cast<u32x2*>(out + g.n + col) = wl;
         if (g.split3) *reinterpret_cast<u32x2*>(out + 2 * g.n + col) = wh;
+        if (g.tperm) *reinterpret_cast<f32x4*>(g.tperm + quad_perm(row, col, g.n)) = acc[i][j];
       }
       continue;
     }
@@ -432,26 +433,24 @@ void gemm_tn_kernel(GemmArgs g) {
     }
     if (EPI == EPI_QUAD) {
       // this k-slice's row sums of C[i, c] * t[i, c] over the tile's 256
-      // columns, t = hi + lo read from A's columns c and n + c (exact in
-      // fp32): a lane's 32 columns, then the 4 lanes of the row (q4), then
-      // the two column waves (LDS)
+      // columns, t in the lanes' own order (one coalesced 16-byte load per
+      // accumulator tile; the padding rows past m are summed, never stored):
+      // a lane's 32 columns, then the 4 lanes of the row (q4), then the two
+      // column waves (LDS)
       float* red = reinterpret_cast<float*>(smem);   // [4 wm][4 i][16 rows] from wn == 1
       float ss[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int row = tile_m * BM + wm * 64 + i * 16 + r16;
-        row = row < g.m ? row : g.m - 1;             // rows past m: summed, never stored
-        const uint16_t* trow = g.a + (size_t)row * g.lda;
+        const int row = tile_m * BM + wm * 64 + i * 16 + r16;
         float t = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int col = tile_n * BN + wn * 128 + j * 16 + q4 * 4;
-          const u32x2 th = *reinterpret_cast<const u32x2*>(trow + col);
-          const u32x2 tl = *reinterpret_cast<const u32x2*>(trow + g.n + col);
-          t += acc[i][j][0] * (lo_bf(th[0]) + lo_bf(tl[0]));
-          t += acc[i][j][1] * (hi_bf(th[0]) + hi_bf(tl[0]));
-          t += acc[i][j][2] * (lo_bf(th[1]) + lo_bf(tl[1]));
-          t += acc[i][j][3] * (hi_bf(th[1]) + hi_bf(tl[1]));
+          const f32x4 tv = *reinterpret_cast<const f32x4*>(g.tperm + quad_perm(row, col, g.n));
+          t += acc[i][j][0] * tv[0];
+          t += acc[i][j][1] * tv[1];
+          t += acc[i][j][2] * tv[2];
+          t += acc[i][j][3] * tv[3];
         }
         t += __shfl_xor(t, 16);
         t += __shfl_xor(t, 32);
@@ -590,6 +589,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
       *reinterpret_cast<u32x2*>(out + col) = wh;
       *reinterpret_cast<u32x2*>(out + g.n + col) = wl;
       if (g.split3) *reinterpret_cast<u32x2*>(out + 2 * g.n + col) = wh;
+      if (g.tperm) *reinterpret_cast<f32x4*>(g.tperm + quad_perm(row, col, g.n)) = a;
     } else {   // EPI_STORE
       const int orow = g.out_rows ? g.out_rows[row] : row;
       uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (long)orow * g.ldc;
@@ -709,17 +709,22 @@ Plan choose_plan(int m, int k, int n, int epi) {
 
 int gemm_ksplit(int m, int k, int n, int epi) { return choose_plan(m, k, n, epi).ksplit; }
 
-// EPI_QUAD: the smallest k-split that gives every CU a workgroup, keeping at
-// least two k-steps per slice (the row sums are linear in C, so each slice
-// finishes its own part and no fp32 tile goes through memory).
+// EPI_QUAD: the k-split (a divisor of the k-steps, at least two per slice)
+// with the fewest rounds of workgroups times k-steps per slice, the smaller
+// split on a tie.  The row sums are linear in C, so each slice finishes its
+// own part and no fp32 tile goes through memory.
 int gemm_quad_ksplit(int m, int k, int n) {
-  const int tiles = ((m + BM - 1) / BM) * (n / BN);
+  const long tiles = (long)((m + BM - 1) / BM) * (n / BN);
   const int KT = k / BK;
   int best = 1;
-  for (int ks = 1; ks <= KT / 2; ++ks) {
+  long best_cost = -1;
+  for (int ks = 1; ks <= (KT >= 2 ? KT / 2 : 1); ++ks) {
     if (KT % ks != 0) continue;
-    best = ks;
-    if ((long)tiles * ks >= kCUs) break;
+    const long cost = ((tiles * ks + kCUs - 1) / kCUs) * (KT / ks);
+    if (best_cost < 0 || cost < best_cost) {
+      best = ks;
+      best_cost = cost;
+    }
   }
   return best;
 }

@@ -22,8 +22,8 @@ enum GemmEpilogue : int {
   EPI_SWIGLU_SPLIT = 7,  // as SWIGLU, the fp32 result h written as bf16 pair: hi = bf16(h)
                          // at column c, lo = bf16(h - hi) at column f + c (f = n / 2)
   EPI_QUAD = 8,    // fp32 out[(i * tiles_n + tile_n) * ksplit + kslice] = sum over the tile's
-                   // columns c of C[i, c] * (A[i, c] + A[i, n + c]) for this k-slice's part of C
-                   // (A holds a bf16 hi/lo pair per column; no gather, no tail split)
+                   // columns c of C[i, c] * t[i, c] for this k-slice's part of C, t read from
+                   // tperm in the lane order of quad_perm (no gather, no tail split)
 };
 
 struct GemmArgs {
@@ -55,7 +55,21 @@ struct GemmArgs {
   // ends [tail_kx, KT) of up to tail_ends tiles.
   int tail_full, tail_tiles, tail_np, tail_ends, tail_kx;
   int split3;               // EPI_SPLIT: also write the hi half again at column 2n + c
+  float* tperm;             // EPI_SPLIT: if set, also the fp32 result in quad_perm order;
+                            // EPI_QUAD: the row factors t, in that order
 };
+
+// Offset (floats) of element (row, col) of an [m, n] fp32 matrix stored in the
+// register order of a 256 x 256 GEMM tile: tile (row / 256, col / 256), then
+// wave row block, 16-row group, wave column block, 16-column group, lane
+// (16 * column quad + row within the group), element.  One 16-byte load per
+// lane and accumulator tile reads a contiguous KiB per wave.  Rows are padded
+// to a multiple of 256: the buffer holds ceil(m / 256) * 256 * n floats.
+__host__ __device__ inline long quad_perm(int row, int col, int n) {
+  const int tm = row >> 8, rr = row & 255, tn = col >> 8, cc = col & 255;
+  const long blk = ((((long)tm * (n >> 8) + tn) * 4 + (rr >> 6)) * 4 + ((rr >> 4) & 3)) * 2 + (cc >> 7);
+  return ((blk * 8 + ((cc >> 4) & 7)) * 64 + (((cc >> 2) & 3) * 16 + (rr & 15))) * 4 + (cc & 3);
+}
 
 // Split count the launcher would use for this problem (1 = no split) and the
 // workspace it then needs (split-K slices or tail pieces, whichever the

@@ -140,24 +140,43 @@ __global__ void rowsum_sqrt_kernel(const float* __restrict__ partial, int n, int
   out[i] = sqrtf(t < 0.f ? 0.f : t);
 }
 
-// G = V V^T for v_t = V^T [d, r]: workgroup i computes row i, threads stride
-// over the columns j (coalesced loads of v_t's rows, the column-i element is
-// a broadcast).  Products of bf16 values are exact in fp64 and the sum runs in
-// k order in fp64, so G is symmetric bit for bit.  Row i of gcat is
-// [hi | hi | lo] with hi = bf16(G[i, :]) and lo = bf16(G[i, :] - hi).
-__global__ void ltp_gram_kernel(const uint16_t* __restrict__ v_t, int d, int r, uint16_t* __restrict__ gcat) {
-  const int i = blockIdx.x;
-  for (int j = threadIdx.x; j < r; j += blockDim.x) {
-    double acc = 0.0;
-    for (int k = 0; k < d; ++k)
-      acc = fma((double)bf2f(v_t[(long)k * r + i]), (double)bf2f(v_t[(long)k * r + j]), acc);
-    const uint16_t hi = f2bf((float)acc);
-    const uint16_t lo = f2bf((float)(acc - (double)bf2f(hi)));
-    uint16_t* row = gcat + (long)i * 3 * r;
-    row[j] = hi;
-    row[r + j] = hi;
-    row[2 * r + j] = lo;
+// G = V V^T for v_t = V^T [d, r]: workgroup (bx, by) computes the 16 x 16
+// block G[16 by .., 16 bx ..], thread (ty, tx) one element.  The two 16-column
+// slices of v_t pass through LDS 64 rows of k at a time (threads 0..127 load
+// the row slice, 128..255 the column slice, 16 bytes each).  Products of bf16
+// values are exact in fp64 and each element sums them in k order, so G is
+// symmetric bit for bit.  Row i of gcat is [hi | hi | lo] with
+// hi = bf16(G[i, :]) and lo = bf16(G[i, :] - hi).
+__global__ __launch_bounds__(256) void ltp_gram_kernel(const uint16_t* __restrict__ v_t, int d, int r,
+                                                       uint16_t* __restrict__ gcat) {
+  __shared__ float sl[2][64][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int which = threadIdx.x >> 7;                       // 0: columns i0.., 1: columns j0..
+  const int lr = (threadIdx.x & 127) >> 1, lc = (threadIdx.x & 1) * 8;
+  const int c0 = which ? j0 : i0;
+  double acc = 0.0;
+  for (int k0 = 0; k0 < d; k0 += 64) {
+    const int k = k0 + lr;
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (k < d) a = ld16(v_t + (long)k * r + c0 + lc);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sl[which][lr][lc + 2 * w] = lo_bf(a[w]);
+      sl[which][lr][lc + 2 * w + 1] = hi_bf(a[w]);
+    }
+    __syncthreads();
+    const int kn = min(64, d - k0);
+    for (int kk = 0; kk < kn; ++kk) acc = fma((double)sl[0][kk][ty], (double)sl[1][kk][tx], acc);
+    __syncthreads();
   }
+  const int i = i0 + ty, j = j0 + tx;
+  const uint16_t hi = f2bf((float)acc);
+  const uint16_t lo = f2bf((float)(acc - (double)bf2f(hi)));
+  uint16_t* row = gcat + (long)i * 3 * r;
+  row[j] = hi;
+  row[r + j] = hi;
+  row[2 * r + j] = lo;
 }
 
 inline dim3 grid_for(long work, int tpb = 256) {
@@ -234,7 +253,7 @@ hipError_t launch_rowsum_sqrt(const float* partial, int n, int parts, float* out
 }
 
 hipError_t launch_ltp_gram(const uint16_t* v_t, int d, int r, uint16_t* gcat, hipStream_t s) {
-  hipLaunchKernelGGL(ltp_gram_kernel, dim3(r), dim3(256), 0, s, v_t, d, r, gcat);
+  hipLaunchKernelGGL(ltp_gram_kernel, dim3(r / 16, r / 16), dim3(256), 0, s, v_t, d, r, gcat);
   return hipGetLastError();
 }
 

@@ -107,16 +107,17 @@ class LayerConfig:
     theta: Optional[float] = None         # None: no rotary embedding
 
 
-def ltp_gram(w):
-    """Gram operand of the linear proxy in weights dict w (spts_ltp_gram),
-    prepared on first use and kept in w; prepared again when v_t is replaced
-    or written in place (its version counter moves)."""
-    v = w["v_t"]
-    key = (v.data_ptr(), v._version, tuple(v.shape))
-    cached = w.get("_ltp_gram")
-    if cached is None or cached[0] != key:
-        cached = (key, capi.spts_ltp_gram(v))
-        w["_ltp_gram"] = cached
+def ltp_gram(w, key="v_t"):
+    """Gram operand of the proxy's last factor w[key] (spts_ltp_gram): v_t of
+    the linear proxy, d_t of the packed structured one.  Prepared on first use
+    and kept in w; prepared again when the factor is replaced or written in
+    place (its version counter moves)."""
+    v = w[key]
+    stamp = (v.data_ptr(), v._version, tuple(v.shape))
+    cached = w.get("_gram_" + key)
+    if cached is None or cached[0] != stamp:
+        cached = (stamp, capi.spts_ltp_gram(v))
+        w["_gram_" + key] = cached
     return cached[1]
 
 
@@ -234,8 +235,13 @@ def ffn_block(h, S, w, cfg: LayerConfig, fused=True, trace=None, tm=NO_TIMER):
     if cfg.proxy == "structured":
         pk = w["proxy_packed"]
         r, d_low = pk["c_t"].shape
-        with tm("ltp_probe", 2.0 * n * 3 * r * (d + d_low)):
-            L = capi.spts_ltp_probe_structured(z, pk)
+        if cfg.ltp_form == "gram":
+            gram = ltp_gram(pk, "d_t")      # offline: once per proxy
+            with tm("ltp_probe", 2.0 * n * r * (2 * d + 3 * d_low + r)):
+                L = capi.spts_ltp_probe_structured(z, pk, gram=gram)
+        else:
+            with tm("ltp_probe", 2.0 * n * 3 * r * (d + d_low)):
+                L = capi.spts_ltp_probe_structured(z, pk)
     elif cfg.ltp_form == "gram":
         r = w["u_t"].shape[0]
         gram = ltp_gram(w)                  # offline: once per proxy

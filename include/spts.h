@@ -246,6 +246,16 @@ spts_status spts_ltp_probe_structured(spts_ctx* ctx, const void* z, const void* 
                                       const void* d_t, int n, int d, int r, int d_low,
                                       float* score);
 
+/* The structured score with its last factor through D's Gram matrix:
+ * score[m]^2 = u G u^T, u = h[m,:] C, G = D D^T, equal to ||u D||^2 (the
+ * rounding as in spts_ltp_probe_gram).  gram [r, 3r] bf16 is spts_ltp_gram
+ * of d_t, prepared once per proxy; the other arguments and the workspace
+ * (spts_ltp_structured_workspace) are those of spts_ltp_probe_structured. */
+spts_status spts_ltp_probe_structured_gram(spts_ctx* ctx, const void* z, const void* a_gu_t,
+                                           const void* b_gate, const void* b_up, const void* c_t,
+                                           const void* gram, int n, int d, int r, int d_low,
+                                           float* score);
+
 /* ------------------------------------------------------------- reduced FFN */
 
 /* Reduced SwiGLU feed-forward ([SPTS] Fig. 2(b)) on k selected rows:

@@ -520,24 +520,30 @@ def _structured_case(n, d, f, d_low, r, seed):
 _SP_KEYS = ("a_g_t", "b_g_t", "a_u_t", "b_u_t", "c_t", "d_t")
 
 
-@pytest.mark.parametrize("n,d,f,d_low,r", [(1000, 512, 1024, 512, 256), (777, 1024, 2048, 256, 256)])
-def test_ltp_structured(n, d, f, d_low, r):
-    _log(f"structured ltp n={n} d={d} d_low={d_low} r={r}")
+@pytest.mark.parametrize("form", ["direct", "gram"])
+@pytest.mark.parametrize("n,d,f,d_low,r", [(1000, 512, 1024, 512, 256), (777, 1024, 2048, 256, 256),
+                                           (300, 512, 1024, 512, 512)])
+def test_ltp_structured(n, d, f, d_low, r, form):
+    """Both forms of the last factor (D itself, or its Gram matrix D D^T)."""
+    _log(f"structured ltp n={n} d={d} d_low={d_low} r={r} {form}")
     z, sp = _structured_case(n, d, f, d_low, r, seed=60)
     packed = capi.pack_structured_proxy(*[_cuda(sp[k]) for k in _SP_KEYS])
-    L = capi.spts_ltp_probe_structured(_cuda(z), packed)
+    gram = capi.spts_ltp_gram(packed["d_t"]) if form == "gram" else None
+    L = capi.spts_ltp_probe_structured(_cuda(z), packed, gram=gram)
     ref = ltp.ltp_structured_scores(W.as_f64(z), *[W.as_f64(sp[k]) for k in _SP_KEYS])
     got = np64(L)
     assert_close(got, ref, F32_REL, "structured ltp")
     assert (np.abs(got - ref) / ref).max() < 5e-5          # per row: three hi/lo stages of ~16 bits
 
 
-def test_ltp_structured_full_size_sampled():
+@pytest.mark.parametrize("form", ["direct", "gram"])
+def test_ltp_structured_full_size_sampled(form):
     n, d, f, d_low, r = 32768, 4096, 14336, 512, 256
-    _log("structured ltp full size (sampled rows)")
+    _log(f"structured ltp full size (sampled rows) {form}")
     z, sp = _structured_case(n, d, f, d_low, r, seed=66)
     packed = capi.pack_structured_proxy(*[_cuda(sp[k]) for k in _SP_KEYS])
-    L = capi.spts_ltp_probe_structured(_cuda(z), packed)
+    gram = capi.spts_ltp_gram(packed["d_t"]) if form == "gram" else None
+    L = capi.spts_ltp_probe_structured(_cuda(z), packed, gram=gram)
     pick = np.random.default_rng(4).choice(n, 128, replace=False)
     ref = ltp.ltp_structured_scores(W.as_f64(z[pick]), *[W.as_f64(sp[k]) for k in _SP_KEYS])
     got = np64(L)[pick]
