@@ -141,8 +141,12 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
             xt = capi.spts_rmsnorm(x, cfg.eps)
     else:
         xt = x
-    # a1: K, V over all current candidates (+ RoPE on K)
-    if k_given is None and fused:
+    # a1: K, V over all current candidates (+ RoPE on K).  At an MSDP boundary
+    # (fused path) only K is needed for every candidate -- the probe scores
+    # them all -- so V is projected after the pruning, for the kept rows only
+    v_late = fused and k_given is None and prune_to is not None and prune_to < n
+    V = None
+    if k_given is None and fused and not v_late:
         with tm("kv_proj", 4.0 * n * d * Hkv * dh):
             K, V = capi.spts_linear_kv(xt, w["wk"], w["wv"], pos if rope else None, rope_table if rope else None)
         K, V = K.view(n, Hkv, dh), V.view(n, Hkv, dh)
@@ -154,8 +158,9 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
             K = K.view(n, Hkv, dh)
         else:
             K = k_given
-        with tm("v_proj", 2.0 * n * d * Hkv * dh):
-            V = capi.spts_linear(xt, w["wv"]).view(n, Hkv, dh)
+        if not v_late:
+            with tm("v_proj", 2.0 * n * d * Hkv * dh):
+                V = capi.spts_linear(xt, w["wv"]).view(n, Hkv, dh)
     # a2: probe queries (last P rows)
     xp = xt[n - P:]
     with tm("probe_q_proj", 2.0 * P * d * Hq * dh):
@@ -182,11 +187,17 @@ def attention_block(x, pos, w: Dict[str, torch.Tensor], cfg: LayerConfig, rope_t
             else:
                 xt_rows = keep
             K = capi.spts_gather(K, keep)
-            V = capi.spts_gather(V, keep)
+            if V is not None:
+                V = capi.spts_gather(V, keep)
             S = capi.spts_gather(S, keep)
         n = prune_to
         if trace is not None:
             trace.update(keep=keep)
+    if V is None:
+        # V of the kept candidates, their normalised rows gathered on load
+        with tm("v_proj", 2.0 * n * d * Hkv * dh):
+            V = (capi.spts_linear(xt, w["wv"], a_rows=xt_rows) if xt_rows is not None
+                 else capi.spts_linear(xt, w["wv"])).view(n, Hkv, dh)
     if kv_out is not None:
         kv_out.append((K, V))             # this layer's cache: its candidates' keys and values
     # a4: select the attention rows

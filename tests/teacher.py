@@ -90,11 +90,14 @@ def check_layer(tr, w, cfg, prune_to=None, n_sample=64, seed=0, log=print, k_giv
 
     # ---- K, V, probe queries from the GPU's xt
     K_pre = np64(tr["K_pre"]).reshape(n_in, Hkv, dh)
-    V_pre = np64(tr["V_pre"]).reshape(n_in, Hkv, dh)
+    # at an MSDP boundary the pipeline projects V only for the kept rows,
+    # after the pruning (V_pre is then None and V is checked below)
+    V_pre = np64(tr["V_pre"]).reshape(n_in, Hkv, dh) if tr["V_pre"] is not None else None
     rows = _sample(n_in, n_sample, rng, must=(0, n_in - 1))
     if not k_given:
         out["K"] = _rows_bar(K_pre[rows], olayer.project(xt[rows], w64["wk"], Hkv, dh, pos_in[rows], theta), "K")
-    out["V"] = _rows_bar(V_pre[rows], olayer.project(xt[rows], w64["wv"], Hkv, dh), "V")
+    if V_pre is not None:
+        out["V"] = _rows_bar(V_pre[rows], olayer.project(xt[rows], w64["wv"], Hkv, dh), "V")
     Qp = np64(tr["Qp"]).reshape(P, Hq, dh)
     out["Qp"] = _rows_bar(Qp, olayer.project(xt[-P:], w64["wq"], Hq, dh, pos_in[-P:], theta), "probe Q")
 
@@ -113,13 +116,20 @@ def check_layer(tr, w, cfg, prune_to=None, n_sample=64, seed=0, log=print, k_giv
         cand = keep
         assert np.array_equal(tr["pos"].cpu().numpy(), pos_in[keep]), "positions after the boundary"
         assert np.array_equal(np64(tr["K"]).reshape(-1, Hkv, dh), K_pre[keep]), "K compaction"
-        assert np.array_equal(np64(tr["V"]).reshape(-1, Hkv, dh), V_pre[keep]), "V compaction"
+        if V_pre is not None:
+            assert np.array_equal(np64(tr["V"]).reshape(-1, Hkv, dh), V_pre[keep]), "V compaction"
         assert np.array_equal(np64(tr["S"]), S_pre[keep]), "S compaction"
     else:
         cand = np.arange(n_in)
     n = len(cand)
     K = K_pre[cand]
-    V = V_pre[cand]
+    if V_pre is not None:
+        V = V_pre[cand]
+    else:
+        # V of the kept rows, projected after the boundary from the same xt rows
+        V = np64(tr["V"]).reshape(n, Hkv, dh)
+        vr = _sample(n, n_sample, rng, must=(0, n - 1))
+        out["V"] = _rows_bar(V[vr], olayer.project(xt[cand[vr]], w64["wv"], Hkv, dh), "V (kept rows)")
     S_c = S_ref[cand]
     pos = pos_in[cand]
 
