@@ -516,7 +516,7 @@ spts_status spts_ltp_probe(spts_ctx* ctx, const void* z, const void* u_t, const 
 spts_status spts_ltp_gram(spts_ctx* ctx, const void* v_t, int d, int r, void* gram) {
   CHECK_CTX();
   REQUIRE(d > 0 && r > 0, SPTS_ERR_SHAPE, "bad LTP Gram sizes");
-  REQUIRE(r % 256 == 0 && d <= 65536, SPTS_ERR_UNSUPPORTED, "LTP Gram needs r %% 256 == 0 and d <= 65536");
+  REQUIRE(r % 256 == 0, SPTS_ERR_UNSUPPORTED, "LTP Gram needs r %% 256 == 0");
   {
     const spts_status st = weight_size_ok(ctx, d, r);
     if (st != SPTS_OK) return st;

@@ -223,7 +223,7 @@ spts_status spts_ltp_probe_gram(spts_ctx* ctx, const void* z, const void* u_t, c
  * [d, r] bf16, accumulated in fp64 (G is symmetric bit for bit), written to
  * gram [r, 3r] bf16 as rows [hi(G) | hi(G) | lo(G)], hi = bf16(G),
  * lo = bf16(G - hi).  The buffer belongs to the caller and stays valid while
- * v_t is unchanged.  Requires r % 256 == 0 and 0 < d <= 65536.  No workspace. */
+ * v_t is unchanged.  Requires r % 256 == 0, d > 0.  No workspace. */
 spts_status spts_ltp_gram(spts_ctx* ctx, const void* v_t, int d, int r, void* gram);
 
 /* The structured proxy form of [SPTS] Table A: the feed-forward restricted to

@@ -159,6 +159,33 @@ def test_gemm_family_validation(L, ctx):
     assert kv(ctx, FAKE, None, 0, 128, FAKE, 1024, FAKE, 1024, FAKE, FAKE, None, None) == OK             # empty: no-op
 
 
+def test_ltp_gram_validation(L, ctx):
+    """The Gram-form LTP calls: sizes, alignment, empty input, the workspace
+    refusal, and the Gram operand's own size check."""
+    g = L.spts_ltp_gram
+    assert g(ctx, FAKE, 4096, 192, FAKE) == UNSUPPORTED                                # r % 256
+    assert g(ctx, FAKE, 0, 256, FAKE) == SHAPE
+    assert g(ctx, MIS, 4096, 256, FAKE) == ALIGN
+    assert g(ctx, FAKE, 4096, 256, None) == INVALID
+    assert g(ctx, FAKE, 8388608, 256, FAKE) == UNSUPPORTED                              # v_t of 4 GiB
+    pg = L.spts_ltp_probe_gram
+    assert pg(ctx, FAKE, FAKE, FAKE, 10, 4096, 100, FAKE) == UNSUPPORTED                 # r % 256
+    assert pg(ctx, FAKE, FAKE, FAKE, 10, 1000, 256, FAKE) == UNSUPPORTED                 # d % 256
+    assert pg(ctx, FAKE, FAKE, FAKE, -1, 4096, 256, FAKE) == SHAPE
+    assert pg(ctx, FAKE, FAKE, FAKE, 0, 4096, 256, FAKE) == OK                           # empty: no-op
+    assert pg(ctx, FAKE, FAKE, None, 10, 4096, 256, FAKE) == INVALID
+    assert pg(ctx, FAKE, FAKE, MIS, 10, 4096, 256, FAKE) == ALIGN
+    assert pg(ctx, FAKE, FAKE, FAKE, 10, 4096, 256, FAKE) == NOMEM                       # no workspace bound
+    assert pg(ctx, FAKE, FAKE, FAKE, 10, 4096, 65536, FAKE) == UNSUPPORTED               # gram of 4 GiB x 3
+    assert L.spts_ltp_gram_workspace(100, 4096, 256) >= 100 * 3 * 256 * 2 + 256 * 256 * 4
+    assert L.spts_ltp_gram_workspace(0, 4096, 256) == 0
+    sg = L.spts_ltp_probe_structured_gram
+    assert sg(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4096, 192, 512, FAKE) == UNSUPPORTED   # r % 256
+    assert sg(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4096, 256, 512, FAKE) == NOMEM
+    assert sg(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4096, 256, 512, FAKE) == OK             # empty
+    assert sg(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, None, 10, 4096, 256, 512, FAKE) == INVALID
+
+
 def test_attention_and_rows_validation(L, ctx):
     f = L.spts_reduced_attention
     assert f(ctx, capi.BF16, FAKE, FAKE, FAKE, FAKE, 10, 5, 32, 8, 128, 0.1, FAKE) == SHAPE   # kq > n
