@@ -18,6 +18,7 @@
 // the remaining digits over them, with no workgroup barrier per digit; a
 // larger bin (many equal scores) continues with 8-bit workgroup passes.
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -505,12 +506,21 @@ hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b,
                        int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s) {
   uint32_t* keys = reinterpret_cast<uint32_t*>(ws);
   const int mult = multiply ? 1 : 0;
-  if (n <= TPB * 8)
-    hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys, 0L, 0L);
-  else if (n <= TPB * 32)
-    hipLaunchKernelGGL(topk_kernel<32>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys, 0L, 0L);
-  else
-    hipLaunchKernelGGL(topk_kernel<0>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, keys, 0L, 0L);
+  // The fewest rows per lane that hold n: wave w owns rows [64 IPT w, 64 IPT (w + 1)),
+  // so a larger IPT than needed leaves waves idle while the busy lanes walk
+  // IPT keys in every pass (11,469 scores: 12 per lane on 15 waves instead of
+  // 32 on 6).
+  const auto go = [&](auto ipt) {
+    hipLaunchKernelGGL(topk_kernel<decltype(ipt)::value>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k,
+                       n_forced, idx, fused_out, keys, 0L, 0L);
+  };
+  if (n <= TPB * 8) go(std::integral_constant<int, 8>{});
+  else if (n <= TPB * 12) go(std::integral_constant<int, 12>{});
+  else if (n <= TPB * 16) go(std::integral_constant<int, 16>{});
+  else if (n <= TPB * 20) go(std::integral_constant<int, 20>{});
+  else if (n <= TPB * 24) go(std::integral_constant<int, 24>{});
+  else if (n <= TPB * 32) go(std::integral_constant<int, 32>{});
+  else go(std::integral_constant<int, 0>{});
   return hipGetLastError();
 }
 

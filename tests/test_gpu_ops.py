@@ -121,7 +121,13 @@ def test_probe_f32_tiny_config():
     (131072, 32768, 128, "exp", 2000), (4097, 2049, 0, "few", 0),
     # more than 8192 keys share the threshold's first digit: workgroup passes finish
     (32768, 16384, 64, "band", 0), (32768, 16384, 64, "band", 300), (32768, 11469, 64, "few3", 0),
-    (131072, 65536, 128, "band", 0)])
+    (131072, 65536, 128, "band", 0),
+    # each keys-per-lane width of the one-workgroup select (12, 16, 20, 24, 32), at its
+    # smallest and largest n and at the MSDP stack's candidate counts
+    (8193, 2868, 64, "exp", 30), (11469, 4014, 64, "exp", 100), (12288, 4300, 64, "few", 0),
+    (12289, 4301, 64, "band", 0), (14746, 5161, 64, "exp", 200), (16384, 8192, 64, "band", 50),
+    (19661, 6881, 64, "exp", 300), (20480, 10240, 64, "band", 0), (20481, 7168, 64, "few3", 0),
+    (24576, 8602, 64, "exp", 0), (24577, 8602, 64, "band", 100)])
 def test_select_bit_exact(n, k, nf, dist, ties):
     _log(f"select n={n} k={k} nf={nf} {dist}")
     s = W.make_scores(n, seed=n + k, ties=ties, dist=dist)
@@ -151,7 +157,8 @@ def test_select_batched_bit_exact(n, k, nf, batch):
 
 @pytest.mark.parametrize("n,k,nf,nan", [(1000, 350, 64, False), (32768, 11469, 64, False),
                                          (131072, 32768, 128, False), (1000, 350, 64, True),
-                                         (131072, 32768, 128, True)])
+                                         (131072, 32768, 128, True), (19661, 6881, 64, False),
+                                         (14746, 5161, 64, True), (11469, 4014, 64, False)])
 def test_select_fused_bit_exact(n, k, nf, nan):
     # n > 32768 keeps the keys in the workspace and takes the maxima in a loop of its own
     _log(f"fused select n={n} nan={nan}")
@@ -168,7 +175,7 @@ def test_select_fused_bit_exact(n, k, nf, nan):
     assert np.array_equal(idx.cpu().numpy().astype(np.int64), select.select_topk(ref_c, k, nf))
 
 
-@pytest.mark.parametrize("n,k,nf", [(1000, 350, 64), (32768, 11469, 64)])
+@pytest.mark.parametrize("n,k,nf", [(1000, 350, 64), (32768, 11469, 64), (19661, 6881, 64)])
 def test_select_multiply_bit_exact(n, k, nf):
     _log(f"multiply select n={n}")
     a = W.make_scores(n, seed=9)
