@@ -358,6 +358,39 @@ def test_linear_rope():
     assert_close(np64(out2), ref[rows.long().numpy()], BF16_REL, "gathered linear rope")
 
 
+@pytest.mark.parametrize("m,kd,n", [(64, 4096, 4096), (1, 64, 256), (65, 192, 512), (128, 4096, 1024),
+                                    (17, 1024, 768), (129, 256, 512)])
+def test_linear_few_rows(m, kd, n):
+    """Few rows (the probe queries' shape, 64 or 128 rows): one partly
+    filled 256-row tile, split along k with fp32 pieces."""
+    _log(f"linear few rows m={m} k={kd} n={n}")
+    a = W.randn((m, kd), seed=32)
+    w = W.randn((n, kd), seed=33, std=0.05)
+    out = capi.spts_linear(_cuda(a), _cuda(w))
+    ref = _linear_ref(a, w)
+    assert_close(np64(out), ref, BF16_REL, "few-rows linear")
+    ulp = np.abs(np64(out) - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert (ulp <= 2 ** -7).mean() > 0.999
+
+
+@pytest.mark.parametrize("m,kd,n", [(64, 4096, 4096), (128, 4096, 4096), (37, 512, 256), (1, 128, 256)])
+def test_linear_rope_few_rows(m, kd, n):
+    """RoPE on few rows (the probe queries' projection), through the
+    split-K reduce's RoPE epilogue."""
+    _log(f"linear rope few rows m={m} k={kd} n={n}")
+    theta = 500000.0
+    a = W.randn((m, kd), seed=34)
+    w = W.randn((n, kd), seed=35, std=0.05)
+    pos = torch.from_numpy(np.sort(np.random.default_rng(2).choice(131072, m, replace=False)).astype(np.int32))
+    table = capi.spts_rope_table(131072, 128, theta, DEV)
+    out = capi.spts_linear_rope(_cuda(a), _cuda(w), _cuda(pos), table)
+    acc = numerics.f32(W.as_f64(a) @ W.as_f64(w).T).reshape(m, n // 128, 128)
+    ref = numerics.bf16(normrope.rope(acc, pos.numpy(), theta)).reshape(m, n)
+    assert_close(np64(out), ref, BF16_REL, "few-rows linear rope")
+    ulp = np.abs(np64(out) - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert (ulp <= 2 ** -7).mean() > 0.995
+
+
 @pytest.mark.parametrize("rope", [True, False])
 def test_linear_kv(rope):
     _log(f"linear kv rope={rope}")
