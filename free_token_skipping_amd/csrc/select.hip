@@ -17,6 +17,7 @@
 // (the usual case), those keys are copied to LDS and a single wave finishes
 // the remaining digits over them, with no workgroup barrier per digit; a
 // larger bin (many equal scores) continues with 8-bit workgroup passes.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -450,6 +451,198 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 #undef SPTS_FRESH_ROWS
 }
 
+// ------------------------------------------- many-workgroup select (n > 32K)
+// Above 32K scores a single workgroup cannot keep the keys in registers and
+// re-reads them on every pass, so a plain selection spreads over the chip:
+// three radix digits (bits 31..21, 20..10, 9..0) are counted by all
+// workgroups into global histograms (integer atomics: exact), each pass
+// recovering the earlier digits from the earlier histograms itself (no
+// separate launch per digit); a count pass fixes the threshold key T and how
+// many rows equal to T to take, counts each workgroup's contiguous row range,
+// a one-workgroup scan turns the counts into output offsets, and a write pass
+// emits the indices in index order.  Same selection as topk_kernel: forced
+// rows, free rows above T, and the lowest-index need_eq free rows equal to T.
+constexpr int MT = 256;                       // threads per workgroup of these passes
+constexpr int MG = 256;                       // most workgroups of the count / write passes
+constexpr int MB = 2048;                      // bins of the 11-bit digits (the last digit uses 1024)
+// workspace ints: hist[3][MB] | st[4] | counts[2 MG] | offs[2 MG]
+constexpr int M_ST = 3 * MB, M_CNT = M_ST + 4, M_OFF = M_CNT + 2 * MG;
+
+__device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 21 : p == 1 ? 10 : 0; }
+__device__ __forceinline__ int digit_bins(int p) { return p == 2 ? 1024 : 2048; }
+
+// inclusive scan of one int per thread over the 256-thread workgroup
+__device__ __forceinline__ int block_incl_scan(int v, int* sh) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int q = 0; q < MT / 64; ++q) before += q < w ? sh[q] : 0;
+  __syncthreads();
+  return before + incl;
+}
+
+// The digits of passes 0 .. np-1 from their histograms: the bin holding the
+// rem-th largest counted key, bins scanned from the top.  Every thread of the
+// workgroup returns the same prefix, mask and remaining rank.
+__device__ void find_digits(const int* __restrict__ hist, int np, uint32_t& prefix, uint32_t& mask, int& rem,
+                            int* sh) {
+  const int t = threadIdx.x;
+  for (int p = 0; p < np; ++p) {
+    const int nb = digit_bins(p), per = nb / MT;
+    const int* h = hist + p * MB;
+    int c[8];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      c[q] = q < per ? h[nb - 1 - (t * per + min(q, per - 1))] : 0;   // this thread's bins, descending
+      sum += c[q];
+    }
+    const int incl = block_incl_scan(sum, sh);
+    const int excl = incl - sum;
+    if (excl < rem && rem <= incl) {                      // exactly one thread holds the crossing
+      int acc = excl, d = -1;                             // acc: keys in bins above d
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (d < 0 && q < per) {
+          if (rem <= acc + c[q]) d = nb - 1 - (t * per + q);
+          else acc += c[q];
+        }
+      }
+      sh[MT / 64] = d;
+      sh[MT / 64 + 1] = rem - acc;
+    }
+    __syncthreads();
+    const int d = sh[MT / 64];
+    rem = sh[MT / 64 + 1];
+    __syncthreads();
+    const int sft = digit_shift(p);
+    prefix |= (uint32_t)d << sft;
+    mask |= (uint32_t)(nb - 1) << sft;
+  }
+}
+
+__global__ __launch_bounds__(MT) void mtopk_init_kernel(int* __restrict__ ws) {
+  for (int i = threadIdx.x; i < 3 * MB; i += MT) ws[i] = 0;
+}
+
+// pass P: histogram of digit P over the free keys that carry the earlier digits
+template <int P>
+__global__ __launch_bounds__(MT) void mtopk_hist_kernel(const float* __restrict__ s, int nfree, int kp,
+                                                        int* __restrict__ ws) {
+  __shared__ int lh[MB];
+  __shared__ int sh[8];
+  uint32_t prefix = 0u, mask = 0u;
+  int rem = kp;
+  find_digits(ws, P, prefix, mask, rem, sh);
+  const int nb = digit_bins(P), sft = digit_shift(P);
+  for (int i = threadIdx.x; i < nb; i += MT) lh[i] = 0;
+  __syncthreads();
+  for (int i = blockIdx.x * MT + threadIdx.x; i < nfree; i += gridDim.x * MT) {
+    const uint32_t key = order_key(s[i]);
+    if ((key & mask) == prefix) atomicAdd(&lh[(key >> sft) & (uint32_t)(nb - 1)], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += MT)
+    if (lh[i]) atomicAdd(&ws[P * MB + i], lh[i]);
+}
+
+// threshold T and need_eq from the three histograms; per workgroup range
+// [b R, (b + 1) R): rows taken for sure (forced, or free above T) and free rows equal to T
+__global__ __launch_bounds__(MT) void mtopk_count_kernel(const float* __restrict__ s, int n, int nfree, int kp,
+                                                         int R, int* __restrict__ ws) {
+  __shared__ int sh[8];
+  uint32_t T = 0xFFFFFFFFu;                                // kp == 0: no free row is taken
+  int need_eq = 0;
+  if (kp > 0) {
+    uint32_t mask = 0u;
+    T = 0u;
+    need_eq = kp;
+    find_digits(ws, 3, T, mask, need_eq, sh);
+  }
+  const int b0 = blockIdx.x * R, b1 = min(n, b0 + R);
+  int g = 0, e = 0;
+  for (int i = b0 + threadIdx.x; i < b1; i += MT) {
+    const uint32_t key = order_key(s[i]);
+    const bool free_row = i < nfree;
+    g += (!free_row | (key > T)) ? 1 : 0;
+    e += (free_row & (key == T)) ? 1 : 0;
+  }
+  g = block_incl_scan(g, sh);                               // thread MT-1 holds the totals
+  e = block_incl_scan(e, sh);
+  if (threadIdx.x == MT - 1) {
+    ws[M_CNT + 2 * blockIdx.x] = g;
+    ws[M_CNT + 2 * blockIdx.x + 1] = e;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ws[M_ST] = (int)T;
+    ws[M_ST + 1] = need_eq;
+  }
+}
+
+// output offset and equal rows before each workgroup's range (one workgroup, G <= MG)
+__global__ __launch_bounds__(MT) void mtopk_scan_kernel(int G, int* __restrict__ ws) {
+  __shared__ int sh[8];
+  const int t = threadIdx.x;
+  const int need_eq = ws[M_ST + 1];
+  const int g = t < G ? ws[M_CNT + 2 * t] : 0;
+  const int e = t < G ? ws[M_CNT + 2 * t + 1] : 0;
+  const int e_excl = block_incl_scan(e, sh) - e;
+  const int take = g + min(max(need_eq - e_excl, 0), e);
+  const int t_excl = block_incl_scan(take, sh) - take;
+  if (t < G) {
+    ws[M_OFF + 2 * t] = t_excl;
+    ws[M_OFF + 2 * t + 1] = e_excl;
+  }
+}
+
+// exclusive count of `flag` over the workgroup's threads in thread order, and the total
+__device__ __forceinline__ int block_excl_count(bool flag, int* sh, int& total) {
+  const int w = threadIdx.x >> 6;
+  const uint64_t m = __ballot(flag);
+  if ((threadIdx.x & 63) == 0) sh[w] = __popcll(m);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int q = 0; q < MT / 64; ++q) {
+    before += q < w ? sh[q] : 0;
+    total += sh[q];
+  }
+  __syncthreads();
+  return before + lanes_below(m);
+}
+
+__global__ __launch_bounds__(MT) void mtopk_write_kernel(const float* __restrict__ s, int n, int nfree, int k,
+                                                         int R, const int* __restrict__ ws,
+                                                         int32_t* __restrict__ idx) {
+  __shared__ int sh[8];
+  const uint32_t T = (uint32_t)ws[M_ST];
+  const int need_eq = ws[M_ST + 1];
+  int out = ws[M_OFF + 2 * blockIdx.x], eq_before = ws[M_OFF + 2 * blockIdx.x + 1];
+  const int b0 = blockIdx.x * R, b1 = min(n, b0 + R);
+  for (int c0 = b0; c0 < b1; c0 += MT) {                    // uniform over the workgroup
+    const int i = c0 + threadIdx.x;
+    const bool valid = i < b1;
+    const uint32_t key = valid ? order_key(s[i]) : 0u;
+    const bool free_row = valid & (i < nfree);
+    const bool eq = free_row & (key == T);
+    int n_eq, n_take;
+    const int er = eq_before + block_excl_count(eq, sh, n_eq);
+    const bool take = (valid & !free_row) | (free_row & (key > T)) | (eq & (er < need_eq));
+    const int pos = out + block_excl_count(take, sh, n_take);
+    if (take & (pos < k)) idx[pos] = i;                     // exactly k are taken; the bound only guards memory
+    out += n_take;
+    eq_before += n_eq;
+  }
+}
+
+__global__ void iota_kernel(int n, int32_t* __restrict__ idx) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) idx[i] = i;
+}
+
 }  // namespace
 
 hipError_t launch_topk_batched(const float* s, long s_stride, int batch, int n, int k, int n_forced, int32_t* idx,
@@ -502,6 +695,31 @@ hipError_t launch_topk_noalloc(const float* s_a, const float* s_b, float w_a, fl
   return launch_topk(s_a, s_b, w_a, w_b, multiply, n, k, n_forced, idx, fused_out, keys, s);
 }
 
+// plain selection over n > 32768 scores on many workgroups (ws: the call's
+// workspace, at least topk_workspace(n) bytes, of which it uses about 30 KiB)
+static hipError_t launch_topk_many(const float* sc, int n, int k, int n_forced, int32_t* idx, int* ws,
+                                   hipStream_t s) {
+  if (k >= n) {
+    hipLaunchKernelGGL(iota_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, s, n, idx);
+    return hipGetLastError();
+  }
+  const int nfree = n - n_forced, kp = k - n_forced;
+  const int hist_blocks = std::min(1024, std::max(1, (nfree + 4 * MT - 1) / (4 * MT)));
+  // contiguous row ranges of whole 256-row chunks, at most MG of them
+  const int R = (((n + MG - 1) / MG) + MT - 1) / MT * MT;
+  const int G = (n + R - 1) / R;
+  hipLaunchKernelGGL(mtopk_init_kernel, dim3(1), dim3(MT), 0, s, ws);
+  if (kp > 0) {
+    hipLaunchKernelGGL(mtopk_hist_kernel<0>, dim3(hist_blocks), dim3(MT), 0, s, sc, nfree, kp, ws);
+    hipLaunchKernelGGL(mtopk_hist_kernel<1>, dim3(hist_blocks), dim3(MT), 0, s, sc, nfree, kp, ws);
+    hipLaunchKernelGGL(mtopk_hist_kernel<2>, dim3(hist_blocks), dim3(MT), 0, s, sc, nfree, kp, ws);
+  }
+  hipLaunchKernelGGL(mtopk_count_kernel, dim3(G), dim3(MT), 0, s, sc, n, nfree, kp, R, ws);
+  hipLaunchKernelGGL(mtopk_scan_kernel, dim3(1), dim3(MT), 0, s, G, ws);
+  hipLaunchKernelGGL(mtopk_write_kernel, dim3(G), dim3(MT), 0, s, sc, n, nfree, k, R, ws, idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
                        int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s) {
   uint32_t* keys = reinterpret_cast<uint32_t*>(ws);
@@ -520,7 +738,8 @@ hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b,
   else if (n <= TPB * 20) go(std::integral_constant<int, 20>{});
   else if (n <= TPB * 24) go(std::integral_constant<int, 24>{});
   else if (n <= TPB * 32) go(std::integral_constant<int, 32>{});
-  else go(std::integral_constant<int, 0>{});
+  else if (s_b) go(std::integral_constant<int, 0>{});        // fused scores: one workgroup
+  else return launch_topk_many(s_a, n, k, n_forced, idx, reinterpret_cast<int*>(ws), s);
   return hipGetLastError();
 }
 

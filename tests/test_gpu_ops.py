@@ -127,13 +127,29 @@ def test_probe_f32_tiny_config():
     (8193, 2868, 64, "exp", 30), (11469, 4014, 64, "exp", 100), (12288, 4300, 64, "few", 0),
     (12289, 4301, 64, "band", 0), (14746, 5161, 64, "exp", 200), (16384, 8192, 64, "band", 50),
     (19661, 6881, 64, "exp", 300), (20480, 10240, 64, "band", 0), (20481, 7168, 64, "few3", 0),
-    (24576, 8602, 64, "exp", 0), (24577, 8602, 64, "band", 100)])
+    (24576, 8602, 64, "exp", 0), (24577, 8602, 64, "band", 100),
+    # above 32K scores a plain selection runs on many workgroups
+    (32769, 11469, 64, "exp", 500), (40000, 10000, 0, "few", 0), (65536, 32768, 128, "band", 300),
+    (50000, 64, 64, "exp", 0), (50000, 65, 64, "few3", 0), (70001, 70000, 64, "exp", 0),
+    (70001, 80000, 64, "exp", 0), (100000, 25000, 128, "band", 0), (1048576, 262144, 128, "exp", 5000)])
 def test_select_bit_exact(n, k, nf, dist, ties):
     _log(f"select n={n} k={k} nf={nf} {dist}")
     s = W.make_scores(n, seed=n + k, ties=ties, dist=dist)
     idx = capi.spts_score_topk(_cuda(s), k, nf)
     ref = select.select_topk(s.numpy(), k, nf)
     assert np.array_equal(idx.cpu().numpy().astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("n", [32769, 131072])
+def test_select_many_workgroups_nan_zero(n):
+    """NaN ranks lowest and -0 equals +0 on the many-workgroup path too."""
+    s = W.make_scores(n, seed=7, ties=300, dist="exp")
+    s[::97] = float("nan")
+    s[::89] = -0.0
+    s[::83] = 0.0
+    for k in (n // 4, n - 2000):
+        idx = capi.spts_score_topk(_cuda(s), k, 64)
+        assert np.array_equal(idx.cpu().numpy().astype(np.int64), select.select_topk(s.numpy(), k, 64))
 
 
 def test_select_special_values():
