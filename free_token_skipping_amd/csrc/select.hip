@@ -453,7 +453,10 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 
 // ------------------------------------------- many-workgroup select (n > 32K)
 // Above 32K scores a single workgroup cannot keep the keys in registers and
-// re-reads them on every pass, so a plain selection spreads over the chip:
+// re-reads them on every pass, so the selection spreads over the chip.  A
+// fused score (MaxNorm-Add needs the two maxima first: one more pass, the
+// maxima as atomicMax over order keys, so NaN is skipped as in topk_kernel)
+// is formed in every pass with the same fp32 operations as topk_kernel.
 // three radix digits (bits 31..21, 20..10, 9..0) are counted by all
 // workgroups into global histograms (integer atomics: exact), each pass
 // recovering the earlier digits from the earlier histograms itself (no
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 constexpr int MT = 256;                       // threads per workgroup of these passes
 constexpr int MG = 256;                       // most workgroups of the count / write passes
 constexpr int MB = 2048;                      // bins of the 11-bit digits (the last digit uses 1024)
-// workspace ints: hist[3][MB] | st[4] | counts[2 MG] | offs[2 MG]
+// workspace ints: hist[3][MB] | st[4] (T, need_eq, max key of s_a, of s_b) | counts[2 MG] | offs[2 MG]
 constexpr int M_ST = 3 * MB, M_CNT = M_ST + 4, M_OFF = M_CNT + 2 * MG;
 
 __device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 21 : p == 1 ? 10 : 0; }
@@ -524,24 +527,72 @@ __device__ void find_digits(const int* __restrict__ hist, int np, uint32_t& pref
   }
 }
 
+// the scores being ranked: s_a alone, or s_a fused with s_b
+struct MScores {
+  const float* a;
+  const float* b;       // nullptr: plain
+  float wa, wb;
+  int mult;
+};
+
+// inverse of order_key (a NaN never reaches it: its key 0 is below every init)
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ float mscore(const MScores& sc, int i, float ma, float mb) {
+  const float a = sc.a[i];
+  if (!sc.b) return a;
+  const float b = sc.b[i];
+  return sc.mult ? __fmul_rn(a, b) : fuse(a, b, ma, mb, sc.wa, sc.wb);
+}
+
+// the maxima of MaxNorm-Add (st[2], st[3] hold their order keys)
+__device__ __forceinline__ void mscore_maxima(const MScores& sc, const int* __restrict__ ws, float& ma,
+                                              float& mb) {
+  ma = mb = 0.f;
+  if (sc.b && !sc.mult) {
+    ma = key_float((uint32_t)ws[M_ST + 2]);
+    mb = key_float((uint32_t)ws[M_ST + 3]);
+  }
+}
+
 __global__ __launch_bounds__(MT) void mtopk_init_kernel(int* __restrict__ ws) {
   for (int i = threadIdx.x; i < 3 * MB; i += MT) ws[i] = 0;
+  if (threadIdx.x < 2) ws[M_ST + 2 + threadIdx.x] = (int)order_key(-INFINITY);
+}
+
+// maxima of s_a and s_b over all rows, NaN skipped (fmaxf), as order keys
+__global__ __launch_bounds__(MT) void mtopk_max_kernel(const float* __restrict__ a, const float* __restrict__ b,
+                                                       int n, int* __restrict__ ws) {
+  float la = -INFINITY, lb = -INFINITY;
+  for (int i = blockIdx.x * MT + threadIdx.x; i < n; i += gridDim.x * MT) {
+    la = fmaxf(la, a[i]);
+    lb = fmaxf(lb, b[i]);
+  }
+  la = wave_max(la);
+  lb = wave_max(lb);
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(reinterpret_cast<unsigned int*>(ws + M_ST + 2), order_key(la));
+    atomicMax(reinterpret_cast<unsigned int*>(ws + M_ST + 3), order_key(lb));
+  }
 }
 
 // pass P: histogram of digit P over the free keys that carry the earlier digits
 template <int P>
-__global__ __launch_bounds__(MT) void mtopk_hist_kernel(const float* __restrict__ s, int nfree, int kp,
-                                                        int* __restrict__ ws) {
+__global__ __launch_bounds__(MT) void mtopk_hist_kernel(MScores sc, int nfree, int kp, int* __restrict__ ws) {
   __shared__ int lh[MB];
   __shared__ int sh[8];
   uint32_t prefix = 0u, mask = 0u;
   int rem = kp;
+  float ma, mb;
+  mscore_maxima(sc, ws, ma, mb);
   find_digits(ws, P, prefix, mask, rem, sh);
   const int nb = digit_bins(P), sft = digit_shift(P);
   for (int i = threadIdx.x; i < nb; i += MT) lh[i] = 0;
   __syncthreads();
   for (int i = blockIdx.x * MT + threadIdx.x; i < nfree; i += gridDim.x * MT) {
-    const uint32_t key = order_key(s[i]);
+    const uint32_t key = order_key(mscore(sc, i, ma, mb));
     if ((key & mask) == prefix) atomicAdd(&lh[(key >> sft) & (uint32_t)(nb - 1)], 1);
   }
   __syncthreads();
@@ -551,9 +602,11 @@ __global__ __launch_bounds__(MT) void mtopk_hist_kernel(const float* __restrict_
 
 // threshold T and need_eq from the three histograms; per workgroup range
 // [b R, (b + 1) R): rows taken for sure (forced, or free above T) and free rows equal to T
-__global__ __launch_bounds__(MT) void mtopk_count_kernel(const float* __restrict__ s, int n, int nfree, int kp,
-                                                         int R, int* __restrict__ ws) {
+__global__ __launch_bounds__(MT) void mtopk_count_kernel(MScores sc, int n, int nfree, int kp, int R,
+                                                         float* __restrict__ fused_out, int* __restrict__ ws) {
   __shared__ int sh[8];
+  float ma, mb;
+  mscore_maxima(sc, ws, ma, mb);
   uint32_t T = 0xFFFFFFFFu;                                // kp == 0: no free row is taken
   int need_eq = 0;
   if (kp > 0) {
@@ -565,7 +618,9 @@ __global__ __launch_bounds__(MT) void mtopk_count_kernel(const float* __restrict
   const int b0 = blockIdx.x * R, b1 = min(n, b0 + R);
   int g = 0, e = 0;
   for (int i = b0 + threadIdx.x; i < b1; i += MT) {
-    const uint32_t key = order_key(s[i]);
+    const float x = mscore(sc, i, ma, mb);
+    if (fused_out) fused_out[i] = x;
+    const uint32_t key = order_key(x);
     const bool free_row = i < nfree;
     g += (!free_row | (key > T)) ? 1 : 0;
     e += (free_row & (key == T)) ? 1 : 0;
@@ -615,10 +670,11 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* sh, int& total) 
   return before + lanes_below(m);
 }
 
-__global__ __launch_bounds__(MT) void mtopk_write_kernel(const float* __restrict__ s, int n, int nfree, int k,
-                                                         int R, const int* __restrict__ ws,
-                                                         int32_t* __restrict__ idx) {
+__global__ __launch_bounds__(MT) void mtopk_write_kernel(MScores sc, int n, int nfree, int k, int R,
+                                                         const int* __restrict__ ws, int32_t* __restrict__ idx) {
   __shared__ int sh[8];
+  float ma, mb;
+  mscore_maxima(sc, ws, ma, mb);
   const uint32_t T = (uint32_t)ws[M_ST];
   const int need_eq = ws[M_ST + 1];
   int out = ws[M_OFF + 2 * blockIdx.x], eq_before = ws[M_OFF + 2 * blockIdx.x + 1];
@@ -626,7 +682,7 @@ __global__ __launch_bounds__(MT) void mtopk_write_kernel(const float* __restrict
   for (int c0 = b0; c0 < b1; c0 += MT) {                    // uniform over the workgroup
     const int i = c0 + threadIdx.x;
     const bool valid = i < b1;
-    const uint32_t key = valid ? order_key(s[i]) : 0u;
+    const uint32_t key = valid ? order_key(mscore(sc, i, ma, mb)) : 0u;
     const bool free_row = valid & (i < nfree);
     const bool eq = free_row & (key == T);
     int n_eq, n_take;
@@ -695,11 +751,12 @@ hipError_t launch_topk_noalloc(const float* s_a, const float* s_b, float w_a, fl
   return launch_topk(s_a, s_b, w_a, w_b, multiply, n, k, n_forced, idx, fused_out, keys, s);
 }
 
-// plain selection over n > 32768 scores on many workgroups (ws: the call's
+// selection over n > 32768 scores on many workgroups (ws: the call's
 // workspace, at least topk_workspace(n) bytes, of which it uses about 30 KiB)
-static hipError_t launch_topk_many(const float* sc, int n, int k, int n_forced, int32_t* idx, int* ws,
-                                   hipStream_t s) {
-  if (k >= n) {
+static hipError_t launch_topk_many(const float* s_a, const float* s_b, float w_a, float w_b, int mult, int n,
+                                   int k, int n_forced, int32_t* idx, float* fused_out, int* ws, hipStream_t s) {
+  const MScores sc{s_a, s_b, w_a, w_b, mult};
+  if (k >= n && !(fused_out && s_b)) {
     hipLaunchKernelGGL(iota_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, s, n, idx);
     return hipGetLastError();
   }
@@ -709,12 +766,21 @@ static hipError_t launch_topk_many(const float* sc, int n, int k, int n_forced, 
   const int R = (((n + MG - 1) / MG) + MT - 1) / MT * MT;
   const int G = (n + R - 1) / R;
   hipLaunchKernelGGL(mtopk_init_kernel, dim3(1), dim3(MT), 0, s, ws);
+  if (s_b && !mult)
+    hipLaunchKernelGGL(mtopk_max_kernel, dim3(std::min(1024, (n + 4 * MT - 1) / (4 * MT))), dim3(MT), 0, s, s_a,
+                       s_b, n, ws);
+  if (k >= n) {
+    // every row is taken; the fused scores are still written
+    hipLaunchKernelGGL(mtopk_count_kernel, dim3(G), dim3(MT), 0, s, sc, n, nfree, 0, R, fused_out, ws);
+    hipLaunchKernelGGL(iota_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, s, n, idx);
+    return hipGetLastError();
+  }
   if (kp > 0) {
     hipLaunchKernelGGL(mtopk_hist_kernel<0>, dim3(hist_blocks), dim3(MT), 0, s, sc, nfree, kp, ws);
     hipLaunchKernelGGL(mtopk_hist_kernel<1>, dim3(hist_blocks), dim3(MT), 0, s, sc, nfree, kp, ws);
     hipLaunchKernelGGL(mtopk_hist_kernel<2>, dim3(hist_blocks), dim3(MT), 0, s, sc, nfree, kp, ws);
   }
-  hipLaunchKernelGGL(mtopk_count_kernel, dim3(G), dim3(MT), 0, s, sc, n, nfree, kp, R, ws);
+  hipLaunchKernelGGL(mtopk_count_kernel, dim3(G), dim3(MT), 0, s, sc, n, nfree, kp, R, fused_out, ws);
   hipLaunchKernelGGL(mtopk_scan_kernel, dim3(1), dim3(MT), 0, s, G, ws);
   hipLaunchKernelGGL(mtopk_write_kernel, dim3(G), dim3(MT), 0, s, sc, n, nfree, k, R, ws, idx);
   return hipGetLastError();
@@ -738,8 +804,7 @@ hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b,
   else if (n <= TPB * 20) go(std::integral_constant<int, 20>{});
   else if (n <= TPB * 24) go(std::integral_constant<int, 24>{});
   else if (n <= TPB * 32) go(std::integral_constant<int, 32>{});
-  else if (s_b) go(std::integral_constant<int, 0>{});        // fused scores: one workgroup
-  else return launch_topk_many(s_a, n, k, n_forced, idx, reinterpret_cast<int*>(ws), s);
+  else return launch_topk_many(s_a, s_b, w_a, w_b, mult, n, k, n_forced, idx, fused_out, reinterpret_cast<int*>(ws), s);
   return hipGetLastError();
 }
 

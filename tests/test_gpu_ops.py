@@ -174,9 +174,11 @@ def test_select_batched_bit_exact(n, k, nf, batch):
 @pytest.mark.parametrize("n,k,nf,nan", [(1000, 350, 64, False), (32768, 11469, 64, False),
                                          (131072, 32768, 128, False), (1000, 350, 64, True),
                                          (131072, 32768, 128, True), (19661, 6881, 64, False),
-                                         (14746, 5161, 64, True), (11469, 4014, 64, False)])
+                                         (14746, 5161, 64, True), (11469, 4014, 64, False),
+                                         (40000, 39000, 64, True), (65537, 70000, 64, True)])
 def test_select_fused_bit_exact(n, k, nf, nan):
-    # n > 32768 keeps the keys in the workspace and takes the maxima in a loop of its own
+    # n > 32768 runs on many workgroups, the maxima in a pass of their own; k >= n
+    # still writes every fused score
     _log(f"fused select n={n} nan={nan}")
     a = W.make_scores(n, seed=7)
     b = W.make_scores(n, seed=8) * 1e-3
@@ -191,7 +193,8 @@ def test_select_fused_bit_exact(n, k, nf, nan):
     assert np.array_equal(idx.cpu().numpy().astype(np.int64), select.select_topk(ref_c, k, nf))
 
 
-@pytest.mark.parametrize("n,k,nf", [(1000, 350, 64), (32768, 11469, 64), (19661, 6881, 64)])
+@pytest.mark.parametrize("n,k,nf", [(1000, 350, 64), (32768, 11469, 64), (19661, 6881, 64),
+                                    (131072, 32768, 128), (50000, 64, 64)])
 def test_select_multiply_bit_exact(n, k, nf):
     _log(f"multiply select n={n}")
     a = W.make_scores(n, seed=9)
