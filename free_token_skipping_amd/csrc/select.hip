@@ -7,8 +7,9 @@
 // ballot compaction in index order then writes exactly k ascending indices:
 // forced rows, rows above T, and the lowest-index rows equal to T.
 //
-// One 1024-thread workgroup does the whole selection: at 32K-128K scores the
-// input is 128-512 KiB and the call is bound by latency, not bandwidth.  Wave
+// Up to 32K scores one 1024-thread workgroup does the whole selection with
+// the keys in registers (the call is bound by latency, not bandwidth; above
+// 32K the selection spreads over many workgroups, see mtopk_* below).  Wave
 // w owns the contiguous rows [w*C, (w+1)*C) and its lanes walk them 64 at a
 // time, so every load is one coalesced 256-byte access.  The radix passes
 // skip the leading key bits that all free rows share (found by an OR/AND
@@ -132,15 +133,15 @@ __device__ __forceinline__ void wave_find_digit(const int* h, int rem, int lane,
   cnt = __builtin_amdgcn_readlane(cc, src);
 }
 
-// IPT > 0: each lane keeps the keys of its IPT rows in registers across all
-// passes (n <= 1024 * IPT).  IPT == 0: keys are re-read from the workspace.
+// Each lane keeps the keys of its IPT rows in registers across all passes
+// (n <= 1024 * IPT); larger selections run on many workgroups (mtopk_* below).
 template <int IPT>
 __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a,
                                                    const float* __restrict__ s_b, float wa, float wb,
                                                    int mult, int n, int k, int nf, int32_t* __restrict__ idx,
-                                                   float* __restrict__ fused_out,
-                                                   uint32_t* __restrict__ keys, long s_stride,
+                                                   float* __restrict__ fused_out, long s_stride,
                                                    long idx_stride) {
+  static_assert(IPT > 0, "keys per lane");
   // Every per-key update below is unconditional: a row that does not count
   // goes to a dummy slot of its own lane (index + lane past the end), so the
   // loops carry no branches and the dummies never collide.
@@ -163,15 +164,10 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
     if (!(fused_out && s_b)) return;
   }
 
-  float ma = 0.f, mb = 0.f;
-  if (IPT == 0 && s_b && !mult) {           // (with IPT > 0 the maxima come from the loaded rows below)
-    float la = -INFINITY, lb = -INFINITY;
-    for (int i = tid; i < n; i += TPB) { la = fmaxf(la, s_a[i]); lb = fmaxf(lb, s_b[i]); }
-    block_max2(la, lb, red, ma, mb);
-  }
-  constexpr int UNROLL_J = IPT > 0 ? IPT : 8;      // workspace keys: 8 loads in flight per lane
+  float ma = 0.f, mb = 0.f;                   // MaxNorm-Add maxima, from the loaded rows below
+  constexpr int UNROLL_J = IPT;
   const int nfree = n - nf;
-  const int J = IPT > 0 ? IPT : (n + TPB - 1) / TPB;   // rows per lane (a constant if IPT > 0)
+  constexpr int J = IPT;                      // rows per lane
   const int base = w * J * 64 + lane;                  // row of (w, j, lane) = base + 64 j
   // a lane's rows base + 64 j are valid (< n) for j < jv and free (< nfree)
   // for j < jf; loops test j against these instead of keeping a mask per row
@@ -180,9 +176,9 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
   // an empty asm that "changes" jv and jf before each loop keeps the compiler
   // from holding 2 x J row masks in scalar registers across loops
 #define SPTS_FRESH_ROWS() asm volatile("" : "+v"(jv), "+v"(jf))
-  uint32_t kr[IPT > 0 ? IPT : 1];
+  uint32_t kr[IPT];
   uint32_t k_or = 0u, k_and = 0xFFFFFFFFu;             // over the free rows
-  if (IPT > 0) {
+  {
     // every load is issued before any is used (the score/fusion choice is
     // made outside the row loop), so a lane's loads are in flight together;
     // kr holds the raw score bits until they become keys
@@ -190,14 +186,14 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
         const int i = base + 64 * j;
-        kr[IPT > 0 ? j : 0] = i < n ? __float_as_uint(s_a[i]) : 0u;
+        kr[j] = i < n ? __float_as_uint(s_a[i]) : 0u;
       }
     } else {
-      float xb[IPT > 0 ? IPT : 1];
+      float xb[IPT];
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
         const int i = base + 64 * j;
-        kr[IPT > 0 ? j : 0] = i < n ? __float_as_uint(s_a[i]) : 0u;
+        kr[j] = i < n ? __float_as_uint(s_a[i]) : 0u;
         xb[j] = i < n ? s_b[i] : 0.f;
       }
       if (!mult) {
@@ -205,54 +201,37 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 #pragma unroll
         for (int j = 0; j < IPT; ++j) {
           const bool v = j < jv;
-          la = fmaxf(la, v ? __uint_as_float(kr[IPT > 0 ? j : 0]) : -INFINITY);
+          la = fmaxf(la, v ? __uint_as_float(kr[j]) : -INFINITY);
           lb = fmaxf(lb, v ? xb[j] : -INFINITY);
         }
         block_max2(la, lb, red, ma, mb);
       }
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
-        const float a = __uint_as_float(kr[IPT > 0 ? j : 0]);
-        kr[IPT > 0 ? j : 0] = __float_as_uint(mult ? __fmul_rn(a, xb[j]) : fuse(a, xb[j], ma, mb, wa, wb));
+        const float a = __uint_as_float(kr[j]);
+        kr[j] = __float_as_uint(mult ? __fmul_rn(a, xb[j]) : fuse(a, xb[j], ma, mb, wa, wb));
       }
     }
     if (fused_out) {
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
         const int i = base + 64 * j;
-        if (i < n) fused_out[i] = __uint_as_float(kr[IPT > 0 ? j : 0]);
+        if (i < n) fused_out[i] = __uint_as_float(kr[j]);
       }
     }
     SPTS_FRESH_ROWS();
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      const uint32_t key = j < jv ? order_key(__uint_as_float(kr[IPT > 0 ? j : 0])) : 0u;
+      const uint32_t key = j < jv ? order_key(__uint_as_float(kr[j])) : 0u;
       const bool fr = j < jf;
       k_or |= fr ? key : 0u;
       k_and &= fr ? key : 0xFFFFFFFFu;
-      kr[IPT > 0 ? j : 0] = key;
-    }
-  } else {
-#pragma unroll UNROLL_J
-    for (int j = 0; j < J; ++j) {
-      const int i = base + 64 * j;
-      if (i < n) {
-        const float x = !s_b ? s_a[i] : mult ? __fmul_rn(s_a[i], s_b[i]) : fuse(s_a[i], s_b[i], ma, mb, wa, wb);
-        if (fused_out) fused_out[i] = x;
-        const uint32_t key = order_key(x);
-        if (i < nfree) { k_or |= key; k_and &= key; }
-        keys[i] = key;
-      }
+      kr[j] = key;
     }
   }
   if (k >= n) return;
-  if (IPT == 0) __threadfence_block();
 
-  auto key_at = [&](int j) -> uint32_t {
-    if (IPT > 0) return kr[j];
-    const int i = base + 64 * j;
-    return i < n ? keys[i] : 0u;                // the workspace holds n keys
-  };
+  auto key_at = [&](int j) -> uint32_t { return kr[j]; };
 
   const int kp = k - nf;            // rows to choose among the free ones
   uint32_t T = 0xFFFFFFFFu;         // no free row is selected when kp == 0 (no key is all ones)
@@ -706,10 +685,10 @@ hipError_t launch_topk_batched(const float* s, long s_stride, int batch, int n, 
   if (batch == 0) return hipSuccess;
   if (n <= TPB * 8)
     hipLaunchKernelGGL(topk_kernel<8>, dim3(batch), dim3(TPB), 0, st, s, nullptr, 0.f, 0.f, 0, n, k, n_forced, idx,
-                       nullptr, nullptr, s_stride, idx_stride);
+                       nullptr, s_stride, idx_stride);
   else
     hipLaunchKernelGGL(topk_kernel<32>, dim3(batch), dim3(TPB), 0, st, s, nullptr, 0.f, 0.f, 0, n, k, n_forced, idx,
-                       nullptr, nullptr, s_stride, idx_stride);
+                       nullptr, s_stride, idx_stride);
   return hipGetLastError();
 }
 
@@ -788,7 +767,6 @@ static hipError_t launch_topk_many(const float* s_a, const float* s_b, float w_a
 
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,
                        int k, int n_forced, int32_t* idx, float* fused_out, void* ws, hipStream_t s) {
-  uint32_t* keys = reinterpret_cast<uint32_t*>(ws);
   const int mult = multiply ? 1 : 0;
   // The fewest rows per lane that hold n: wave w owns rows [64 IPT w, 64 IPT (w + 1)),
   // so a larger IPT than needed leaves waves idle while the busy lanes walk
@@ -796,7 +774,7 @@ hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b,
   // 32 on 6).
   const auto go = [&](auto ipt) {
     hipLaunchKernelGGL(topk_kernel<decltype(ipt)::value>, dim3(1), dim3(TPB), 0, s, s_a, s_b, w_a, w_b, mult, n, k,
-                       n_forced, idx, fused_out, keys, 0L, 0L);
+                       n_forced, idx, fused_out, 0L, 0L);
   };
   if (n <= TPB * 8) go(std::integral_constant<int, 8>{});
   else if (n <= TPB * 12) go(std::integral_constant<int, 12>{});
