@@ -695,11 +695,13 @@ hipError_t launch_topk_batched(const float* s, long s_stride, int batch, int n, 
 size_t topk_workspace(int n) { return (((size_t)n * 4) + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------- allocation-free top-k
-// Key storage of launch_topk_noalloc: a file-scope device array, one copy
-// per GPU, held until the process ends.  Its host-side name is not a device
-// address; host code uses only the address hipGetSymbolAddress gives for the
-// current device, resolved once per device.  Every call on one GPU shares it
-// (the kernel writes each key before reading it, so nothing needs clearing),
+// Workspace of launch_topk_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends (a selection above 32K scores keeps its
+// histograms and counters there, about 29 KiB; up to 32K none is used).  Its
+// host-side name is not a device address; host code uses only the address
+// hipGetSymbolAddress gives for the current device, resolved once per
+// device.  Every call on one GPU shares it (the histograms are cleared by the
+// call's own first kernel, every other slot is written before it is read),
 // so calls that overlap on one GPU race.
 static __device__ __align__(256) uint32_t scratch[kTopkNoallocMaxN];
 

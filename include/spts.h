@@ -134,10 +134,11 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
 /* spts_score_topk without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, rules and results as
- * spts_score_topk; the context's workspace is not used.  The keys of a
- * selection over more than 32768 scores go to a static device array of the
- * library (1048576 entries, 4 MiB, one per GPU, held until the process
- * ends) instead of the workspace; nothing is allocated or freed.  Every call
+ * spts_score_topk; the context's workspace is not used.  A selection over
+ * more than 32768 scores keeps its radix histograms and counters (about
+ * 29 KiB) in a static device array of the library (4 MiB, one per GPU, held
+ * until the process ends) instead of the workspace; nothing is allocated or
+ * freed.  Every call
  * on one GPU shares that array, so calls that overlap on one GPU (on
  * different streams or host threads) race; calls in one stream's order do
  * not.  Requires n <= 1048576 (SPTS_ERR_UNSUPPORTED otherwise). */
