@@ -224,6 +224,7 @@ spts_status spts_score_topk(spts_ctx* ctx, const float* s_a, const float* s_b, f
   if (s_b) REQUIRE_ALIGN(s_b);
   if (fused_out) REQUIRE_ALIGN(fused_out);
   REQUIRE(n >= 1, SPTS_ERR_SHAPE, "n must be >= 1");
+  REQUIRE(n <= kTopkMaxN, SPTS_ERR_UNSUPPORTED, "top-k over %d scores: at most 2^30", n);
   REQUIRE(n_forced >= 0 && n_forced <= k && n_forced <= n, SPTS_ERR_SHAPE,
           "need 0 <= n_forced <= k and n_forced <= n (n=%d k=%d n_forced=%d)", n, k, n_forced);
   const size_t need = topk_workspace(n);
@@ -241,6 +242,7 @@ spts_status spts_score_topk_noalloc(spts_ctx* ctx, const float* s_a, const float
   if (s_b) REQUIRE_ALIGN(s_b);
   if (fused_out) REQUIRE_ALIGN(fused_out);
   REQUIRE(n >= 1, SPTS_ERR_SHAPE, "n must be >= 1");
+  REQUIRE(n <= kTopkMaxN, SPTS_ERR_UNSUPPORTED, "top-k over %d scores: at most 2^30", n);
   REQUIRE(n <= kTopkNoallocMaxN, SPTS_ERR_UNSUPPORTED,
           "score_topk_noalloc holds at most %d scores in its static scratch (n=%d)", kTopkNoallocMaxN, n);
   REQUIRE(n_forced >= 0 && n_forced <= k && n_forced <= n, SPTS_ERR_SHAPE,
@@ -273,6 +275,7 @@ spts_status spts_score_topk_multiply(spts_ctx* ctx, const float* s_a, const floa
   REQUIRE_ALIGN(s_a); REQUIRE_ALIGN(s_b); REQUIRE_ALIGN(idx);
   if (fused_out) REQUIRE_ALIGN(fused_out);
   REQUIRE(n >= 1, SPTS_ERR_SHAPE, "n must be >= 1");
+  REQUIRE(n <= kTopkMaxN, SPTS_ERR_UNSUPPORTED, "top-k over %d scores: at most 2^30", n);
   REQUIRE(n_forced >= 0 && n_forced <= k && n_forced <= n, SPTS_ERR_SHAPE,
           "need 0 <= n_forced <= k and n_forced <= n (n=%d k=%d n_forced=%d)", n, k, n_forced);
   const size_t need = topk_workspace(n);
@@ -834,6 +837,7 @@ spts_status spts_msdp_stage(spts_ctx* ctx, const float* scores, int n_prev, int 
   CHECK_CTX();
   REQUIRE_PTR(scores); REQUIRE_PTR(pos_prev); REQUIRE_PTR(keep); REQUIRE_PTR(pos_new);
   REQUIRE_ALIGN(scores); REQUIRE_ALIGN(pos_prev); REQUIRE_ALIGN(keep); REQUIRE_ALIGN(pos_new);
+  REQUIRE(n_prev <= kTopkMaxN, SPTS_ERR_UNSUPPORTED, "MSDP stage over %d candidates: at most 2^30", n_prev);
   REQUIRE(n_prev >= 1 && budget >= n_forced && n_forced >= 0 && budget <= n_prev, SPTS_ERR_SHAPE,
           "need n_forced <= budget <= n_prev (n_prev=%d budget=%d n_forced=%d)", n_prev, budget, n_forced);
   if (x_prev) {

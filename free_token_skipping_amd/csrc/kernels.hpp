@@ -96,6 +96,8 @@ hipError_t launch_attn_f32(const float* q, const int32_t* idx, const float* k, c
 
 // --------------------------------------------------------------- select
 size_t topk_workspace(int n);
+// most scores one selection takes (row indices and grid strides stay in 32 bits)
+constexpr int kTopkMaxN = 1 << 30;
 // s_b == nullptr: rank s_a; else fuse s_a and s_b by MaxNorm-Add (multiply == false)
 // or by their product (multiply == true)
 hipError_t launch_topk(const float* s_a, const float* s_b, float w_a, float w_b, bool multiply, int n,

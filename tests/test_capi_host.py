@@ -122,6 +122,12 @@ def test_select_validation(L, ctx):
     assert m(ctx, FAKE, MIS, 10, 4, 1, FAKE, None) == ALIGN
     assert L.spts_msdp_stage(ctx, FAKE, 100, 120, 4, FAKE, FAKE, FAKE, None, None, 0) == SHAPE
     assert L.spts_msdp_stage(ctx, FAKE, 100, 50, 60, FAKE, FAKE, FAKE, None, None, 0) == SHAPE
+    # more than 2^30 scores: row indices and grid strides of the selection stay in 32 bits
+    big = (1 << 30) + 1
+    assert f(ctx, FAKE, None, 0.5, 0.5, big, 4, 1, FAKE, None) == UNSUPPORTED
+    assert b"at most 2^30" in L.spts_last_error(ctx)
+    assert m(ctx, FAKE, FAKE, big, 4, 1, FAKE, None) == UNSUPPORTED
+    assert L.spts_msdp_stage(ctx, FAKE, big, 50, 4, FAKE, FAKE, FAKE, None, None, 0) == UNSUPPORTED
 
 
 def test_gemm_family_validation(L, ctx):
