@@ -431,19 +431,19 @@ __global__ __launch_bounds__(TPB) void topk_kernel(const float* __restrict__ s_a
 }
 
 // ------------------------------------------- many-workgroup select (n > 32K)
-// Above 32K scores a single workgroup cannot keep the keys in registers and
-// re-reads them on every pass, so the selection spreads over the chip.  A
-// fused score (MaxNorm-Add needs the two maxima first: one more pass, the
-// maxima as atomicMax over order keys, so NaN is skipped as in topk_kernel)
-// is formed in every pass with the same fp32 operations as topk_kernel.
-// three radix digits (bits 31..21, 20..10, 9..0) are counted by all
-// workgroups into global histograms (integer atomics: exact), each pass
-// recovering the earlier digits from the earlier histograms itself (no
-// separate launch per digit); a count pass fixes the threshold key T and how
-// many rows equal to T to take, counts each workgroup's contiguous row range,
-// a one-workgroup scan turns the counts into output offsets, and a write pass
-// emits the indices in index order.  Same selection as topk_kernel: forced
-// rows, free rows above T, and the lowest-index need_eq free rows equal to T.
+// Above 32K scores a single workgroup cannot keep the keys in registers, so
+// the selection spreads over the chip.  Three radix digits (bits 31..21,
+// 20..10, 9..0) are counted by all workgroups into global histograms (integer
+// atomics: exact), each pass recovering the earlier digits from the earlier
+// histograms itself (no separate launch per digit); a count pass fixes the
+// threshold key T and how many rows equal to T to take and counts each
+// workgroup's contiguous row range, a one-workgroup scan turns the counts
+// into output offsets, and a write pass emits the indices in index order.
+// Same selection as topk_kernel: forced rows, free rows above T, and the
+// lowest-index need_eq free rows equal to T.  A fused score is formed in every
+// pass with the same fp32 operations as topk_kernel; MaxNorm-Add needs the two
+// maxima first, one more pass (atomicMax over order keys, so NaN is skipped
+// as there).
 constexpr int MT = 256;                       // threads per workgroup of these passes
 constexpr int MG = 256;                       // most workgroups of the count / write passes
 constexpr int MB = 2048;                      // bins of the 11-bit digits (the last digit uses 1024)
